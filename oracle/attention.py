@@ -1,0 +1,122 @@
+"""Softmax attention restricted to the selected blocks (oracle), fwd and bwd.
+
+[Prism §Blocks] replaces full self-attention by Prism Block Sparse Attention:
+every query attends only to the key blocks selected for its query block. The
+page gives no formula; the reading taken here (parity against Prism's own
+code unpinned) is the plain one:
+
+  O[n] = sum_{m in K(n)} softmax_m(Q_n . K_m * scale) V_m,
+  lse[n] = ln sum_{m in K(n)} exp(Q_n . K_m * scale),
+
+with K(n) the real tokens of the blocks listed for block(n), scale = 1/sqrt(d)
+by default, non-causal, no dropout, no bias, and the softmax normalised over
+the selected keys only (no correction for the dropped mass).
+
+Backward (same pairs, forward lists reused), with P the probabilities above:
+  D_n = dO_n . O_n,  dV_m = sum_n P_nm dO_n,  dP_nm = dO_n . V_m,
+  dS_nm = P_nm (dP_nm - D_n),  dQ_n = scale sum_m dS_nm K_m,
+  dK_m = scale sum_n dS_nm Q_n.
+
+Two evaluators:
+- ``*_dense_masked``: dense [N, N] logits with an explicit boolean mask in
+  raster order (the definition; small N only);
+- ``*_gathered``: per (head, query block), only the selected keys (the same
+  sums, fast enough for sampled rows of the large workloads).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layout import Layout
+
+
+def attn_fwd_dense_masked(q, k, v, mask, scale):
+    """One head. q,k,v [N, d] fp64, mask [N, N] bool. Returns (O [N,d], lse [N])."""
+    s = (q @ k.T) * scale
+    s = np.where(mask, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.where(mask, np.exp(s - mx), 0.0)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    return p @ v, (mx + np.log(z))[:, 0]
+
+
+def attn_bwd_dense_masked(q, k, v, do, mask, scale):
+    """One head. Returns (dQ, dK, dV), each [N, d]."""
+    s = np.where(mask, (q @ k.T) * scale, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.where(mask, np.exp(s - mx), 0.0)
+    p = e / e.sum(axis=1, keepdims=True)
+    o = p @ v
+    D = (do * o).sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - D)
+    dq = (ds @ k) * scale
+    dk = (ds.T @ q) * scale
+    return dq, dk, dv
+
+
+def _block_tokens(L: Layout, perm: np.ndarray):
+    """Raster ids of the real tokens of every block."""
+    B = L.block_tokens
+    pb = perm.reshape(L.n_blocks, B)
+    return [row[row >= 0] for row in pb]
+
+
+def attn_fwd_gathered(L: Layout, perm, q, k, v, lists, scale, pairs=None):
+    """All heads, raster layout. q,k,v [H, N, d] (any float dtype, upcast to fp64).
+
+    ``pairs``: iterable of (head, query block) to evaluate (default: all).
+    Returns (O [H,N,d], lse [H,N]); rows not evaluated are NaN."""
+    H, N, d = q.shape
+    toks = _block_tokens(L, perm)
+    O = np.full((H, N, d), np.nan)
+    lse = np.full((H, N), np.nan)
+    if pairs is None:
+        pairs = [(h, i) for h in range(H) for i in range(L.n_blocks)]
+    for h, i in pairs:
+        rows = toks[i]
+        if rows.size == 0:
+            continue
+        keys = np.concatenate([toks[j] for j in lists[h][i]])
+        qi = q[h, rows].astype(np.float64)
+        kj = k[h, keys].astype(np.float64)
+        vj = v[h, keys].astype(np.float64)
+        s = (qi @ kj.T) * scale
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        z = e.sum(axis=1, keepdims=True)
+        O[h, rows] = (e / z) @ vj
+        lse[h, rows] = (mx + np.log(z))[:, 0]
+    return O, lse
+
+
+def attn_bwd_gathered(L: Layout, perm, q, k, v, do, lists, scale, heads=None):
+    """All (or the given) heads, raster layout. Returns dQ, dK, dV [H, N, d] fp64
+    (zeros for heads not evaluated)."""
+    H, N, d = q.shape
+    toks = _block_tokens(L, perm)
+    dQ = np.zeros((H, N, d))
+    dK = np.zeros((H, N, d))
+    dV = np.zeros((H, N, d))
+    for h in (range(H) if heads is None else heads):
+        qh = q[h].astype(np.float64)
+        kh = k[h].astype(np.float64)
+        vh = v[h].astype(np.float64)
+        doh = do[h].astype(np.float64)
+        for i in range(L.n_blocks):
+            rows = toks[i]
+            if rows.size == 0:
+                continue
+            keys = np.concatenate([toks[j] for j in lists[h][i]])
+            s = (qh[rows] @ kh[keys].T) * scale
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ vh[keys]
+            D = (doh[rows] * o).sum(axis=1, keepdims=True)
+            dV[h, keys] += p.T @ doh[rows]
+            ds = p * (doh[rows] @ vh[keys].T - D)
+            dQ[h, rows] += (ds @ kh[keys]) * scale
+            dK[h, keys] += (ds.T @ qh[rows]) * scale
+    return dQ, dK, dV

@@ -1,0 +1,164 @@
+"""Pins of the oracle's block-sparse attention, forward and backward.
+
+Library routines (torch's scaled_dot_product_attention with a boolean mask,
+torch.logsumexp, torch autograd, all fp64 on the CPU) for the masked softmax
+attention; exact probes (V = 1, V = one-hot); central finite differences; and
+exact gradient invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from oracle import layout as lay
+from oracle import pipeline as pipe
+from oracle import select as sel
+
+
+def _case(grid=(3, 8, 8), mode="fixed", block=(1, 8, 8), H=2, d=64, S=5000, tau=0.2, seed=0,
+          random_shapes=False):
+    rng = np.random.default_rng(seed)
+    N = int(np.prod(grid))
+    q, k, v = (rng.standard_normal((H, N, d)) for _ in range(3))
+    zs = None
+    if random_shapes:
+        L = lay.make_layout(grid, mode, block)
+        zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    r = pipe.run_selection(grid, mode, block, q, k, S, tau, zone_shape=zs)
+    return r, q, k, v
+
+
+def _sdpa(q, k, v, mask):
+    t = [torch.from_numpy(x)[None] for x in (q, k, v)]
+    return torch.nn.functional.scaled_dot_product_attention(
+        *t, attn_mask=torch.from_numpy(mask)[None])[0].numpy()
+
+
+CASES = [dict(), dict(grid=(5, 20, 36), mode="dynamic", block=(4, 16, 16), d=16, S=9300,
+                      random_shapes=True, seed=1)]
+
+
+@pytest.mark.parametrize("kw", CASES)
+def test_masked_forward_matches_library_sdpa(kw):
+    r, q, k, v = _case(**kw)
+    L = r["layout"]
+    scale = 1 / np.sqrt(q.shape[2])
+    for h in range(q.shape[0]):
+        mask = sel.block_mask(L, r["lists"], h, r["perm"])
+        o, lse = att.attn_fwd_dense_masked(q[h], k[h], v[h], mask, scale)
+        np.testing.assert_allclose(o, _sdpa(q[h], k[h], v[h], mask), rtol=1e-12, atol=1e-13)
+        logits = torch.from_numpy(q[h] @ k[h].T * scale).masked_fill(
+            ~torch.from_numpy(mask), float("-inf"))
+        np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=1).numpy(), rtol=1e-13)
+
+
+def test_sparsity_zero_is_full_attention():
+    r, q, k, v = _case(S=0)
+    L = r["layout"]
+    for h in range(2):
+        o, _ = att.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], 1 / 8.0)
+        full = _sdpa(q[h], k[h], v[h], np.ones((L.n_tokens, L.n_tokens), bool))
+        np.testing.assert_allclose(o[h], full, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kw", CASES)
+def test_gathered_equals_dense_masked(kw):
+    r, q, k, v = _case(**kw)
+    L = r["layout"]
+    scale = 1 / np.sqrt(q.shape[2])
+    O, lse = att.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], scale)
+    for h in range(q.shape[0]):
+        mask = sel.block_mask(L, r["lists"], h, r["perm"])
+        o, l = att.attn_fwd_dense_masked(q[h], k[h], v[h], mask, scale)
+        np.testing.assert_allclose(O[h], o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[h], l, rtol=1e-13)
+
+
+def test_constant_values_give_constant_output():
+    r, q, k, v = _case(S=5000)
+    O, _ = att.attn_fwd_gathered(r["layout"], r["perm"], q, k, np.ones_like(v), r["lists"], 0.125)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-14)
+
+
+def test_one_hot_values_expose_the_probabilities():
+    """V = identity over keys: O = P, so every masked entry is exactly 0 and
+    every row is a probability vector over its selected keys."""
+    r, q, k, _ = _case(grid=(5, 20, 36), mode="dynamic", block=(4, 16, 16), d=16, S=9300,
+                       random_shapes=True, seed=3)
+    L = r["layout"]
+    N = L.n_tokens
+    for h in range(2):
+        mask = sel.block_mask(L, r["lists"], h, r["perm"])
+        P, _ = att.attn_fwd_dense_masked(q[h], k[h], np.eye(N), mask, 0.25)
+        assert np.all(P[~mask] == 0.0)
+        assert np.all(P[mask] > 0.0)
+        np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=1e-13)
+        s = q[h] @ k[h].T * 0.25
+        i = 17
+        sel_keys = np.nonzero(mask[i])[0]
+        e = np.exp(s[i, sel_keys] - s[i, sel_keys].max())
+        np.testing.assert_allclose(P[i, sel_keys], e / e.sum(), rtol=1e-12)
+
+
+def test_backward_matches_library_autograd():
+    r, q, k, v = _case(grid=(5, 20, 36), mode="dynamic", block=(4, 16, 16), d=16, S=9300,
+                       random_shapes=True, seed=5)
+    L = r["layout"]
+    do = np.random.default_rng(9).standard_normal(q.shape)
+    for h in range(2):
+        mask = sel.block_mask(L, r["lists"], h, r["perm"])
+        tq, tk, tv = (torch.from_numpy(x[h]).requires_grad_() for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq[None], tk[None], tv[None], attn_mask=torch.from_numpy(mask)[None])[0]
+        o.backward(torch.from_numpy(do[h]))
+        dq, dk, dv = att.attn_bwd_dense_masked(q[h], k[h], v[h], do[h], mask, 0.25)
+        for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            np.testing.assert_allclose(a, b.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_finite_differences():
+    """Central differences (step 1e-6) of <dO, O(Q,K,V)> on the tiny layout."""
+    r, q, k, v = _case(H=1, d=8)
+    L = r["layout"]
+    mask = sel.block_mask(L, r["lists"], 0, r["perm"])
+    do = np.random.default_rng(1).standard_normal(q[0].shape)
+    scale = 0.3
+
+    def f(qq, kk, vv):
+        return float((att.attn_fwd_dense_masked(qq, kk, vv, mask, scale)[0] * do).sum())
+
+    dq, dk, dv = att.attn_bwd_dense_masked(q[0], k[0], v[0], do, mask, scale)
+    rng = np.random.default_rng(2)
+    eps = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(12):
+            n, c = int(rng.integers(0, q.shape[1])), int(rng.integers(0, 8))
+            args = [q[0].copy(), k[0].copy(), v[0].copy()]
+            args[which][n, c] += eps
+            fp = f(*args)
+            args[which][n, c] -= 2 * eps
+            fm = f(*args)
+            num = (fp - fm) / (2 * eps)
+            assert abs(num - grad[n, c]) <= 1e-6 * max(1.0, abs(num))
+
+
+@pytest.mark.parametrize("kw", CASES)
+def test_backward_invariants_and_gathered(kw):
+    """sum_m dV_m = sum_n dO_n (each row of P sums to 1) and sum_m dK_m = 0
+    (softmax is invariant to a shift of the logits); the gathered evaluator
+    equals the dense one; dO = 0 gives zero gradients."""
+    r, q, k, v = _case(**kw)
+    L = r["layout"]
+    scale = 1 / np.sqrt(q.shape[2])
+    do = np.random.default_rng(4).standard_normal(q.shape)
+    dQ, dK, dV = att.attn_bwd_gathered(L, r["perm"], q, k, v, do, r["lists"], scale)
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(dV[h].sum(axis=0), do[h].sum(axis=0), rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(dK[h].sum(axis=0), 0.0, atol=1e-11)
+        mask = sel.block_mask(L, r["lists"], h, r["perm"])
+        dq, dk, dv = att.attn_bwd_dense_masked(q[h], k[h], v[h], do[h], mask, scale)
+        np.testing.assert_allclose(dQ[h], dq, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dK[h], dk, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dV[h], dv, rtol=1e-11, atol=1e-12)
+    z = att.attn_bwd_gathered(L, r["perm"], q, k, v, np.zeros_like(do), r["lists"], scale)
+    assert all(np.all(g == 0) for g in z)
