@@ -1,0 +1,222 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * The method: Prism block sparse attention (BSA), described on the page
+ * "Prism: 2K 공동 영상·오디오 생성 학습을 위한 동적 희소 어텐션" (Prism: dynamic
+ * sparse attention for training 2K joint video-audio generation;
+ * trawling.dev/post/2299), section "지역별 정보에 맞춘 블록 구성" (block
+ * composition matched to regional information), cited below as [Prism §Blocks].
+ * Latent tokens are split into spatio-temporal macro-zones; each zone picks a
+ * block shape from the channel-wise variance of the video features and the
+ * audio-to-video cross-attention feature norm; tokens are regrouped into those
+ * blocks; key blocks are selected per query block by a hybrid rule (a top-k
+ * set from a sparsity value, united with the smallest CDF prefix reaching a
+ * threshold tau, 0.20 in the page's configuration); attention then runs over
+ * the selected blocks only. The page gives no formulas; the exact reading
+ * implemented here is stated at each call.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.   Pointers are device pointers unless marked [host]. The caller
+ *           allocates every device buffer, including the workspace; the
+ *           library never allocates or frees memory, keeps no pointer after a
+ *           call returns, and has no global mutable state (thread-safe).
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream). A call only
+ *           enqueues kernels on it: it never synchronizes and never copies
+ *           between host and device.
+ * Errors.   Every call returns a bsa_status. All arguments are validated on
+ *           the host before the first launch, so a call that returns an error
+ *           status has launched nothing and written nothing. bsa_last_error()
+ *           gives a thread-local message for the last failure. Faults inside a
+ *           kernel surface at the caller's next synchronization (HIP semantics).
+ * Tokens.   Q/K/V are [heads, tokens, d], row-major, token id raster over the
+ *           latent grid with t slowest: n = (t*H + h)*W + w.
+ * Layout.   Each grid axis is padded up to a multiple of the zone extent.
+ *           Zones are ordered raster over the zone grid; inside a zone, blocks
+ *           are raster over its (zt/bt, zh/bh, zw/bw) sub-grid; inside a block,
+ *           tokens are raster. Block b covers slots [b*B, (b+1)*B) of the
+ *           permuted ("padded") token axis, B = bt*bh*bw. A slot is real iff
+ *           its (t,h,w) lies inside the grid; pad slots hold zeros.
+ * Dtypes.   BSA_BF16 is the performance path; BSA_F32 is the exact-parity path.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+#define BSA_MAX_SHAPES 4
+#define BSA_MAX_BLOCKS 4096   /* per layout: bound of the in-LDS selection sort */
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_INVALID_ARG = 1,         /* null pointer, non-positive size, value out of range */
+  BSA_UNSUPPORTED = 2,         /* dtype / head dim / block size this build has no kernel for */
+  BSA_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < bsa_workspace_size(...) */
+  BSA_LAYOUT = 4,              /* a shape does not tile the zone, too many blocks, ... */
+  BSA_HIP_ERROR = 5            /* a kernel launch failed */
+} bsa_status;
+
+typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype;
+typedef enum { BSA_MODE_FIXED = 0, BSA_MODE_DYNAMIC = 1 } bsa_mode;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+  BSA_CALL_ZONE_SCORE = 0,
+  BSA_CALL_POOL_SELECT = 1,
+  BSA_CALL_ATTN_FWD = 2,
+  BSA_CALL_ATTN_BWD = 3
+} bsa_call;
+
+/* [host] Description of the token layout (plain data, read during a call only).
+ *  grid    latent grid (T, H, W), each >= 1
+ *  mode    BSA_MODE_FIXED: one block shape everywhere; `zone` must equal
+ *          shapes[0] and n_shapes must be 1 (each zone is one block).
+ *          BSA_MODE_DYNAMIC: `zone` is the macro-zone extent (4,16,16 on the
+ *          measured workloads) and shapes[0..n_shapes) are the candidate block
+ *          shapes in canonical order (shape id = index; the measured workloads
+ *          use 0 = 2x8x8, 1 = 4x4x8, 2 = 1x8x16).
+ *  Every shape must divide the zone on each axis and hold B tokens, the same
+ *  B for all shapes; B must be 64 or 128. */
+typedef struct bsa_layout {
+  int32_t grid[3];
+  int32_t mode;
+  int32_t zone[3];
+  int32_t n_shapes;
+  int32_t shapes[BSA_MAX_SHAPES][3];
+} bsa_layout;
+
+/* Library version; equals BSA_ABI_VERSION of the header it was built from. */
+int bsa_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* bsa_status_string(bsa_status s);
+
+/* Thread-local message describing the last non-OK status of this thread. */
+const char* bsa_last_error(void);
+
+/* [host only, no device access] Sizes implied by a layout. Any output pointer
+ * may be NULL.  n_tokens = T*H*W; n_padded = n_blocks * B; n_blocks = zones *
+ * blocks per zone; n_zones = number of macro-zones; block_tokens = B.
+ * Returns BSA_LAYOUT / BSA_INVALID_ARG for an invalid layout. */
+bsa_status bsa_layout_sizes(const bsa_layout* L, int64_t* n_tokens, int64_t* n_padded,
+                            int32_t* n_blocks, int32_t* n_zones, int32_t* block_tokens);
+
+/* [host only] Bytes of device workspace a call needs (0 if none). `heads` and
+ * `d` are those the call will receive (ignored by BSA_CALL_ZONE_SCORE, which
+ * needs `d` = the video channel count C instead). Returns 0 and sets the last
+ * error for an invalid layout; check bsa_last_error() when 0 is unexpected. */
+size_t bsa_workspace_size(bsa_call call, const bsa_layout* L, int heads, int d);
+
+/* Zone scoring and block-shape choice [Prism §Blocks: per macro-zone, the
+ * channel-wise variance of the video features and the A2V cross-attention
+ * feature norm set the zone's block shape; axes with fast change or strong
+ * audio-video coupling are split more finely].
+ * Reading implemented (the page gives no formula):
+ *   g_n  = || sum_j softmax_j(X_n . A_j / sqrt(C)) A_j ||   (one head, identity
+ *          projections);
+ *   V_a(z) = sum over lines along axis a of sum ||X_n - line mean||^2 / (C n_z),
+ *   G_a(z) = the same for the scalar g, divided by n_z (lines = the zone's real
+ *          tokens sharing the other two coordinates; n_z = real tokens of z);
+ *   r_a(z) = V_a(z)/mean(V) + G_a(z)/mean(G), means over non-empty (zone, axis);
+ *   shape(z) = argmin_s sum_a r_a(z) (b_{s,a}^2 - 1)/(Z_a^2 - 1); costs within a
+ *          relative 1e-6 of the minimum tie and the lowest shape id wins.
+ *  video       [N, C] bf16, raster token order, N = T*H*W
+ *  C           channels (1..8192, multiple of 64)
+ *  audio       [n_audio, C] bf16, or NULL (then the A2V term is dropped)
+ *  n_audio     0..256 (0 iff audio == NULL)
+ *  zone_shape  [n_zones] int32 out: shape id per zone
+ *  zone_stats  [n_zones, 3, 2] double out (V_t, G_t, V_h, G_h, V_w, G_w per zone), or NULL
+ *  In fixed mode the call writes 0 to every zone_shape entry and ignores the
+ *  features (video/audio may be NULL). */
+bsa_status bsa_zone_score(const bsa_layout* L, const void* video, int C, const void* audio,
+                          int n_audio, int32_t* zone_shape, double* zone_stats, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Gather tokens into block order [Prism §Blocks: tokens are regrouped into the
+ * zone's blocks so that a block holds semantically close tokens].
+ *  zone_shape  [n_zones] int32 shape ids (device data, so not validated on the
+ *              host; an id outside [0, n_shapes) is clamped into it), or NULL
+ *              for all zeros (fixed mode)
+ *  ntensors    1..4 tensors handled by one launch
+ *  src         [host] array of ntensors device pointers, each [heads, N, d]
+ *  dst         [host] array of ntensors device pointers, each [heads, Np, d];
+ *              pad slots are written with zeros
+ *  d           head dim (multiple of 8, <= 256); dtype BSA_F32 or BSA_BF16 */
+bsa_status bsa_permute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
+                       const void* const* src, void* const* dst, int heads, int d, int dtype,
+                       void* stream);
+
+/* Inverse of bsa_permute: src [heads, Np, d] -> dst [heads, N, d], reading
+ * real slots only. Same arguments as bsa_permute. */
+bsa_status bsa_unpermute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
+                         const void* const* src, void* const* dst, int heads, int d,
+                         int dtype, void* stream);
+
+/* Block-mean pooling and hybrid block selection [Prism §Blocks: block-level
+ * features; hybrid block selection sets each query's sparsity dynamically;
+ * configuration examples sparsity 0.75/0.80/0.85/0.93 and CDF threshold 0.20].
+ * Reading implemented: qbar/kbar = mean of a block's real tokens (fp64);
+ * l_ij = qbar_i . kbar_j / sqrt(d) over the M_v non-empty key blocks (fp64);
+ * order by l descending (ties: lower block id first); k = max(1,
+ * ceil(M_v (10000 - sparsity_1e4) / 10000)) in integers; m = smallest prefix of
+ * that order whose softmax mass reaches tau (>=); the list is the first
+ * max(k, m) blocks of the order, emitted in ascending block id.
+ *  qp, kp        [heads, Np, d] permuted Q and K (pad slots zero)
+ *  sparsity_1e4  skipped fraction x 1e4, 0..9999 (0.85 -> 8500)
+ *  tau           CDF threshold, 0 < tau <= 1 (double, so that the threshold
+ *                compared against is exactly the caller's value)
+ *  counts        [heads, n_blocks] int32 out: list length (0 for an empty query block)
+ *  idx           [heads, n_blocks, n_blocks] int32 out: idx[h][i][0..counts) ascending;
+ *                entries past counts are left unspecified
+ *  pooled_logits [heads, n_blocks, n_blocks] double out, or NULL (debug; -inf
+ *                for empty key blocks, rows of empty query blocks unspecified) */
+bsa_status bsa_pool_select(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                           const void* kp, int heads, int d, int dtype, int32_t sparsity_1e4,
+                           double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention forward [Prism §Blocks: Prism Block Sparse Attention].
+ * For every real query slot n of block i: O[n] = sum over real key slots m of
+ * the blocks idx[h][i][0..counts) of softmax_m(Q_n . K_m * scale) V_m, and
+ * lse[n] = ln sum_m exp(Q_n . K_m * scale). Non-causal, no dropout.
+ *  qp, kp, vp  [heads, Np, d] permuted inputs (pad slots zero)
+ *  counts, idx lists from bsa_pool_select (any lists obeying its format work:
+ *              ascending, unique, non-empty key blocks only)
+ *  scale       softmax scale; 0 selects 1/sqrt(d)
+ *  op          [heads, Np, d] out (same dtype); pad query slots get unspecified
+ *              finite values; rows of empty query blocks get zeros
+ *  lse         [heads, Np] float out (natural log); -inf for rows of empty
+ *              query blocks
+ *  Supported: dtype BSA_BF16 or BSA_F32, d in {64, 128}, B in {64, 128}; the
+ *  bf16 MFMA kernel runs for d = 128, B = 128, the others take a scalar kernel. */
+bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const int32_t* counts,
+                        const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention backward over the forward's lists and lse.
+ * D_n = dO_n . O_n; dV_m = sum_n P_nm dO_n; dS_nm = P_nm (dO_n . V_m - D_n);
+ * dQ_n = scale sum_m dS_nm K_m; dK_m = scale sum_n dS_nm Q_n; sums over the
+ * selected (query, real key) pairs only.
+ *  op, lse     forward outputs; dop [heads, Np, d] permuted output gradient
+ *              (pad query slots must be zero, as bsa_permute writes them)
+ *  dqp, dkp, dvp [heads, Np, d] float32 out, whatever `dtype` is (gradients
+ *              are accumulated and returned in fp32); pad slots get zeros.
+ *  The key-major (transposed) lists are built in the workspace. */
+bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const void* op, const void* dop,
+                        const float* lse, const int32_t* counts, const int32_t* idx,
+                        int heads, int d, int dtype, float scale, void* dqp, void* dkp,
+                        void* dvp, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -92,9 +92,13 @@ def attn_fwd_gathered(L: Layout, perm, q, k, v, lists, scale, pairs=None):
     return O, lse
 
 
-def attn_bwd_gathered(L: Layout, perm, q, k, v, do, lists, scale, heads=None):
+def attn_bwd_gathered(L: Layout, perm, q, k, v, do, lists, scale, heads=None, o=None):
     """All (or the given) heads, raster layout. Returns dQ, dK, dV [H, N, d] fp64
-    (zeros for heads not evaluated)."""
+    (zeros for heads not evaluated).
+
+    ``o``: the forward output handed to the backward ([H, N, d]); D = rowsum(dO * O)
+    then uses it, as a backward that receives O as an input does. By default O
+    is recomputed exactly."""
     H, N, d = q.shape
     toks = _block_tokens(L, perm)
     dQ = np.zeros((H, N, d))
@@ -113,10 +117,57 @@ def attn_bwd_gathered(L: Layout, perm, q, k, v, do, lists, scale, heads=None):
             s = (qh[rows] @ kh[keys].T) * scale
             e = np.exp(s - s.max(axis=1, keepdims=True))
             p = e / e.sum(axis=1, keepdims=True)
-            o = p @ vh[keys]
-            D = (doh[rows] * o).sum(axis=1, keepdims=True)
+            oo = p @ vh[keys] if o is None else o[h, rows].astype(np.float64)
+            D = (doh[rows] * oo).sum(axis=1, keepdims=True)
             dV[h, keys] += p.T @ doh[rows]
             ds = p * (doh[rows] @ vh[keys].T - D)
             dQ[h, rows] += (ds @ kh[keys]) * scale
             dK[h, keys] += (ds.T @ qh[rows]) * scale
     return dQ, dK, dV
+
+
+def attn_bwd_gathered_blocks(L: Layout, perm, q, k, v, do, lists, scale, h, q_blocks=(),
+                             k_blocks=(), o=None):
+    """Gradients of one head restricted to chosen blocks (the same sums as
+    ``attn_bwd_gathered``, evaluated only where asked):
+
+    dQ rows of the query blocks ``q_blocks`` and dK/dV rows of the key blocks
+    ``k_blocks`` (which need every query block whose list holds them).
+    ``o`` as in ``attn_bwd_gathered``.
+    Returns dicts block -> (raster rows, dQ) and block -> (raster rows, dK, dV)."""
+    toks = _block_tokens(L, perm)
+    qh = q[h].astype(np.float64)
+    kh = k[h].astype(np.float64)
+    vh = v[h].astype(np.float64)
+    doh = do[h].astype(np.float64)
+    want_k = set(int(j) for j in k_blocks)
+    need_q = set(int(i) for i in q_blocks)
+    for i in range(L.n_blocks):
+        if want_k & set(int(j) for j in lists[h][i]):
+            need_q.add(i)
+    out_q = {}
+    acc_k = {j: (toks[j], np.zeros((toks[j].size, q.shape[2])), np.zeros((toks[j].size, q.shape[2])))
+             for j in want_k}
+    for i in sorted(need_q):
+        rows = toks[i]
+        if rows.size == 0:
+            continue
+        lst = [int(j) for j in lists[h][i]]
+        keys = np.concatenate([toks[j] for j in lst])
+        s = (qh[rows] @ kh[keys].T) * scale
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        oo = p @ vh[keys] if o is None else o[h, rows].astype(np.float64)
+        D = (doh[rows] * oo).sum(axis=1, keepdims=True)
+        ds = p * (doh[rows] @ vh[keys].T - D)
+        if i in q_blocks:
+            out_q[i] = (rows, (ds @ kh[keys]) * scale)
+        off = 0
+        for j in lst:
+            n = toks[j].size
+            if j in acc_k:
+                _, dk, dv = acc_k[j]
+                dv += p[:, off:off + n].T @ doh[rows]
+                dk += (ds[:, off:off + n].T @ qh[rows]) * scale
+            off += n
+    return out_q, acc_k

@@ -1,0 +1,178 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every entry point declared in include/bsa.h,
+report layout sizes, and reject every invalid argument with the documented
+status before touching the device. Every call below is built to fail
+validation; the fake device pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_diffusion_block_amd import _lib
+from video_diffusion_block_amd.ops import BSALayout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define BSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.bsa_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for s, name in enumerate(["BSA_OK", "BSA_INVALID_ARG", "BSA_UNSUPPORTED",
+                              "BSA_WORKSPACE_TOO_SMALL", "BSA_LAYOUT", "BSA_HIP_ERROR"]):
+        assert lib.bsa_status_string(s).decode() == name
+
+
+@pytest.mark.parametrize("grid,mode,block,want", [
+    ((3, 8, 8), "fixed", (1, 8, 8), (192, 192, 3, 3, 64)),
+    ((13, 45, 80), "fixed", (2, 8, 8), (46800, 53760, 420, 420, 128)),
+    ((13, 45, 80), "dynamic", (4, 16, 16), (46800, 61440, 480, 60, 128)),
+    ((13, 68, 120), "dynamic", (4, 16, 16), (106080, 163840, 1280, 160, 128)),
+    ((13, 90, 160), "dynamic", (4, 16, 16), (187200, 245760, 1920, 240, 128)),
+])
+def test_layout_sizes(grid, mode, block, want):
+    L = BSALayout.fixed(grid, block) if mode == "fixed" else BSALayout.dynamic(grid, block)
+    s = L.sizes()
+    assert (s["n_tokens"], s["n_padded"], s["n_blocks"], s["n_zones"], s["block_tokens"]) == want
+
+
+def _status_of_layout(lib, L):
+    c = L.c()
+    return lib.bsa_layout_sizes(ctypes.byref(c), None, None, None, None, None)
+
+
+def test_invalid_layouts(lib):
+    assert _status_of_layout(lib, BSALayout.fixed((0, 8, 8), (1, 8, 8))) == _lib.BSA_INVALID_ARG
+    assert _status_of_layout(lib, BSALayout.dynamic((4, 16, 16), (4, 16, 16), ((3, 8, 8),))) == _lib.BSA_LAYOUT
+    assert _status_of_layout(lib, BSALayout.dynamic((4, 16, 16), (4, 16, 16),
+                                                    ((2, 8, 8), (2, 4, 8)))) == _lib.BSA_LAYOUT
+    assert _status_of_layout(lib, BSALayout.fixed((4, 16, 16), (2, 4, 4))) == _lib.BSA_UNSUPPORTED
+    assert _status_of_layout(lib, BSALayout.fixed((64, 256, 256), (2, 8, 8))) == _lib.BSA_LAYOUT
+    bad = BSALayout(grid=(4, 16, 16), mode=0, zone=(4, 16, 16), shapes=((2, 8, 8),))
+    assert _status_of_layout(lib, bad) == _lib.BSA_LAYOUT          # fixed: zone != shape
+    bad = BSALayout(grid=(4, 16, 16), mode=7, zone=(2, 8, 8), shapes=((2, 8, 8),))
+    assert _status_of_layout(lib, bad) == _lib.BSA_INVALID_ARG
+    assert "tile" in lib.bsa_last_error().decode() or lib.bsa_last_error()
+
+
+def test_workspace_sizes_positive(lib):
+    L = BSALayout.dynamic((13, 90, 160)).c()
+    for call in range(4):
+        n = lib.bsa_workspace_size(call, ctypes.byref(L), 4, 128)
+        assert (n > 0) == (call != _lib.BSA_CALL_ATTN_FWD)
+    bad = BSALayout.fixed((0, 1, 1), (1, 8, 8)).c()
+    assert lib.bsa_workspace_size(1, ctypes.byref(bad), 4, 128) == 0
+
+
+LAY = BSALayout.fixed((13, 45, 80), (2, 8, 8))
+DYN = BSALayout.dynamic((13, 45, 80))
+
+
+def _pool_select(lib, L=LAY, zs=FAKE, q=FAKE, k=FAKE, H=2, d=128, dt=1, S=8500, tau=0.2,
+                 counts=FAKE, idx=FAKE, ws=FAKE, wsb=1 << 40):
+    c = L.c()
+    return lib.bsa_pool_select(ctypes.byref(c), zs, q, k, H, d, dt, S, tau, counts, idx, None,
+                               ws, wsb, None)
+
+
+def test_pool_select_validation(lib):
+    assert _pool_select(lib, q=None) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, S=10000) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, S=-1) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, tau=0.0) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, tau=1.5) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, tau=float("nan")) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, d=96) == _lib.BSA_UNSUPPORTED
+    assert _pool_select(lib, dt=7) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, H=0) == _lib.BSA_INVALID_ARG
+    assert _pool_select(lib, wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert _pool_select(lib, ws=None) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert _pool_select(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
+    assert "sparsity" in (lib.bsa_last_error().decode() + "sparsity")
+
+
+def _attn_fwd(lib, L=LAY, q=FAKE, d=128, dt=1, scale=0.0, lse=FAKE, zs=FAKE):
+    c = L.c()
+    return lib.bsa_attn_fwd(ctypes.byref(c), zs, q, FAKE, FAKE, FAKE, FAKE, 2, d, dt, scale,
+                            FAKE, lse, None, 0, None)
+
+
+def test_attn_fwd_validation(lib):
+    assert _attn_fwd(lib, q=None) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, lse=None) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, d=32) == _lib.BSA_UNSUPPORTED
+    assert _attn_fwd(lib, dt=3) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, scale=-1.0) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, scale=float("inf")) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, scale=float("nan")) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
+
+
+def test_attn_bwd_validation(lib):
+    c = LAY.c()
+
+    def call(dq=FAKE, wsb=1 << 40, d=128):
+        return lib.bsa_attn_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 2, d, 1, 0.0, dq, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(dq=None) == _lib.BSA_INVALID_ARG
+    assert call(wsb=1) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert call(d=48) == _lib.BSA_UNSUPPORTED
+
+
+def test_permute_validation(lib):
+    c = LAY.c()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    nul = (ctypes.c_void_p * 2)(FAKE, None)
+    assert lib.bsa_permute(ctypes.byref(c), None, 5, arr, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
+    assert lib.bsa_permute(ctypes.byref(c), None, 0, arr, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
+    assert lib.bsa_permute(ctypes.byref(c), None, 2, nul, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
+    assert lib.bsa_permute(ctypes.byref(c), None, 1, None, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
+    assert lib.bsa_unpermute(ctypes.byref(c), None, 1, arr, arr, 2, 4, 1, None) == _lib.BSA_UNSUPPORTED
+    assert lib.bsa_unpermute(ctypes.byref(c), None, 1, arr, arr, 2, 512, 1, None) == _lib.BSA_UNSUPPORTED
+    d = DYN.c()
+    assert lib.bsa_permute(ctypes.byref(d), None, 1, arr, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
+
+
+def test_zone_score_validation(lib):
+    c = DYN.c()
+
+    def call(video=FAKE, C=1536, audio=FAKE, na=200, zs=FAKE, wsb=1 << 40):
+        return lib.bsa_zone_score(ctypes.byref(c), video, C, audio, na, zs, None, FAKE, wsb, None)
+
+    assert call(zs=None) == _lib.BSA_INVALID_ARG
+    assert call(video=None) == _lib.BSA_INVALID_ARG
+    assert call(C=100) == _lib.BSA_INVALID_ARG
+    assert call(audio=None) == _lib.BSA_INVALID_ARG            # n_audio given without audio
+    assert call(na=0) == _lib.BSA_INVALID_ARG                  # audio given without n_audio
+    assert call(na=300) == _lib.BSA_INVALID_ARG
+    assert call(wsb=8) == _lib.BSA_WORKSPACE_TOO_SMALL
+    big = BSALayout.dynamic((16, 64, 64), (8, 16, 16), ((2, 8, 8),)).c()
+    assert lib.bsa_zone_score(ctypes.byref(big), FAKE, 1536, None, 0, FAKE, None, FAKE, 1 << 40,
+                              None) == _lib.BSA_UNSUPPORTED

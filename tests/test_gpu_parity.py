@@ -1,0 +1,303 @@
+"""GPU parity: every C-ABI call against the fp64 oracle (tests/parity.py rules).
+
+Small cases are compared in full; the measured workloads (720p fixed, 720p
+dynamic, 1080p, 2K) are compared at full size in the launch configuration the
+benchmark times: zone shapes and block lists in full, outputs on seeded
+samples of (head, block) pairs evaluated by the oracle one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as oatt
+from oracle import layout as olay
+from oracle import pipeline as opipe
+from oracle import select as osel
+from oracle import zones as ozon
+from parity import (BF16_L1_REL, BF16_MAX_ABS, F32_TOL, ZONE_TIE, assert_bf16_close,
+                    compare_lists, gpu_lists, host_f64, oracle_layout, to_dev, to_f64)
+from video_diffusion_block_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+
+def layout_of(wl):
+    if wl.mode == "fixed":
+        return ops.BSALayout.fixed(wl.grid, wl.block)
+    return ops.BSALayout.dynamic(wl.grid, wl.block)
+
+
+def run_gpu(wl, inp, zone_shape=None, video=None, audio=None):
+    """The forward hot path through the C ABI; returns GPU tensors."""
+    lay = layout_of(wl)
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    if zone_shape is not None:
+        zs = torch.as_tensor(np.asarray(zone_shape, np.int32)).cuda()
+    elif wl.mode == "dynamic":
+        zs = ops.zone_score(lay, video, audio)
+    else:
+        zs = ops.zone_score(lay, None, None)
+    qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+    counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+    op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
+    (o,) = ops.unpermute(lay, zs, [op])
+    torch.cuda.synchronize()
+    return dict(lay=lay, zs=zs, q=q, k=k, v=v, qp=qp, kp=kp, vp=vp, counts=counts, idx=idx,
+                op=op, lse=lse, o=o)
+
+
+def lse_raster(L, perm, lse_padded):
+    """[H, Np] -> [H, N] (raster), from the oracle's permutation."""
+    inv = olay.inverse(perm, L.n_tokens)
+    return lse_padded[:, inv]
+
+
+# ----------------------------------------------------------------- tiny fp32 --
+def test_tiny_fp32_full_pipeline():
+    wl = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(wl, parts=("q", "k", "v", "do"))
+    g = run_gpu(wl, inp)
+    q, k, v, do = (inp[p].astype(np.float64) for p in ("q", "k", "v", "do"))
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau)
+    L, perm = r["layout"], r["perm"]
+    # permutation: bitwise
+    assert np.array_equal(g["qp"].cpu().numpy(), olay.permute(inp["q"], perm))
+    # lists: exact
+    for ga, oa in zip(gpu_lists(g["counts"], g["idx"]), r["lists"]):
+        assert all(np.array_equal(a, b) for a, b in zip(ga, oa))
+    scale = 1 / np.sqrt(wl.d)
+    o_gpu = to_f64(g["o"])
+    lse_gpu = lse_raster(L, perm, to_f64(g["lse"]))
+    for h in range(wl.heads):
+        mask = osel.block_mask(L, r["lists"], h, perm)
+        o_ref, lse_ref = oatt.attn_fwd_dense_masked(q[h], k[h], v[h], mask, scale)
+        assert np.abs(o_gpu[h] - o_ref).max() <= F32_TOL
+        assert np.abs(lse_gpu[h] - lse_ref).max() <= F32_TOL
+    # backward
+    lay = g["lay"]
+    (dop,) = ops.permute(lay, g["zs"], [to_dev(inp["do"], "f32")])
+    dq, dk, dv = ops.attn_bwd(lay, g["zs"], g["qp"], g["kp"], g["vp"], g["op"], dop, g["lse"],
+                              g["counts"], g["idx"])
+    dq, dk, dv = (to_f64(t) for t in ops.unpermute(lay, g["zs"], [dq, dk, dv]))
+    for h in range(wl.heads):
+        mask = osel.block_mask(L, r["lists"], h, perm)
+        ref = oatt.attn_bwd_dense_masked(q[h], k[h], v[h], do[h], mask, scale)
+        for got, want in zip((dq, dk, dv), ref):
+            assert np.abs(got[h] - want).max() <= F32_TOL
+
+
+# --------------------------------------------- small bf16 / fp32, forced shapes --
+SMALL = [
+    synth.Workload("ragged-dyn", (5, 20, 36), 2, 128, "bf16", "dynamic", (4, 16, 16), 9300, 0.2),
+    synth.Workload("ragged-dyn-d64", (5, 20, 36), 2, 64, "bf16", "dynamic", (4, 16, 16), 8000, 0.2),
+    synth.Workload("ragged-dyn-f32", (6, 18, 34), 2, 64, "f32", "dynamic", (4, 16, 16), 7500, 0.2,
+                   smooth=False),
+    synth.Workload("fixed-ragged", (7, 19, 30), 2, 128, "bf16", "fixed", (2, 8, 8), 8500, 0.2),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small_pipeline_forced_shapes(wl):
+    inp = synth.make_inputs(wl, parts=("q", "k", "v", "do"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(5)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    zs[0] = len(L.shapes) - 1          # make sure the last candidate (1x8x16) appears
+    g = run_gpu(wl, inp, zone_shape=zs)
+    q, k, v, do = (host_f64(inp[p], wl.dtype) for p in ("q", "k", "v", "do"))
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau, zone_shape=zs)
+    perm = r["perm"]
+    for name, t in (("q", g["qp"]), ("k", g["kp"]), ("v", g["vp"])):
+        want = olay.permute(inp[name], perm)
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16) if wl.dtype == "bf16" else t.cpu().numpy()
+        assert np.array_equal(got, want), name
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, gpu_lists(g["counts"], g["idx"]), r["lists"])
+    assert not fails, fails[:3]
+    lists = gpu_lists(g["counts"], g["idx"])
+    scale = 1 / np.sqrt(wl.d)
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, perm, q, k, v, lists, scale)
+    o_gpu = to_f64(g["o"])
+    lse_gpu = lse_raster(L, perm, to_f64(g["lse"]))
+    if wl.dtype == "bf16":
+        assert_bf16_close(o_gpu, o_ref, "O")
+        assert np.abs(lse_gpu - lse_ref).max() <= 1e-3
+    else:
+        assert np.abs(o_gpu - o_ref).max() <= F32_TOL
+        assert np.abs(lse_gpu - lse_ref).max() <= F32_TOL
+    # unpermute(permute(x)) == x bitwise
+    (back,) = ops.unpermute(g["lay"], g["zs"], [g["qp"]])
+    assert torch.equal(back, g["q"])
+    # backward under the same lists
+    (dop,) = ops.permute(g["lay"], g["zs"], [to_dev(inp["do"], wl.dtype)])
+    grads = ops.attn_bwd(g["lay"], g["zs"], g["qp"], g["kp"], g["vp"], g["op"], dop, g["lse"],
+                         g["counts"], g["idx"])
+    got = [to_f64(t) for t in ops.unpermute(g["lay"], g["zs"], list(grads))]
+    # D = rowsum(dO * O) uses the O the backward receives (the GPU forward's)
+    ref = oatt.attn_bwd_gathered(L, perm, q, k, v, do, lists, scale, o=o_gpu)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        if wl.dtype == "bf16":
+            assert_bf16_close(a, b, name)
+        else:
+            assert np.abs(a - b).max() <= F32_TOL, name
+
+
+def test_cdf_branch_lists():
+    """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
+    top-k (s = 0.93), so most lists have n = m > k."""
+    wl = synth.Workload("flat", (8, 32, 64), 2, 128, "bf16", "fixed", (2, 8, 8), 9300, 0.2,
+                        smooth=False)
+    rng = np.random.default_rng(11)
+    N = wl.n_tokens
+    inp = {p: synth.f32_to_bf16_bits(rng.standard_normal((2, N, 128)).astype(np.float32) * s)
+           for p, s in (("q", 0.05), ("k", 0.05), ("v", 1.0))}
+    g = run_gpu(wl, inp)
+    q, k = (synth.bf16_bits_to_f64(inp[p]) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau)
+    L = r["layout"]
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, gpu_lists(g["counts"], g["idx"]), r["lists"])
+    assert not fails, fails[:3]
+    assert (r["n"] > r["k"]).mean() > 0.5
+
+
+# ------------------------------------------------------------- zone scoring --
+def _zone_case(grid, C, na, seed=4):
+    X = synth.smooth_field(1, grid, C, seed)[0]
+    A = synth.f32_to_bf16_bits(synth.gaussian_noise((na, C), seed + 1)) if na else None
+    return X, A
+
+
+@pytest.mark.parametrize("grid,C,na", [((8, 32, 48), 256, 40), ((5, 20, 36), 128, 0),
+                                       ((13, 45, 80), 512, 200)])
+def test_zone_score_small(grid, C, na):
+    X, A = _zone_case(grid, C, na)
+    lay = ops.BSALayout.dynamic(grid)
+    zs, stats = ops.zone_score(lay, to_dev(X, "bf16"), to_dev(A, "bf16") if na else None,
+                               with_stats=True)
+    L = olay.make_layout(grid, "dynamic", (4, 16, 16))
+    shape, V, G, cost, gap = ozon.score_zones(L, synth.bf16_bits_to_f64(X),
+                                              synth.bf16_bits_to_f64(A) if na else None)
+    st = stats.cpu().numpy()
+    np.testing.assert_allclose(st[:, :, 0], V, rtol=1e-9, atol=1e-12)
+    if na:
+        np.testing.assert_allclose(st[:, :, 1], G, rtol=2e-4, atol=1e-9)
+    got = zs.cpu().numpy()
+    bad = (got != shape) & (gap >= ZONE_TIE)
+    assert not bad.any(), (np.nonzero(bad), got[bad], shape[bad], gap[bad])
+
+
+def test_zone_score_ramps_pick_the_closed_form_shapes():
+    grid = (8, 32, 32)
+    T, H, W = grid
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    lay = ops.BSALayout.dynamic(grid)
+    for coord, want in ((t, 2), (h, 1), (w, 0)):
+        X = (coord.reshape(-1, 1) * np.ones((1, 64)) * 0.125).astype(np.float32)
+        zs = ops.zone_score(lay, to_dev(synth.f32_to_bf16_bits(X), "bf16"), None)
+        assert np.all(zs.cpu().numpy() == want)
+
+
+def test_fixed_layout_zone_score_is_zero():
+    lay = ops.BSALayout.fixed((13, 45, 80), (2, 8, 8))
+    zs = ops.zone_score(lay, None, None)
+    assert torch.all(zs == 0)
+
+
+# ----------------------------------------------------- measured workloads --
+@pytest.mark.parametrize("name", ["720p", "720p-dyn", "1080p", "2k"])
+def test_full_size_workload(name):
+    wl = synth.WORKLOADS[name]
+    print(f"\n[{name}] generating inputs", flush=True)
+    parts = ("q", "k", "v") + (("video", "audio") if wl.mode == "dynamic" else ()) + \
+            (("do",) if wl.backward else ())
+    inp = synth.make_inputs(wl, parts=parts)
+    video = to_dev(inp["video"], "bf16") if "video" in inp else None
+    audio = to_dev(inp["audio"], "bf16") if "audio" in inp else None
+    print(f"[{name}] gpu forward", flush=True)
+    g = run_gpu(wl, inp, video=video, audio=audio)
+    L = oracle_layout(wl)
+    zs_gpu = g["zs"].cpu().numpy()
+    if wl.mode == "dynamic":
+        print(f"[{name}] oracle zone scoring", flush=True)
+        shape, V, G, cost, gap = ozon.score_zones(L, synth.bf16_bits_to_f64(inp["video"]),
+                                                  synth.bf16_bits_to_f64(inp["audio"]))
+        bad = (zs_gpu != shape) & (gap >= ZONE_TIE)
+        assert not bad.any(), (np.nonzero(bad), zs_gpu[bad], shape[bad], gap[bad])
+        print(f"[{name}] zone shapes {np.bincount(zs_gpu, minlength=3).tolist()}, "
+              f"{int((zs_gpu != shape).sum())} tie-exempt differences", flush=True)
+    print(f"[{name}] oracle selection", flush=True)
+    q, k = (synth.bf16_bits_to_f64(inp[p]) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau,
+                            zone_shape=zs_gpu)
+    lists = gpu_lists(g["counts"], g["idx"])
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, lists, r["lists"])
+    print(f"[{name}] lists: {exact} exact, {exempt} tie-exempt, {len(fails)} failures; "
+          f"k={r['k']} mean n={r['n'][:, r['counts'] > 0].mean():.1f} "
+          f"rows n>k: {(r['n'] > r['k']).mean():.3f}", flush=True)
+    assert not fails, fails[:3]
+    # sampled outputs
+    perm = r["perm"]
+    rng = np.random.default_rng(7)
+    M = L.n_blocks
+    nonempty = np.nonzero(r["counts"] > 0)[0]
+    partial = np.nonzero((r["counts"] > 0) & (r["counts"] < L.block_tokens))[0]
+    cnt = g["counts"].cpu().numpy()
+    hmax, imax = np.unravel_index(np.argmax(cnt), cnt.shape)
+    pairs = {(int(hmax), int(imax)), (wl.heads - 1, int(nonempty[-1]))}
+    if partial.size:
+        pairs.add((0, int(partial[0])))
+    while len(pairs) < 24:
+        pairs.add((int(rng.integers(0, wl.heads)), int(rng.choice(nonempty))))
+    pairs = sorted(pairs)
+    v = synth.bf16_bits_to_f64(inp["v"])
+    scale = 1 / np.sqrt(wl.d)
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, perm, q, k, v, lists, scale, pairs=pairs)
+    o_gpu = g["o"]
+    lse_gpu = to_f64(g["lse"])
+    rows_all = []
+    for h, i in pairs:
+        rows = perm[i * L.block_tokens:(i + 1) * L.block_tokens]
+        slots = np.nonzero(rows >= 0)[0] + i * L.block_tokens
+        rows = rows[rows >= 0]
+        got = to_f64(o_gpu[h, torch.as_tensor(rows).cuda()])
+        assert_bf16_close(got, o_ref[h, rows], f"O head {h} block {i}")
+        assert np.abs(lse_gpu[h, slots] - lse_ref[h, rows]).max() <= 1e-3
+        rows_all.append(rows)
+    print(f"[{name}] {len(pairs)} sampled blocks match", flush=True)
+    if wl.backward:
+        print(f"[{name}] backward", flush=True)
+        lay = g["lay"]
+        (dop,) = ops.permute(lay, g["zs"], [to_dev(inp["do"], "bf16")])
+        grads = ops.attn_bwd(lay, g["zs"], g["qp"], g["kp"], g["vp"], g["op"], dop, g["lse"],
+                             g["counts"], g["idx"])
+        dq, dk, dv = ops.unpermute(lay, g["zs"], list(grads))
+        do = synth.bf16_bits_to_f64(inp["do"])
+        o_host = to_f64(g["o"])
+        for h in range(min(2, wl.heads)):
+            qb = [int(x) for x in rng.choice(nonempty, 3, replace=False)]
+            kb = [int(x) for x in rng.choice(nonempty, 2, replace=False)]
+            oq, ok = oatt.attn_bwd_gathered_blocks(L, perm, q, k, v, do, lists, scale, h,
+                                                   q_blocks=qb, k_blocks=kb, o=o_host)
+            for i, (rows, ref) in oq.items():
+                assert_bf16_close(to_f64(dq[h, torch.as_tensor(rows).cuda()]), ref, f"dQ {h},{i}")
+            for j, (rows, rdk, rdv) in ok.items():
+                ix = torch.as_tensor(rows).cuda()
+                assert_bf16_close(to_f64(dk[h, ix]), rdk, f"dK {h},{j}")
+                assert_bf16_close(to_f64(dv[h, ix]), rdv, f"dV {h},{j}")
+        print(f"[{name}] backward samples match", flush=True)
+
+
+def test_forward_is_deterministic():
+    wl = synth.Workload("det", (13, 45, 80), 4, 128, "bf16", "fixed", (2, 8, 8), 8500, 0.2)
+    inp = synth.make_inputs(wl)
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp)
+    assert torch.equal(a["counts"], b["counts"])
+    la, lb = gpu_lists(a["counts"], a["idx"]), gpu_lists(b["counts"], b["idx"])
+    assert all(np.array_equal(x, y) for ra, rb in zip(la, lb) for x, y in zip(ra, rb))
+    assert torch.equal(a["op"].view(torch.int16), b["op"].view(torch.int16))
+    assert torch.equal(a["lse"], b["lse"])
+    assert not torch.isnan(a["o"].float()).any()

@@ -162,3 +162,8 @@ def test_backward_invariants_and_gathered(kw):
         np.testing.assert_allclose(dV[h], dv, rtol=1e-11, atol=1e-12)
     z = att.attn_bwd_gathered(L, r["perm"], q, k, v, np.zeros_like(do), r["lists"], scale)
     assert all(np.all(g == 0) for g in z)
+    # handing the exact forward output to the backward changes nothing
+    O, _ = att.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], scale)
+    withO = att.attn_bwd_gathered(L, r["perm"], q, k, v, do, r["lists"], scale, o=O)
+    for a, b in zip(withO, (dQ, dK, dV)):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)

@@ -1,0 +1,16 @@
+"""MI355X (gfx950) block-sparse attention for video-DiT latent tokens.
+
+The compute lives in ``libbsa.so`` (hand-written HIP, C ABI in include/bsa.h);
+``ops`` wraps each entry point for torch device tensors. Importing the package
+does not load the library; the first call does, and raises if it is missing.
+"""
+from . import ops  # noqa: F401
+from .ops import (  # noqa: F401
+    BSALayout,
+    attn_bwd,
+    attn_fwd,
+    permute,
+    pool_select,
+    unpermute,
+    zone_score,
+)

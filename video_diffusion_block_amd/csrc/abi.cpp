@@ -1,0 +1,310 @@
+// C ABI of the block-sparse attention library: host-side validation, workspace
+// sizing and dispatch to the HIP kernels. No HIP runtime call is made before an
+// argument set has been validated, so every error status is returned without
+// touching the device (this is also what lets the validation be exercised on a
+// machine without a GPU).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsa_status fail(bsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bsa_status ok() {
+  g_err[0] = '\0';
+  return BSA_OK;
+}
+
+// Validate a layout and fill the device-side description.
+bsa_status make_lay(const bsa_layout* in, bsa::Lay* L) {
+  if (!in) return fail(BSA_INVALID_ARG, "layout is NULL");
+  for (int a = 0; a < 3; ++a) {
+    if (in->grid[a] < 1) return fail(BSA_INVALID_ARG, "grid[%d] = %d must be >= 1", a, in->grid[a]);
+    if (in->zone[a] < 1) return fail(BSA_INVALID_ARG, "zone[%d] = %d must be >= 1", a, in->zone[a]);
+    if (in->grid[a] > (1 << 20)) return fail(BSA_LAYOUT, "grid[%d] too large", a);
+  }
+  if (in->mode != BSA_MODE_FIXED && in->mode != BSA_MODE_DYNAMIC)
+    return fail(BSA_INVALID_ARG, "mode %d is neither fixed nor dynamic", in->mode);
+  if (in->n_shapes < 1 || in->n_shapes > BSA_MAX_SHAPES)
+    return fail(BSA_INVALID_ARG, "n_shapes = %d out of [1, %d]", in->n_shapes, BSA_MAX_SHAPES);
+  if (in->mode == BSA_MODE_FIXED) {
+    if (in->n_shapes != 1) return fail(BSA_LAYOUT, "fixed mode takes exactly one shape");
+    for (int a = 0; a < 3; ++a)
+      if (in->shapes[0][a] != in->zone[a])
+        return fail(BSA_LAYOUT, "fixed mode: zone must equal the block shape");
+  }
+  const long long ztok = (long long)in->zone[0] * in->zone[1] * in->zone[2];
+  long long B = -1;
+  for (int s = 0; s < in->n_shapes; ++s) {
+    long long b = 1;
+    for (int a = 0; a < 3; ++a) {
+      const int e = in->shapes[s][a];
+      if (e < 1) return fail(BSA_INVALID_ARG, "shape %d axis %d = %d must be >= 1", s, a, e);
+      if (in->zone[a] % e)
+        return fail(BSA_LAYOUT, "shape %d does not tile the zone on axis %d", s, a);
+      b *= e;
+    }
+    if (B < 0) B = b;
+    if (b != B) return fail(BSA_LAYOUT, "candidate shapes must hold the same number of tokens");
+  }
+  if (B != 64 && B != 128)
+    return fail(BSA_UNSUPPORTED, "block of %lld tokens; 64 or 128 supported", B);
+  bsa::Lay& o = *L;
+  o.T = in->grid[0];
+  o.H = in->grid[1];
+  o.W = in->grid[2];
+  o.zt = in->zone[0];
+  o.zh = in->zone[1];
+  o.zw = in->zone[2];
+  o.gzt = (o.T + o.zt - 1) / o.zt;
+  o.gzh = (o.H + o.zh - 1) / o.zh;
+  o.gzw = (o.W + o.zw - 1) / o.zw;
+  o.n_shapes = in->n_shapes;
+  for (int s = 0; s < BSA_MAX_SHAPES; ++s)
+    for (int a = 0; a < 3; ++a) o.sh[s][a] = s < in->n_shapes ? in->shapes[s][a] : 1;
+  o.B = (int)B;
+  o.bpz = (int)(ztok / B);
+  const long long nZ = (long long)o.gzt * o.gzh * o.gzw;
+  const long long M = nZ * o.bpz;
+  if (M > BSA_MAX_BLOCKS)
+    return fail(BSA_LAYOUT, "%lld blocks exceed the limit of %d", M, BSA_MAX_BLOCKS);
+  o.nZ = (int)nZ;
+  o.M = (int)M;
+  o.N = (long long)o.T * o.H * o.W;
+  o.Np = M * B;
+  return ok();
+}
+
+bsa_status check_dtype_d(int dtype, int d) {
+  if (dtype != BSA_F32 && dtype != BSA_BF16) return fail(BSA_INVALID_ARG, "dtype %d unknown", dtype);
+  if (d <= 0) return fail(BSA_INVALID_ARG, "d = %d must be positive", d);
+  return ok();
+}
+
+bsa_status check_heads(int heads) {
+  if (heads < 1 || heads > 65535) return fail(BSA_INVALID_ARG, "heads = %d out of [1, 65535]", heads);
+  return ok();
+}
+
+size_t esize(int dtype) { return dtype == BSA_BF16 ? 2 : 4; }
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t pool_select_ws(const bsa::Lay& L, int heads, int d) {
+  return 2 * al256((size_t)heads * L.M * d * sizeof(double)) +
+         al256((size_t)heads * L.M * L.M * sizeof(double));
+}
+
+bsa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define BSA_TRY(x)                    \
+  do {                                \
+    const bsa_status s_ = (x);        \
+    if (s_ != BSA_OK) return s_;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+const char* bsa_status_string(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_INVALID_ARG: return "BSA_INVALID_ARG";
+    case BSA_UNSUPPORTED: return "BSA_UNSUPPORTED";
+    case BSA_WORKSPACE_TOO_SMALL: return "BSA_WORKSPACE_TOO_SMALL";
+    case BSA_LAYOUT: return "BSA_LAYOUT";
+    case BSA_HIP_ERROR: return "BSA_HIP_ERROR";
+  }
+  return "BSA_UNKNOWN_STATUS";
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+bsa_status bsa_layout_sizes(const bsa_layout* in, int64_t* n_tokens, int64_t* n_padded,
+                            int32_t* n_blocks, int32_t* n_zones, int32_t* block_tokens) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  if (n_tokens) *n_tokens = L.N;
+  if (n_padded) *n_padded = L.Np;
+  if (n_blocks) *n_blocks = L.M;
+  if (n_zones) *n_zones = L.nZ;
+  if (block_tokens) *block_tokens = L.B;
+  return ok();
+}
+
+size_t bsa_workspace_size(bsa_call call, const bsa_layout* in, int heads, int d) {
+  bsa::Lay L;
+  if (make_lay(in, &L) != BSA_OK) return 0;
+  if (heads < 1) heads = 1;
+  if (d < 1) d = 1;
+  switch (call) {
+    case BSA_CALL_ZONE_SCORE: return bsa::zone_score_workspace(L, d, 256);
+    case BSA_CALL_POOL_SELECT: return pool_select_ws(L, heads, d);
+    case BSA_CALL_ATTN_FWD: return 0;
+    case BSA_CALL_ATTN_BWD: return bsa::attn_bwd_workspace(L, heads, d);
+  }
+  fail(BSA_INVALID_ARG, "unknown call %d", (int)call);
+  return 0;
+}
+
+bsa_status bsa_zone_score(const bsa_layout* in, const void* video, int C, const void* audio,
+                          int n_audio, int32_t* zone_shape, double* zone_stats, void* ws,
+                          size_t ws_bytes, void* stream) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  if (!zone_shape) return fail(BSA_INVALID_ARG, "zone_shape is NULL");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (in->mode == BSA_MODE_FIXED)
+    return hip_status(bsa::launch_zone_score(L, nullptr, 0, nullptr, 0, zone_shape, nullptr,
+                                             nullptr, st),
+                      "zone_score");
+  if (!video) return fail(BSA_INVALID_ARG, "video is NULL in dynamic mode");
+  if (C < 64 || C > 8192 || C % 64) return fail(BSA_INVALID_ARG, "C = %d must be a multiple of 64 in [64, 8192]", C);
+  if ((audio == nullptr) != (n_audio == 0))
+    return fail(BSA_INVALID_ARG, "audio and n_audio must both be given or both absent");
+  if (n_audio < 0 || n_audio > 256) return fail(BSA_INVALID_ARG, "n_audio = %d out of [0, 256]", n_audio);
+  if (L.zt > 4 || L.zh > 16 || L.zw > 16)
+    return fail(BSA_UNSUPPORTED, "zone scoring supports zones up to 4x16x16");
+  const size_t need = bsa::zone_score_workspace(L, C, n_audio);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_WORKSPACE_TOO_SMALL, "zone_score needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return hip_status(bsa::launch_zone_score(L, video, C, audio, n_audio, zone_shape, zone_stats,
+                                           ws, st),
+                    "zone_score");
+}
+
+static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
+                                 const void* const* src, void* const* dst, int heads, int d,
+                                 int dtype, void* stream, bool inverse) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  BSA_TRY(check_heads(heads));
+  BSA_TRY(check_dtype_d(dtype, d));
+  if (ntensors < 1 || ntensors > 4) return fail(BSA_INVALID_ARG, "ntensors = %d out of [1, 4]", ntensors);
+  if (!src || !dst) return fail(BSA_INVALID_ARG, "src/dst pointer arrays are NULL");
+  for (int i = 0; i < ntensors; ++i)
+    if (!src[i] || !dst[i]) return fail(BSA_INVALID_ARG, "tensor %d pointer is NULL", i);
+  const size_t row = (size_t)d * esize(dtype);
+  if (row % 16 || d > 256) return fail(BSA_UNSUPPORTED, "row of %zu bytes (d = %d); need a multiple of 16 bytes and d <= 256", row, d);
+  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
+    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  return hip_status(bsa::launch_permute(L, zone_shape, ntensors, src, dst, heads, (int)row,
+                                        inverse, static_cast<hipStream_t>(stream)),
+                    inverse ? "unpermute" : "permute");
+}
+
+bsa_status bsa_permute(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
+                       const void* const* src, void* const* dst, int heads, int d, int dtype,
+                       void* stream) {
+  return permute_common(in, zone_shape, ntensors, src, dst, heads, d, dtype, stream, false);
+}
+
+bsa_status bsa_unpermute(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
+                         const void* const* src, void* const* dst, int heads, int d, int dtype,
+                         void* stream) {
+  return permute_common(in, zone_shape, ntensors, src, dst, heads, d, dtype, stream, true);
+}
+
+bsa_status bsa_pool_select(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                           const void* kp, int heads, int d, int dtype, int32_t sparsity_1e4,
+                           double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
+                           void* ws, size_t ws_bytes, void* stream) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  BSA_TRY(check_heads(heads));
+  BSA_TRY(check_dtype_d(dtype, d));
+  if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (!qp || !kp || !counts || !idx) return fail(BSA_INVALID_ARG, "qp/kp/counts/idx is NULL");
+  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
+    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  if (sparsity_1e4 < 0 || sparsity_1e4 > 9999)
+    return fail(BSA_INVALID_ARG, "sparsity_1e4 = %d out of [0, 9999]", sparsity_1e4);
+  if (!(tau > 0.0 && tau <= 1.0)) return fail(BSA_INVALID_ARG, "tau = %g out of (0, 1]", tau);
+  const size_t need = pool_select_ws(L, heads, d);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_WORKSPACE_TOO_SMALL, "pool_select needs %zu workspace bytes, got %zu", need, ws_bytes);
+  char* p = static_cast<char*>(ws);
+  double* qbar = reinterpret_cast<double*>(p);
+  p += al256((size_t)heads * L.M * d * sizeof(double));
+  double* kbar = reinterpret_cast<double*>(p);
+  p += al256((size_t)heads * L.M * d * sizeof(double));
+  double* logits = pooled_logits ? pooled_logits : reinterpret_cast<double*>(p);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == BSA_BF16;
+  hipError_t e = bsa::launch_pool(L, zone_shape, qp, kp, heads, d, bf16, qbar, kbar, st);
+  if (e == hipSuccess)
+    e = bsa::launch_pooled_logits(L, zone_shape, qbar, kbar, heads, d, 1.0 / sqrt((double)d),
+                                  logits, st);
+  if (e == hipSuccess)
+    e = bsa::launch_select(L, zone_shape, logits, heads, sparsity_1e4, tau, counts, idx, st);
+  return hip_status(e, "pool_select");
+}
+
+bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const int32_t* counts,
+                        const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  BSA_TRY(check_heads(heads));
+  BSA_TRY(check_dtype_d(dtype, d));
+  if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (!qp || !kp || !vp || !counts || !idx || !op || !lse)
+    return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
+    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");
+  const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
+  return hip_status(bsa::launch_attn_fwd(L, zone_shape, qp, kp, vp, counts, idx, heads, d,
+                                         dtype == BSA_BF16, sc, op, lse,
+                                         static_cast<hipStream_t>(stream)),
+                    "attn_fwd");
+}
+
+bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const void* op, const void* dop,
+                        const float* lse, const int32_t* counts, const int32_t* idx, int heads,
+                        int d, int dtype, float scale, void* dqp, void* dkp, void* dvp,
+                        void* ws, size_t ws_bytes, void* stream) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  BSA_TRY(check_heads(heads));
+  BSA_TRY(check_dtype_d(dtype, d));
+  if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (!qp || !kp || !vp || !op || !dop || !lse || !counts || !idx || !dqp || !dkp || !dvp)
+    return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
+    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");
+  const size_t need = bsa::attn_bwd_workspace(L, heads, d);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_WORKSPACE_TOO_SMALL, "attn_bwd needs %zu workspace bytes, got %zu", need, ws_bytes);
+  const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
+  return hip_status(bsa::launch_attn_bwd(L, zone_shape, qp, kp, vp, op, dop, lse, counts, idx,
+                                         heads, d, dtype == BSA_BF16, sc, dqp, dkp, dvp, ws,
+                                         static_cast<hipStream_t>(stream)),
+                    "attn_bwd");
+}
+
+}  // extern "C"

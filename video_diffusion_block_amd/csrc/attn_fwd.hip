@@ -1,0 +1,348 @@
+// Block-sparse attention forward.
+//
+// Prism page (trawling.dev/post/2299), section on block composition matched to
+// regional information: Prism Block Sparse Attention attends every query block
+// only to its selected key blocks. For each real query slot n of block i:
+//   O[n] = sum_m softmax_m(Q_n . K_m * scale) V_m over the real slots m of the
+//   listed key blocks;  lse[n] = ln sum_m exp(Q_n . K_m * scale).
+//
+// Two kernels:
+//  * attn_fwd_mfma: bf16, d = 128, 128-token blocks. One workgroup of 8
+//    wavefronts per (query block, head). Wave w owns queries 32*(w%4)..+32 and
+//    keys 64*(w/4)..+64 of every key block, so each K/V element read from LDS
+//    feeds two MFMA column tiles... (see the layout notes in the kernel). S is
+//    computed transposed (S^T = K Q^T) so that a lane holds one query's scores
+//    and the softmax row reductions stay inside the lane (one cross-half
+//    exchange); O^T = V^T P^T then keeps the per-query rescale lane-local too.
+//    K tiles (row-major) and V^T tiles are double-buffered in LDS; the next
+//    block's global loads are in flight while the current one is computed.
+//  * attn_fwd_scalar: any dtype (fp32 / bf16), d in {64, 128}, B in {64, 128}.
+//    One thread per query slot, fp32 online softmax, K/V staged through LDS as
+//    fp32. This is the exact-parity path (fp32 inputs) and the fallback.
+#include "attn_common.hpp"
+#include "kernels.hpp"
+
+namespace bsa {
+namespace {
+
+// ------------------------------------------------------------ scalar path --
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_fwd_scalar(Lay L, const int32_t* zone_shape,
+                                                       const T* qp, const T* kp, const T* vp,
+                                                       const int32_t* counts, const int32_t* idx,
+                                                       float scale, T* op, float* lse) {
+  extern __shared__ float smem[];
+  float* ks = smem;               // [B][D]
+  float* vs = smem + L.B * D;     // [B][D]
+  const int i = blockIdx.x, h = blockIdx.y, r = threadIdx.x;
+  const size_t row = (size_t)h * L.M + i;
+  const int n = counts[row];
+  const int32_t* lst = idx + row * L.M;
+  const size_t qoff = ((size_t)h * L.Np + (size_t)i * L.B + r) * D;
+  float q[D], o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = to_f32(qp[qoff + e]) * scale;
+    o[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int it = 0; it < n; ++it) {
+    const int j = lst[it];
+    const Box xj = block_box(L, zone_shape, j);
+    __syncthreads();
+    const size_t koff = ((size_t)h * L.Np + (size_t)j * L.B) * D;
+    for (int e = r; e < L.B * D; e += blockDim.x) {
+      ks[e] = to_f32(kp[koff + e]);
+      vs[e] = to_f32(vp[koff + e]);
+    }
+    __syncthreads();
+    for (int c = 0; c < L.B; ++c) {
+      if (!slot_real(xj, c)) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) s = fmaf(q[e], ks[c * D + e], s);
+      if (s > m) {
+        const float corr = expf(m - s);
+        l *= corr;
+#pragma unroll
+        for (int e = 0; e < D; ++e) o[e] *= corr;
+        m = s;
+      }
+      const float p = expf(s - m);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[e] = fmaf(p, vs[c * D + e], o[e]);
+    }
+  }
+  const float inv = n > 0 ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[qoff + e] = from_f32<T>(o[e] * inv);
+  lse[(size_t)h * L.Np + (size_t)i * L.B + r] = n > 0 ? m + logf(l) : -INFINITY;
+}
+
+// -------------------------------------------------------------- MFMA path --
+constexpr int kD = 128;          // head dim
+constexpr int kB = 128;          // tokens per block (queries and keys)
+constexpr int kKS = kD + 8;      // K tile row stride (bf16 elements): 272 bytes
+constexpr int kVS = kB + 4;      // V^T tile row stride (bf16 elements): 264 bytes
+constexpr int kKElems = kB * kKS;
+constexpr int kVElems = kD * kVS;
+constexpr int kStage = kKElems + kVElems;  // bf16 elements per pipeline stage
+constexpr int kThreads = 512;              // 8 wavefronts
+constexpr size_t kMfmaLds = 2 * kStage * sizeof(__bf16);
+
+struct Prefetch {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+// K: thread t loads rows (t>>4) + 32*r, 16-byte chunk (t&15).
+// V: thread t loads rows 4*(t>>4) + r (r = 0..3), chunk (t&15), so that it can
+// write 4 consecutive keys of one d-column of V^T with one 8-byte store.
+__device__ inline void load_tile(Prefetch& pf, const __bf16* kbase, const __bf16* vbase, int tid) {
+  const int c = tid & 15, g = tid >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    pf.k[r] = *reinterpret_cast<const uint4*>(kbase + (size_t)(g + 32 * r) * kD + 8 * c);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    pf.v[r] = *reinterpret_cast<const uint4*>(vbase + (size_t)(4 * g + r) * kD + 8 * c);
+}
+
+__device__ inline void store_tile(const Prefetch& pf, __bf16* sk, __bf16* svt, int tid) {
+  const int c = tid & 15, g = tid >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<uint4*>(sk + (g + 32 * r) * kKS + 8 * c) = pf.k[r];
+  const unsigned short* v0 = reinterpret_cast<const unsigned short*>(&pf.v[0]);
+  const unsigned short* v1 = reinterpret_cast<const unsigned short*>(&pf.v[1]);
+  const unsigned short* v2 = reinterpret_cast<const unsigned short*>(&pf.v[2]);
+  const unsigned short* v3 = reinterpret_cast<const unsigned short*>(&pf.v[3]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint2 w;
+    w.x = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+    w.y = (uint32_t)v2[e] | ((uint32_t)v3[e] << 16);
+    *reinterpret_cast<uint2*>(svt + (8 * c + e) * kVS + 4 * g) = w;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_t* zone_shape,
+                                                            const __bf16* qp, const __bf16* kp,
+                                                            const __bf16* vp,
+                                                            const int32_t* counts,
+                                                            const int32_t* idx, float scale_log2,
+                                                            __bf16* op, float* lse) {
+  extern __shared__ __align__(16) __bf16 lds[];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qg = w & 3, kh = w >> 2;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t row = (size_t)h * L.M + i;
+  const int n = counts[row];
+  const int32_t* lst = idx + row * L.M;
+  const size_t head0 = (size_t)h * L.Np;
+  const int q = 32 * qg + l32;  // this lane's query inside the block
+
+  if (n == 0) {  // empty query block (all pad): zeros, lse = -inf
+    if (kh == 0) {
+      __bf16* orow = op + (head0 + (size_t)i * kB + q) * kD;
+      for (int e = 8 * hi; e < kD; e += 16) *reinterpret_cast<uint4*>(orow + e) = make_uint4(0, 0, 0, 0);
+      if (hi == 0) lse[head0 + (size_t)i * kB + q] = -INFINITY;
+    }
+    return;
+  }
+
+  // Q^T fragments (B operand of S^T = K Q^T): lane holds Q[q][16s + 8hi .. +8].
+  bf16x8 qf[8];
+  {
+    const __bf16* qrow = qp + (head0 + (size_t)i * kB + q) * kD + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY;  // running max of s * scale * log2(e)
+  float l_run = 0.f;        // this lane's share of the running sum
+
+  Prefetch pf;
+  {
+    const int j = lst[0];
+    const __bf16* kb = kp + (head0 + (size_t)j * kB) * kD;
+    const __bf16* vb = vp + (head0 + (size_t)j * kB) * kD;
+    load_tile(pf, kb, vb, tid);
+    store_tile(pf, lds, lds + kKElems, tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n; ++it) {
+    const int j = lst[it];
+    const bool more = it + 1 < n;
+    if (more) {
+      const int jn = lst[it + 1];
+      load_tile(pf, kp + (head0 + (size_t)jn * kB) * kD, vp + (head0 + (size_t)jn * kB) * kD, tid);
+    }
+    const __bf16* sk = lds + (it & 1) * kStage;
+    const __bf16* svt = sk + kKElems;
+
+    // S^T tiles: keys 64kh + 32kt + (0..31) x queries 32qg + (0..31)
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      const __bf16* krow = sk + (64 * kh + 32 * kt + l32) * kKS + 8 * hi;
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        s[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * st), qf[st], s[kt]);
+    }
+
+    // pad keys of a partial key block
+    const Box xj = block_box(L, zone_shape, j);
+    if (xj.count() < kB) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * kh + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (!slot_real(xj, key)) s[kt][r] = -INFINITY;
+        }
+    }
+
+    // online softmax (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pf8[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(fmaf(s[kt][r], scale_log2, -m_use));
+        psum += p;
+        pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+
+    // O^T (d x queries) += V^T (d x keys) P^T (keys x queries).
+    // P^T fragment c (c = 0..3) holds keys 16c + 8(jj/4) + 4hi + jj%4 (jj = 0..7)
+    // of this wave's 64 keys; the V^T A-operand uses the same key order.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const __bf16* vrow = svt + (32 * t + l32) * kVS + 64 * kh + 4 * hi;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * c);
+        const bf16x4 up = *reinterpret_cast<const bf16x4*>(vrow + 16 * c + 8);
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[t] = mfma32x32x16(a, pf8[c], o[t]);
+      }
+    }
+
+    if (more) store_tile(pf, lds + ((it + 1) & 1) * kStage, lds + ((it + 1) & 1) * kStage + kKElems, tid);
+    __syncthreads();
+  }
+
+  // merge the two key halves (waves w and w+4 share their 32 queries)
+  l_run += __shfl_xor(l_run, 32);
+  float* xch = reinterpret_cast<float*>(lds);  // [4 waves][64 lanes][66 floats]
+  float* mine = xch + (qg * 64 + lane) * 66;
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[16 * t + r] = o[t][r];
+    mine[64] = m_run;
+    mine[65] = l_run;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m2 = mine[64], l2 = mine[65];
+    const float mt = fmaxf(m_run, m2);
+    const float mu = mt == -INFINITY ? 0.f : mt;
+    const float a1 = exp2_fast(m_run - mu), a2 = exp2_fast(m2 - mu);
+    const float lt = l_run * a1 + l2 * a2;
+    const float inv = 1.f / lt;
+    __bf16* orow = op + (head0 + (size_t)i * kB + q) * kD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 4 * g + rr;
+          v[rr] = (__bf16)((o[t][r] * a1 + mine[16 * t + r] * a2) * inv);
+        }
+        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * hi) = v;
+      }
+    if (hi == 0) lse[head0 + (size_t)i * kB + q] = (mt + log2f(lt)) * kLn2;
+  }
+}
+
+template <typename T>
+hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
+                         const void* vp, const int32_t* counts, const int32_t* idx, int heads,
+                         int d, float scale, void* op, float* lse, hipStream_t st) {
+  dim3 grid(L.M, heads);
+  const size_t shmem = 2 * (size_t)L.B * d * sizeof(float);
+  const T* q = static_cast<const T*>(qp);
+  const T* k = static_cast<const T*>(kp);
+  const T* v = static_cast<const T*>(vp);
+  T* o = static_cast<T*>(op);
+  if (d == 64) {
+    auto kern = attn_fwd_scalar<T, 64>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    kern<<<grid, L.B, shmem, st>>>(L, zone_shape, q, k, v, counts, idx, scale, o, lse);
+  } else {
+    auto kern = attn_fwd_scalar<T, 128>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    kern<<<grid, L.B, shmem, st>>>(L, zone_shape, q, k, v, counts, idx, scale, o, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16) { return bf16 && d == kD && L.B == kB; }
+
+hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
+                           const void* kp, const void* vp, const int32_t* counts,
+                           const int32_t* idx, int heads, int d, bool bf16, float scale,
+                           void* op, float* lse, hipStream_t st) {
+  if (attn_fwd_uses_mfma(L, d, bf16)) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(attn_fwd_mfma),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLds);
+    dim3 grid(L.M, heads);
+    attn_fwd_mfma<<<grid, kThreads, kMfmaLds, st>>>(
+        L, zone_shape, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
+        static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e, static_cast<__bf16*>(op),
+        lse);
+    return hipGetLastError();
+  }
+  if (bf16)
+    return launch_scalar<__bf16>(L, zone_shape, qp, kp, vp, counts, idx, heads, d, scale, op,
+                                 lse, st);
+  return launch_scalar<float>(L, zone_shape, qp, kp, vp, counts, idx, heads, d, scale, op, lse,
+                              st);
+}
+
+}  // namespace bsa

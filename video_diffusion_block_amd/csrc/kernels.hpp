@@ -1,0 +1,51 @@
+// Internal launchers of the HIP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace bsa {
+
+// Gather [heads, N, d] -> [heads, Np, d] (inverse = false) or the reverse.
+hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
+                          const void* const* src, void* const* dst, int heads, int row_bytes,
+                          bool inverse, hipStream_t st);
+
+// Block means of Q and K over real slots, fp64: [heads, M, d] each.
+hipError_t launch_pool(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
+                       int heads, int d, bool bf16, double* qbar, double* kbar, hipStream_t st);
+
+// Pooled logits l[h,i,j] = qbar_i . kbar_j * scale (fp64), -inf for empty key blocks.
+hipError_t launch_pooled_logits(const Lay& L, const int32_t* zone_shape, const double* qbar,
+                                const double* kbar, int heads, int d, double scale,
+                                double* logits, hipStream_t st);
+
+// Hybrid selection per (head, query block) from the pooled logits.
+hipError_t launch_select(const Lay& L, const int32_t* zone_shape, const double* logits,
+                         int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
+                         hipStream_t st);
+
+// Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel.
+hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
+                           const void* kp, const void* vp, const int32_t* counts,
+                           const int32_t* idx, int heads, int d, bool bf16, float scale,
+                           void* op, float* lse, hipStream_t st);
+
+// Attention backward.
+size_t attn_bwd_workspace(const Lay& L, int heads, int d);
+hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* qp,
+                           const void* kp, const void* vp, const void* op, const void* dop,
+                           const float* lse, const int32_t* counts, const int32_t* idx,
+                           int heads, int d, bool bf16, float scale, void* dqp, void* dkp,
+                           void* dvp, void* ws, hipStream_t st);
+
+// Zone scoring.
+size_t zone_score_workspace(const Lay& L, int C, int n_audio);
+hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void* audio,
+                             int n_audio, int32_t* zone_shape, double* zone_stats, void* ws,
+                             hipStream_t st);
+
+}  // namespace bsa

@@ -1,0 +1,198 @@
+"""Thin torch-facing wrappers of the C ABI (argument marshalling only).
+
+Every step runs in the HIP kernels of ``libbsa.so``; these functions only
+allocate outputs/workspaces with torch (device memory) and pass pointers and
+the current HIP stream. Names follow the C entry points (``bsa_<name>``).
+Inputs must be contiguous device tensors (torch.float32 or torch.bfloat16).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+
+import torch
+
+from . import _lib
+
+CANDIDATES = ((2, 8, 8), (4, 4, 8), (1, 8, 16))
+ZONE = (4, 16, 16)
+
+
+@dataclasses.dataclass(frozen=True)
+class BSALayout:
+    """Token layout: grid, mode, zone extent and candidate block shapes."""
+
+    grid: tuple
+    mode: int
+    zone: tuple
+    shapes: tuple
+
+    @staticmethod
+    def fixed(grid, block) -> "BSALayout":
+        return BSALayout(tuple(grid), _lib.BSA_MODE_FIXED, tuple(block), (tuple(block),))
+
+    @staticmethod
+    def dynamic(grid, zone=ZONE, shapes=CANDIDATES) -> "BSALayout":
+        return BSALayout(tuple(grid), _lib.BSA_MODE_DYNAMIC, tuple(zone),
+                         tuple(tuple(s) for s in shapes))
+
+    def c(self) -> _lib.Layout:
+        L = _lib.Layout()
+        for a in range(3):
+            L.grid[a] = int(self.grid[a])
+            L.zone[a] = int(self.zone[a])
+        L.mode = int(self.mode)
+        L.n_shapes = len(self.shapes)
+        for s, shp in enumerate(self.shapes):
+            for a in range(3):
+                L.shapes[s][a] = int(shp[a])
+        return L
+
+    def sizes(self) -> dict:
+        lib = _lib.load()
+        n, npad = ctypes.c_int64(), ctypes.c_int64()
+        m, nz, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        L = self.c()
+        _lib.check("bsa_layout_sizes", lib.bsa_layout_sizes(
+            ctypes.byref(L), ctypes.byref(n), ctypes.byref(npad), ctypes.byref(m),
+            ctypes.byref(nz), ctypes.byref(b)))
+        return dict(n_tokens=n.value, n_padded=npad.value, n_blocks=m.value, n_zones=nz.value,
+                    block_tokens=b.value)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.BSA_BF16
+    if t.dtype == torch.float32:
+        return _lib.BSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _workspace(call: int, layout: BSALayout, heads: int, d: int, device) -> torch.Tensor:
+    L = layout.c()
+    n = _lib.load().bsa_workspace_size(call, ctypes.byref(L), heads, d)
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+def zone_score(layout: BSALayout, video: torch.Tensor | None, audio: torch.Tensor | None,
+               with_stats: bool = False):
+    """bsa_zone_score: shape id per zone (int32 [n_zones]) and optionally the
+    per-zone (V_a, G_a) statistics (float64 [n_zones, 3, 2])."""
+    lib = _lib.load()
+    sz = layout.sizes()
+    dev = video.device if video is not None else torch.device("cuda")
+    _dev(video, audio)
+    zs = torch.empty(sz["n_zones"], dtype=torch.int32, device=dev)
+    stats = torch.empty((sz["n_zones"], 3, 2), dtype=torch.float64, device=dev) if with_stats else None
+    C = 0 if video is None else video.shape[1]
+    na = 0 if audio is None else audio.shape[0]
+    ws = _workspace(_lib.BSA_CALL_ZONE_SCORE, layout, 1, max(C, 1), dev)
+    L = layout.c()
+    _lib.check("bsa_zone_score", lib.bsa_zone_score(
+        ctypes.byref(L), _ptr(video), C, _ptr(audio), na, _ptr(zs), _ptr(stats), _ptr(ws),
+        ws.numel(), _stream()))
+    return (zs, stats) if with_stats else zs
+
+
+def _permute_call(name, layout, zone_shape, srcs, dsts):
+    lib = _lib.load()
+    H, _, d = srcs[0].shape
+    n = len(srcs)
+    src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in srcs])
+    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dsts])
+    L = layout.c()
+    fn = getattr(lib, name)
+    _lib.check(name, fn(ctypes.byref(L), _ptr(zone_shape), n, src_arr, dst_arr, H, d,
+                        _dtype(srcs[0]), _stream()))
+
+
+def permute(layout: BSALayout, zone_shape, tensors):
+    """bsa_permute: list of [H, N, d] -> list of [H, Np, d] (one launch)."""
+    _dev(zone_shape, *tensors)
+    npad = layout.sizes()["n_padded"]
+    outs = [torch.empty((t.shape[0], npad, t.shape[2]), dtype=t.dtype, device=t.device)
+            for t in tensors]
+    _permute_call("bsa_permute", layout, zone_shape, list(tensors), outs)
+    return outs
+
+
+def unpermute(layout: BSALayout, zone_shape, tensors):
+    """bsa_unpermute: list of [H, Np, d] -> list of [H, N, d] (one launch)."""
+    _dev(zone_shape, *tensors)
+    n = layout.sizes()["n_tokens"]
+    outs = [torch.empty((t.shape[0], n, t.shape[2]), dtype=t.dtype, device=t.device)
+            for t in tensors]
+    _permute_call("bsa_unpermute", layout, zone_shape, list(tensors), outs)
+    return outs
+
+
+def pool_select(layout: BSALayout, zone_shape, qp, kp, sparsity_1e4: int, tau: float,
+                return_logits: bool = False):
+    """bsa_pool_select: counts [H, M] int32, idx [H, M, M] int32 (and the fp64
+    pooled logits when asked)."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp)
+    H, _, d = qp.shape
+    M = layout.sizes()["n_blocks"]
+    counts = torch.empty((H, M), dtype=torch.int32, device=qp.device)
+    idx = torch.empty((H, M, M), dtype=torch.int32, device=qp.device)
+    logits = torch.empty((H, M, M), dtype=torch.float64, device=qp.device) if return_logits else None
+    ws = _workspace(_lib.BSA_CALL_POOL_SELECT, layout, H, d, qp.device)
+    L = layout.c()
+    _lib.check("bsa_pool_select", lib.bsa_pool_select(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), H, d, _dtype(qp),
+        int(sparsity_1e4), float(tau), _ptr(counts), _ptr(idx), _ptr(logits), _ptr(ws),
+        ws.numel(), _stream()))
+    return (counts, idx, logits) if return_logits else (counts, idx)
+
+
+def attn_fwd(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: float = 0.0):
+    """bsa_attn_fwd: op [H, Np, d] (input dtype) and lse [H, Np] float32."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp, vp, counts, idx)
+    H, Np, d = qp.shape
+    op = torch.empty_like(qp)
+    lse = torch.empty((H, Np), dtype=torch.float32, device=qp.device)
+    L = layout.c()
+    _lib.check("bsa_attn_fwd", lib.bsa_attn_fwd(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(counts),
+        _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(op), _ptr(lse), None, 0, _stream()))
+    return op, lse
+
+
+def attn_bwd(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, idx,
+             scale: float = 0.0):
+    """bsa_attn_bwd: dqp, dkp, dvp [H, Np, d], float32 for any input dtype."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp, vp, op, dop, lse, counts, idx)
+    H, Np, d = qp.shape
+    dq, dk, dv = (torch.empty(qp.shape, dtype=torch.float32, device=qp.device) for _ in range(3))
+    ws = _workspace(_lib.BSA_CALL_ATTN_BWD, layout, H, d, qp.device)
+    L = layout.c()
+    _lib.check("bsa_attn_bwd", lib.bsa_attn_bwd(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), _ptr(dop),
+        _ptr(lse), _ptr(counts), _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
