@@ -193,6 +193,8 @@ bsa_status bsa_pool_select(const bsa_layout* L, const int32_t* zone_shape, const
  *              finite values; rows of empty query blocks get zeros
  *  lse         [heads, Np] float out (natural log); -inf for rows of empty
  *              query blocks
+ *  ws          workspace of bsa_workspace_size(BSA_CALL_ATTN_FWD, ...) bytes (a
+ *              per-block table; 0 bytes, ws may be NULL, when that size is 0)
  *  Supported: dtype BSA_BF16 or BSA_F32, d in {64, 128}, B in {64, 128}; the
  *  bf16 MFMA kernel runs for d = 128, B = 128, the others take a scalar kernel. */
 bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,

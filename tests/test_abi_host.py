@@ -78,14 +78,15 @@ def test_invalid_layouts(lib):
     assert _status_of_layout(lib, bad) == _lib.BSA_LAYOUT          # fixed: zone != shape
     bad = BSALayout(grid=(4, 16, 16), mode=7, zone=(2, 8, 8), shapes=((2, 8, 8),))
     assert _status_of_layout(lib, bad) == _lib.BSA_INVALID_ARG
-    assert "tile" in lib.bsa_last_error().decode() or lib.bsa_last_error()
+    assert "mode" in lib.bsa_last_error().decode()
 
 
 def test_workspace_sizes_positive(lib):
     L = BSALayout.dynamic((13, 90, 160)).c()
     for call in range(4):
-        n = lib.bsa_workspace_size(call, ctypes.byref(L), 4, 128)
-        assert (n > 0) == (call != _lib.BSA_CALL_ATTN_FWD)
+        assert lib.bsa_workspace_size(call, ctypes.byref(L), 4, 128) > 0
+    # the forward needs only its per-block table: 32 bytes per block
+    assert lib.bsa_workspace_size(_lib.BSA_CALL_ATTN_FWD, ctypes.byref(L), 4, 128) == 1920 * 32
     bad = BSALayout.fixed((0, 1, 1), (1, 8, 8)).c()
     assert lib.bsa_workspace_size(1, ctypes.byref(bad), 4, 128) == 0
 
@@ -114,7 +115,8 @@ def test_pool_select_validation(lib):
     assert _pool_select(lib, wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
     assert _pool_select(lib, ws=None) == _lib.BSA_WORKSPACE_TOO_SMALL
     assert _pool_select(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
-    assert "sparsity" in (lib.bsa_last_error().decode() + "sparsity")
+    assert _pool_select(lib, S=12000) == _lib.BSA_INVALID_ARG
+    assert "sparsity" in lib.bsa_last_error().decode()
 
 
 def _attn_fwd(lib, L=LAY, q=FAKE, d=128, dt=1, scale=0.0, lse=FAKE, zs=FAKE):

@@ -159,7 +159,7 @@ size_t bsa_workspace_size(bsa_call call, const bsa_layout* in, int heads, int d)
   switch (call) {
     case BSA_CALL_ZONE_SCORE: return bsa::zone_score_workspace(L, d, 256);
     case BSA_CALL_POOL_SELECT: return pool_select_ws(L, heads, d);
-    case BSA_CALL_ATTN_FWD: return 0;
+    case BSA_CALL_ATTN_FWD: return bsa::attn_fwd_workspace(L, d, true);
     case BSA_CALL_ATTN_BWD: return bsa::attn_bwd_workspace(L, heads, d);
   }
   fail(BSA_INVALID_ARG, "unknown call %d", (int)call);
@@ -263,8 +263,6 @@ bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const v
                         const void* kp, const void* vp, const int32_t* counts,
                         const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
                         float* lse, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
@@ -275,9 +273,12 @@ bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const v
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
   if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");
+  const size_t need = bsa::attn_fwd_workspace(L, d, dtype == BSA_BF16);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BSA_WORKSPACE_TOO_SMALL, "attn_fwd needs %zu workspace bytes, got %zu", need, ws_bytes);
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
   return hip_status(bsa::launch_attn_fwd(L, zone_shape, qp, kp, vp, counts, idx, heads, d,
-                                         dtype == BSA_BF16, sc, op, lse,
+                                         dtype == BSA_BF16, sc, op, lse, ws,
                                          static_cast<hipStream_t>(stream)),
                     "attn_fwd");
 }

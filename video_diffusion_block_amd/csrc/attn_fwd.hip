@@ -9,13 +9,16 @@
 // Two kernels:
 //  * attn_fwd_mfma: bf16, d = 128, 128-token blocks. One workgroup of 8
 //    wavefronts per (query block, head). Wave w owns queries 32*(w%4)..+32 and
-//    keys 64*(w/4)..+64 of every key block, so each K/V element read from LDS
-//    feeds two MFMA column tiles... (see the layout notes in the kernel). S is
-//    computed transposed (S^T = K Q^T) so that a lane holds one query's scores
-//    and the softmax row reductions stay inside the lane (one cross-half
-//    exchange); O^T = V^T P^T then keeps the per-query rescale lane-local too.
-//    K tiles (row-major) and V^T tiles are double-buffered in LDS; the next
-//    block's global loads are in flight while the current one is computed.
+//    keys 64*(w/4)..+64 of every listed key block. S is computed transposed
+//    (S^T = K Q^T on v_mfma_f32_32x32x16_bf16) so that a lane holds one query's
+//    scores: the softmax row reductions stay inside the lane (plus one exchange
+//    with the lane 32 away), and O^T = V^T P^T keeps the per-query rescale
+//    lane-local too. K and V tiles are stored row-major in LDS (XOR-swizzled,
+//    double-buffered); the V^T operand comes straight from the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16), so V is never transposed in
+//    registers. The next key block's global loads are in flight while the
+//    current one is computed. Pad keys of partial blocks are masked from a
+//    per-block 128-bit validity mask (computed once per call).
 //  * attn_fwd_scalar: any dtype (fp32 / bf16), d in {64, 128}, B in {64, 128}.
 //    One thread per query slot, fp32 online softmax, K/V staged through LDS as
 //    fp32. This is the exact-parity path (fp32 inputs) and the fallback.
@@ -83,51 +86,47 @@ __global__ __launch_bounds__(128) void attn_fwd_scalar(Lay L, const int32_t* zon
 // -------------------------------------------------------------- MFMA path --
 constexpr int kD = 128;          // head dim
 constexpr int kB = 128;          // tokens per block (queries and keys)
-constexpr int kKS = kD + 8;      // K tile row stride (bf16 elements): 272 bytes
-constexpr int kVS = kB + 4;      // V^T tile row stride (bf16 elements): 264 bytes
-constexpr int kKElems = kB * kKS;
-constexpr int kVElems = kD * kVS;
-constexpr int kStage = kKElems + kVElems;  // bf16 elements per pipeline stage
-constexpr int kThreads = 512;              // 8 wavefronts
-constexpr size_t kMfmaLds = 2 * kStage * sizeof(__bf16);
+constexpr int kTile = kB * kD;   // bf16 elements of one K or V tile (32 KB)
+constexpr int kStage = 2 * kTile;
+constexpr int kThreads = 512;    // 8 wavefronts
+constexpr size_t kMfmaLds = 2 * kStage * sizeof(__bf16);  // 128 KB, double-buffered K and V
 
-struct Prefetch {
-  uint4 k[4];
-  uint4 v[4];
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// K: thread t loads rows (t>>4) + 32*r, 16-byte chunk (t&15).
-// V: thread t loads rows 4*(t>>4) + r (r = 0..3), chunk (t&15), so that it can
-// write 4 consecutive keys of one d-column of V^T with one 8-byte store.
-__device__ inline void load_tile(Prefetch& pf, const __bf16* kbase, const __bf16* vbase, int tid) {
-  const int c = tid & 15, g = tid >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    pf.k[r] = *reinterpret_cast<const uint4*>(kbase + (size_t)(g + 32 * r) * kD + 8 * c);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    pf.v[r] = *reinterpret_cast<const uint4*>(vbase + (size_t)(4 * g + r) * kD + 8 * c);
+// LDS tiles are row-major (row = token, 256 bytes = 16 chunks of 16 bytes) with
+// an XOR swizzle of the chunk index: K chunk q of row r sits at q ^ (r & 15),
+// V chunk q at q ^ 4 (r & 3). With these, the K operand reads (16 rows x one
+// chunk per 16-lane phase), the V transposed reads (4 rows x 64 bytes per
+// 32-lane phase) and the tile stores (one row x 16 chunks) are bank-conflict
+// free.
+__device__ inline int kswz(int r, int q) { return q ^ (r & 15); }
+__device__ inline int vswz(int r, int q) { return q ^ ((r & 3) << 2); }
+
+// Thread t moves rows (t >> 4) + 32 i (i = 0..3), chunk t & 15, of K and V.
+#define BSA_LOAD_TILE(PK, PV, KBASE, VBASE)                                                    \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
+      PK[i_] = *reinterpret_cast<const u32x4*>((KBASE) + (size_t)(ld_g + 32 * i_) * kD + 8 * ld_c); \
+      PV[i_] = *reinterpret_cast<const u32x4*>((VBASE) + (size_t)(ld_g + 32 * i_) * kD + 8 * ld_c); \
+    }                                                                                          \
+  } while (0)
+
+#define BSA_STORE_TILE(PK, PV, SK, SV)                                                         \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
+      const int r_ = ld_g + 32 * i_;                                                           \
+      *reinterpret_cast<u32x4*>((SK) + r_ * kD + 8 * kswz(r_, ld_c)) = PK[i_];                 \
+      *reinterpret_cast<u32x4*>((SV) + r_ * kD + 8 * vswz(r_, ld_c)) = PV[i_];                 \
+    }                                                                                          \
+  } while (0)
+
+__device__ inline bf16x4 tr_read(const __bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
-__device__ inline void store_tile(const Prefetch& pf, __bf16* sk, __bf16* svt, int tid) {
-  const int c = tid & 15, g = tid >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    *reinterpret_cast<uint4*>(sk + (g + 32 * r) * kKS + 8 * c) = pf.k[r];
-  const unsigned short* v0 = reinterpret_cast<const unsigned short*>(&pf.v[0]);
-  const unsigned short* v1 = reinterpret_cast<const unsigned short*>(&pf.v[1]);
-  const unsigned short* v2 = reinterpret_cast<const unsigned short*>(&pf.v[2]);
-  const unsigned short* v3 = reinterpret_cast<const unsigned short*>(&pf.v[3]);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint2 w;
-    w.x = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
-    w.y = (uint32_t)v2[e] | ((uint32_t)v3[e] << 16);
-    *reinterpret_cast<uint2*>(svt + (8 * c + e) * kVS + 4 * g) = w;
-  }
-}
-
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_t* zone_shape,
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockMeta* meta,
                                                             const __bf16* qp, const __bf16* kp,
                                                             const __bf16* vp,
                                                             const int32_t* counts,
@@ -135,7 +134,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
                                                             __bf16* op, float* lse) {
   extern __shared__ __align__(16) __bf16 lds[];
   const int i = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = w & 3, kh = w >> 2;
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t row = (size_t)h * L.M + i;
@@ -161,6 +161,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
 
+  // Per-lane parts of the LDS offsets.
+  // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
+  const int koff = (64 * kh + l32) * kD;
+  // V transposed read: lane (G = lane >> 4, u = lane & 15) supplies the 8 bytes
+  // of row R + (u >> 2), columns 32t + 16(G & 1) + 4(u & 3) .. +4, and receives
+  // V[R + 0..3][32t + l32] (R = 64kh + 16c + 4hi, second read R + 8).
+  const int G = lane >> 4, u = lane & 15;
+  const int vy = u >> 2, vx = 2 * (G & 1) + ((u & 3) >> 1);
+  int voff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    voff[t] = (64 * kh + 4 * hi + vy) * kD + 8 * (4 * (t ^ vy) + vx) + 4 * (u & 1);
+
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -169,13 +182,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
   float m_run = -INFINITY;  // running max of s * scale * log2(e)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  Prefetch pf;
+  const int ld_c = tid & 15, ld_g = tid >> 4;
+  u32x4 pk[4], pv[4];
   {
     const int j = lst[0];
-    const __bf16* kb = kp + (head0 + (size_t)j * kB) * kD;
-    const __bf16* vb = vp + (head0 + (size_t)j * kB) * kD;
-    load_tile(pf, kb, vb, tid);
-    store_tile(pf, lds, lds + kKElems, tid);
+    BSA_LOAD_TILE(pk, pv, kp + (head0 + (size_t)j * kB) * kD, vp + (head0 + (size_t)j * kB) * kD);
+    BSA_STORE_TILE(pk, pv, lds, lds + kTile);
   }
   __syncthreads();
 
@@ -184,10 +196,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
     const bool more = it + 1 < n;
     if (more) {
       const int jn = lst[it + 1];
-      load_tile(pf, kp + (head0 + (size_t)jn * kB) * kD, vp + (head0 + (size_t)jn * kB) * kD, tid);
+      BSA_LOAD_TILE(pk, pv, kp + (head0 + (size_t)jn * kB) * kD, vp + (head0 + (size_t)jn * kB) * kD);
     }
     const __bf16* sk = lds + (it & 1) * kStage;
-    const __bf16* svt = sk + kKElems;
+    const __bf16* sv = sk + kTile;
 
     // S^T tiles: keys 64kh + 32kt + (0..31) x queries 32qg + (0..31)
     f32x16 s[2];
@@ -195,22 +207,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const __bf16* krow = sk + (64 * kh + 32 * kt + l32) * kKS + 8 * hi;
+      const __bf16* krow = sk + koff + 32 * kt * kD;
 #pragma unroll
       for (int st = 0; st < 8; ++st)
-        s[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * st), qf[st], s[kt]);
+        s[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * ((2 * st + hi) ^ (l32 & 15))),
+                             qf[st], s[kt]);
     }
 
-    // pad keys of a partial key block
-    const Box xj = block_box(L, zone_shape, j);
-    if (xj.count() < kB) {
+    // pad keys of a partial key block: bit r of the block's mask = slot r real
+    const int cnt = meta[j].count;
+    if (cnt < kB) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t word = meta[j].mask[2 * kh + kt] >> (4 * hi);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * kh + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (!slot_real(xj, key)) s[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (!((word >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = -INFINITY;
+      }
     }
 
     // online softmax (log2 domain)
@@ -235,27 +248,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
         pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
       }
     l_run = fmaf(l_run, alpha, psum);
+    if (__ballot(alpha != 1.f)) {  // rescale only when some running max moved
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
 
     // O^T (d x queries) += V^T (d x keys) P^T (keys x queries).
     // P^T fragment c (c = 0..3) holds keys 16c + 8(jj/4) + 4hi + jj%4 (jj = 0..7)
-    // of this wave's 64 keys; the V^T A-operand uses the same key order.
+    // of this wave's 64 keys; the transposed V reads produce the same key order.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const __bf16* vrow = svt + (32 * t + l32) * kVS + 64 * kh + 4 * hi;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * c);
-        const bf16x4 up = *reinterpret_cast<const bf16x4*>(vrow + 16 * c + 8);
+        const __bf16* p0 = sv + voff[t] + 16 * c * kD;
+        const bf16x4 lo = tr_read(p0);
+        const bf16x4 up = tr_read(p0 + 8 * kD);
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
         o[t] = mfma32x32x16(a, pf8[c], o[t]);
       }
     }
 
-    if (more) store_tile(pf, lds + ((it + 1) & 1) * kStage, lds + ((it + 1) & 1) * kStage + kKElems, tid);
+    if (more) {
+      __bf16* nk = lds + ((it + 1) & 1) * kStage;
+      BSA_STORE_TILE(pk, pv, nk, nk + kTile);
+    }
     __syncthreads();
   }
 
@@ -296,6 +314,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const int32_
   }
 }
 
+#undef BSA_LOAD_TILE
+#undef BSA_STORE_TILE
+
 template <typename T>
 hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
                          const void* vp, const int32_t* counts, const int32_t* idx, int heads,
@@ -324,16 +345,23 @@ hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp
 
 bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16) { return bf16 && d == kD && L.B == kB; }
 
+size_t attn_fwd_workspace(const Lay& L, int d, bool bf16) {
+  return attn_fwd_uses_mfma(L, d, bf16) ? (size_t)L.M * sizeof(BlockMeta) : 0;
+}
+
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, hipStream_t st) {
+                           void* op, float* lse, void* ws, hipStream_t st) {
   if (attn_fwd_uses_mfma(L, d, bf16)) {
+    BlockMeta* meta = static_cast<BlockMeta*>(ws);
+    hipError_t e = launch_block_meta(L, zone_shape, meta, st);
+    if (e != hipSuccess) return e;
     hipFuncSetAttribute(reinterpret_cast<const void*>(attn_fwd_mfma),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLds);
     dim3 grid(L.M, heads);
     attn_fwd_mfma<<<grid, kThreads, kMfmaLds, st>>>(
-        L, zone_shape, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
+        L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
         static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e, static_cast<__bf16*>(op),
         lse);
     return hipGetLastError();

@@ -28,11 +28,24 @@ hipError_t launch_select(const Lay& L, const int32_t* zone_shape, const double* 
                          int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
                          hipStream_t st);
 
-// Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel.
+// Per-block facts the attention kernels need inside their loops: bit r of
+// mask (r < B, 32 slots per word) = slot r is real; count = real slots.
+struct BlockMeta {
+  uint32_t mask[4];
+  int32_t count;
+  int32_t pad[3];
+};
+hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
+                             hipStream_t st);
+
+// Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel, which
+// needs attn_fwd_workspace() bytes (the block table).
+bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16);
+size_t attn_fwd_workspace(const Lay& L, int d, bool bf16);
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, hipStream_t st);
+                           void* op, float* lse, void* ws, hipStream_t st);
 
 // Attention backward.
 size_t attn_bwd_workspace(const Lay& L, int heads, int d);

@@ -44,7 +44,27 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
   }
 }
 
+__global__ __launch_bounds__(256) void block_meta_kernel(Lay L, const int32_t* zone_shape,
+                                                         BlockMeta* meta) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= L.M) return;
+  const Box x = block_box(L, zone_shape, b);
+  BlockMeta m;
+  for (int w = 0; w < 4; ++w) m.mask[w] = 0u;
+  for (int r = 0; r < L.B && r < 128; ++r)
+    if (slot_real(x, r)) m.mask[r >> 5] |= 1u << (r & 31);
+  m.count = x.count();
+  m.pad[0] = m.pad[1] = m.pad[2] = 0;
+  meta[b] = m;
+}
+
 }  // namespace
+
+hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
+                             hipStream_t st) {
+  block_meta_kernel<<<(L.M + 255) / 256, 256, 0, st>>>(L, zone_shape, meta);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
                           const void* const* src, void* const* dst, int heads, int row_bytes,

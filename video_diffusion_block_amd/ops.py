@@ -171,10 +171,12 @@ def attn_fwd(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: floa
     H, Np, d = qp.shape
     op = torch.empty_like(qp)
     lse = torch.empty((H, Np), dtype=torch.float32, device=qp.device)
+    ws = _workspace(_lib.BSA_CALL_ATTN_FWD, layout, H, d, qp.device)
     L = layout.c()
     _lib.check("bsa_attn_fwd", lib.bsa_attn_fwd(
         ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(counts),
-        _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(op), _ptr(lse), None, 0, _stream()))
+        _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(op), _ptr(lse), _ptr(ws), ws.numel(),
+        _stream()))
     return op, lse
 
 
