@@ -87,52 +87,86 @@ __global__ __launch_bounds__(128) void attn_fwd_scalar(Lay L, const int32_t* zon
 constexpr int kD = 128;          // head dim
 constexpr int kB = 128;          // tokens per block (queries and keys)
 constexpr int kTile = kB * kD;   // bf16 elements of one K or V tile (32 KB)
-constexpr int kStage = 2 * kTile;
 constexpr int kThreads = 512;    // 8 wavefronts
-constexpr size_t kMfmaLds = 2 * kStage * sizeof(__bf16);  // 128 KB, double-buffered K and V
+constexpr float kLazy = 8.f;     // log2 headroom of the lazily updated softmax max
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS tiles are row-major (row = token, 256 bytes = 16 chunks of 16 bytes) with
 // an XOR swizzle of the chunk index: K chunk q of row r sits at q ^ (r & 15),
 // V chunk q at q ^ 4 (r & 3). With these, the K operand reads (16 rows x one
-// chunk per 16-lane phase), the V transposed reads (4 rows x 64 bytes per
-// 32-lane phase) and the tile stores (one row x 16 chunks) are bank-conflict
-// free.
+// chunk per 16-lane phase) and the V transposed reads (4 rows x 64 bytes per
+// 32-lane phase) are bank-conflict free.
 __device__ inline int kswz(int r, int q) { return q ^ (r & 15); }
 __device__ inline int vswz(int r, int q) { return q ^ ((r & 3) << 2); }
 
-// Thread t moves rows (t >> 4) + 32 i (i = 0..3), chunk t & 15, of K and V.
-#define BSA_LOAD_TILE(PK, PV, KBASE, VBASE)                                                    \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
-      PK[i_] = *reinterpret_cast<const u32x4*>((KBASE) + (size_t)(ld_g + 32 * i_) * kD + 8 * ld_c); \
-      PV[i_] = *reinterpret_cast<const u32x4*>((VBASE) + (size_t)(ld_g + 32 * i_) * kD + 8 * ld_c); \
-    }                                                                                          \
-  } while (0)
+// Tiles arrive by direct global->LDS loads (16 bytes per lane): load m
+// (0..3) of wave w fills LDS slots (8m + w) * 64 + lane, i.e. row
+// 4 (8m + w) + lane / 16, physical chunk lane % 16; the lane therefore fetches
+// the logical chunk that the swizzle puts there.
+template <bool kIsV>
+__device__ inline void dma_tile(__bf16* tile, const __bf16* gtile, int w, int lane) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = 4 * (8 * m + w) + (lane >> 4);
+    const int q = kIsV ? vswz(r, lane & 15) : kswz(r, lane & 15);
+    __builtin_amdgcn_global_load_lds(gtile + r * kD + 8 * q, (lds_void*)(tile + (8 * m + w) * 512),
+                                     16, 0, 0);
+  }
+}
 
-#define BSA_STORE_TILE(PK, PV, SK, SV)                                                         \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                         \
-      const int r_ = ld_g + 32 * i_;                                                           \
-      *reinterpret_cast<u32x4*>((SK) + r_ * kD + 8 * kswz(r_, ld_c)) = PK[i_];                 \
-      *reinterpret_cast<u32x4*>((SV) + r_ * kD + 8 * vswz(r_, ld_c)) = PV[i_];                 \
-    }                                                                                          \
-  } while (0)
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ inline bf16x4 tr_read(const __bf16* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockMeta* meta,
-                                                            const __bf16* qp, const __bf16* kp,
-                                                            const __bf16* vp,
-                                                            const int32_t* counts,
-                                                            const int32_t* idx, float scale_log2,
-                                                            __bf16* op, float* lse) {
-  extern __shared__ __align__(16) __bf16 lds[];
+// S^T = K Q^T for this wave's 64 keys of the block in `sk` (two 32x32 tiles).
+// The eight K fragments of a tile are loaded in one batch before its MFMAs so
+// that LDS latency overlaps the other tile's matrix work.
+__device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int kswz_lane,
+                                const bf16x8 (&qf)[8], int hi) {
+  bf16x8 a[2][8];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      a[kt][st] = *reinterpret_cast<const bf16x8*>(sk + koff + 32 * kt * kD +
+                                                   8 * ((2 * st + hi) ^ kswz_lane));
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+  }
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[kt][st], qf[st], s[kt]);
+}
+
+// Pad keys of a partial key block: bit r of the block's mask = slot r real.
+// Lane (l32, hi) holds keys 64kh + 32kt + 8(r/4) + 4hi + r%4 in element r.
+__device__ inline void mask_pad_keys(f32x16 (&s)[2], const BlockMeta& m, int kh, int hi) {
+  if (m.count >= 128) return;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const uint32_t word = m.mask[2 * kh + kt] >> (4 * hi);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!((word >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = -INFINITY;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
+    Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
+    const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ idx, float scale_log2,
+    __bf16* __restrict__ op, float* __restrict__ lse) {
+  __shared__ __align__(16) __bf16 sK[3][kTile];  // 3 x 32 KB
+  __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB: 160 KB in all
   const int i = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -152,6 +186,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockM
     }
     return;
   }
+  const __bf16* kh0 = kp + head0 * kD;
+  const __bf16* vh0 = vp + head0 * kD;
+
+  // prologue DMA: K0, K1, V0
+  dma_tile<false>(sK[0], kh0 + (size_t)lst[0] * kTile, w, lane);
+  if (n > 1) dma_tile<false>(sK[1], kh0 + (size_t)lst[1] * kTile, w, lane);
+  dma_tile<true>(sV[0], vh0 + (size_t)lst[0] * kTile, w, lane);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds Q[q][16s + 8hi .. +8].
   bf16x8 qf[8];
@@ -161,9 +202,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockM
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
 
-  // Per-lane parts of the LDS offsets.
   // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
   const int koff = (64 * kh + l32) * kD;
+  const int kswz_lane = l32 & 15;
   // V transposed read: lane (G = lane >> 4, u = lane & 15) supplies the 8 bytes
   // of row R + (u >> 2), columns 32t + 16(G & 1) + 4(u & 3) .. +4, and receives
   // V[R + 0..3][32t + l32] (R = 64kh + 16c + 4hi, second read R + 8).
@@ -179,119 +220,107 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockM
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = -INFINITY;  // running max of s * scale * log2(e)
+  float m_run = -INFINITY;  // reference max of s * scale * log2(e)
   float l_run = 0.f;        // this lane's share of the running sum
 
-  const int ld_c = tid & 15, ld_g = tid >> 4;
-  u32x4 pk[4], pv[4];
-  {
-    const int j = lst[0];
-    BSA_LOAD_TILE(pk, pv, kp + (head0 + (size_t)j * kB) * kD, vp + (head0 + (size_t)j * kB) * kD);
-    BSA_STORE_TILE(pk, pv, lds, lds + kTile);
-  }
+  // The two wavefronts of each SIMD (kh = 0 and kh = 1) walk the blocks in
+  // opposite phase orders so that one's matrix work overlaps the other's
+  // exponentials: kh = 0 runs S_j -> softmax_j -> PV_j, kh = 1 runs
+  // softmax_j -> PV_j -> S_{j+1}. K is triple-buffered (K_j, K_{j+1} in use,
+  // K_{j+2} streaming in), V double-buffered.
+  f32x16 s_cur[2];
+  wait_dma();
   __syncthreads();
-
-  for (int it = 0; it < n; ++it) {
-    const int j = lst[it];
-    const bool more = it + 1 < n;
-    if (more) {
-      const int jn = lst[it + 1];
-      BSA_LOAD_TILE(pk, pv, kp + (head0 + (size_t)jn * kB) * kD, vp + (head0 + (size_t)jn * kB) * kD);
-    }
-    const __bf16* sk = lds + (it & 1) * kStage;
-    const __bf16* sv = sk + kTile;
-
-    // S^T tiles: keys 64kh + 32kt + (0..31) x queries 32qg + (0..31)
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const __bf16* krow = sk + koff + 32 * kt * kD;
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-        s[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * ((2 * st + hi) ^ (l32 & 15))),
-                             qf[st], s[kt]);
+  if (kh == 1) {
+    qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi);
+    mask_pad_keys(s_cur, meta[lst[0]], kh, hi);
+  }
+  int kb = 0;  // K buffer of block j (j mod 3)
+  for (int j = 0; j < n; ++j) {
+    const int kb1 = kb == 2 ? 0 : kb + 1;   // block j+1
+    const int kb2 = kb1 == 2 ? 0 : kb1 + 1; // block j+2
+    const int vb = j & 1;
+    if (j + 2 < n) dma_tile<false>(sK[kb2], kh0 + (size_t)lst[j + 2] * kTile, w, lane);
+    if (j + 1 < n) dma_tile<true>(sV[vb ^ 1], vh0 + (size_t)lst[j + 1] * kTile, w, lane);
+    if (kh == 0) {
+      qk_tiles(s_cur, sK[kb], koff, kswz_lane, qf, hi);
+      mask_pad_keys(s_cur, meta[lst[j]], kh, hi);
     }
 
-    // pad keys of a partial key block: bit r of the block's mask = slot r real
-    const int cnt = meta[j].count;
-    if (cnt < kB) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint32_t word = meta[j].mask[2 * kh + kt] >> (4 * hi);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((word >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = -INFINITY;
-      }
-    }
-
-    // online softmax (log2 domain)
+    // Online softmax (log2 domain) with a lazily updated reference max: the
+    // exponent base m_run moves only when a row max exceeds it by more than
+    // kLazy (then p <= 2^kLazy, safe in bf16 and fp32), so O is rarely rescaled.
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    if (__ballot(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pf8[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kt][r], scale_log2, -m_use));
+        const float p = exp2_fast(fmaf(s_cur[kt][r], scale_log2, -m_use));
         psum += p;
         pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.f)) {  // rescale only when some running max moved
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-    }
+    l_run += psum;
 
     // O^T (d x queries) += V^T (d x keys) P^T (keys x queries).
     // P^T fragment c (c = 0..3) holds keys 16c + 8(jj/4) + 4hi + jj%4 (jj = 0..7)
     // of this wave's 64 keys; the transposed V reads produce the same key order.
+    // The four V^T fragments of a d-tile are read in one batch.
+    const __bf16* sv = sV[vb];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      bf16x8 a[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const __bf16* p0 = sv + voff[t] + 16 * c * kD;
         const bf16x4 lo = tr_read(p0);
         const bf16x4 up = tr_read(p0 + 8 * kD);
-        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[t] = mfma32x32x16(a, pf8[c], o[t]);
+        a[c] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[t] = mfma32x32x16(a[c], pf8[c], o[t]);
     }
-
-    if (more) {
-      __bf16* nk = lds + ((it + 1) & 1) * kStage;
-      BSA_STORE_TILE(pk, pv, nk, nk + kTile);
+    if (kh == 1 && j + 1 < n) {
+      qk_tiles(s_cur, sK[kb1], koff, kswz_lane, qf, hi);
+      mask_pad_keys(s_cur, meta[lst[j + 1]], kh, hi);
     }
+    kb = kb1;
+    wait_dma();
     __syncthreads();
   }
 
   // merge the two key halves (waves w and w+4 share their 32 queries)
   l_run += __shfl_xor(l_run, 32);
-  float* xch = reinterpret_cast<float*>(lds);  // [4 waves][64 lanes][66 floats]
-  float* mine = xch + (qg * 64 + lane) * 66;
+  float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;  // 64 KB
+  float* xm = reinterpret_cast<float*>(&sV[0][0]) + (qg * 64 + lane) * 2;
   if (kh == 1) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mine[16 * t + r] = o[t][r];
-    mine[64] = m_run;
-    mine[65] = l_run;
+      for (int r = 0; r < 16; ++r) xo[16 * t + r] = o[t][r];
+    xm[0] = m_run;
+    xm[1] = l_run;
   }
   __syncthreads();
   if (kh == 0) {
-    const float m2 = mine[64], l2 = mine[65];
+    const float m2 = xm[0], l2 = xm[1];
     const float mt = fmaxf(m_run, m2);
     const float mu = mt == -INFINITY ? 0.f : mt;
     const float a1 = exp2_fast(m_run - mu), a2 = exp2_fast(m2 - mu);
@@ -306,16 +335,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(Lay L, const BlockM
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int r = 4 * g + rr;
-          v[rr] = (__bf16)((o[t][r] * a1 + mine[16 * t + r] * a2) * inv);
+          v[rr] = (__bf16)((o[t][r] * a1 + xo[16 * t + r] * a2) * inv);
         }
         *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * hi) = v;
       }
     if (hi == 0) lse[head0 + (size_t)i * kB + q] = (mt + log2f(lt)) * kLn2;
   }
 }
-
-#undef BSA_LOAD_TILE
-#undef BSA_STORE_TILE
 
 template <typename T>
 hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
@@ -357,10 +383,8 @@ hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* 
     BlockMeta* meta = static_cast<BlockMeta*>(ws);
     hipError_t e = launch_block_meta(L, zone_shape, meta, st);
     if (e != hipSuccess) return e;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(attn_fwd_mfma),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLds);
     dim3 grid(L.M, heads);
-    attn_fwd_mfma<<<grid, kThreads, kMfmaLds, st>>>(
+    attn_fwd_mfma<<<grid, kThreads, 0, st>>>(
         L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
         static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e, static_cast<__bf16*>(op),
         lse);
