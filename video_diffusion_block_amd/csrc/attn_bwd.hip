@@ -199,6 +199,321 @@ __global__ __launch_bounds__(128) void dq_scalar(Lay L, const int32_t* zone_shap
   for (int e = 0; e < D; ++e) dqp[qoff + e] = real ? dq[e] : 0.f;
 }
 
+// ------------------------------------------------------------- MFMA path --
+// bf16, d = 128, 128-token blocks. Tiles live in LDS row-major (256-byte rows of
+// 16 chunks) with the chunk swizzle q ^ (4 (r & 3) + ((r >> 2) & 3)), which is
+// bank-conflict free both for row reads (16 consecutive rows, one chunk) and
+// for the gfx950 transposing reads (4 consecutive rows x 4 chunks).
+constexpr int kD = 128;
+constexpr int kB = 128;
+constexpr int kTile = kB * kD;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline int uswz_f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__device__ inline bf16x4 tr_read(const __bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Direct global->LDS copy of one 128 x 128 bf16 tile by kWaves wavefronts:
+// load m of wave w fills LDS slots (kWaves m + w) * 64 + lane (row r = slot/16,
+// physical chunk lane % 16), fetching the logical chunk the swizzle puts there.
+template <int kWaves>
+__device__ inline void dma_tile(__bf16* tile, const __bf16* gtile, int w, int lane) {
+#pragma unroll
+  for (int m = 0; m < 32 / kWaves; ++m) {
+    const int r = 4 * (kWaves * m + w) + (lane >> 4);
+    const int q = (lane & 15) ^ uswz_f(r);
+    __builtin_amdgcn_global_load_lds(gtile + r * kD + 8 * q,
+                                     (lds_void*)(tile + (kWaves * m + w) * 512), 16, 0, 0);
+  }
+}
+
+// Offsets (bf16 elements) of the two transposed reads that give lane
+// (G = lane/16, u = lane%16) the A operand rows [R + 0..3] and [R + 8..11] of
+// column 32t + l32, R = base row + 16c + 4hi (add 16c*kD for k-step c).
+__device__ inline void tr_offsets(int (&o1)[4], int (&o2)[4], int row0, int lane) {
+  const int G = lane >> 4, u = lane & 15, hi = lane >> 5;
+  const int vy = u >> 2, vx = 2 * (G & 1) + ((u & 3) >> 1);
+  const int r1 = row0 + 4 * hi + vy, r2 = r1 + 8;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    o1[t] = r1 * kD + 8 * ((4 * t + vx) ^ uswz_f(r1)) + 4 * (u & 1);
+    o2[t] = r2 * kD + 8 * ((4 * t + vx) ^ uswz_f(r2)) + 4 * (u & 1);
+  }
+}
+
+// dQ for one (query block, head): for every listed key block j,
+//   S^T = K Q^T, dP^T = V dO^T, P^T = exp(S^T scale - lse), dS^T = P^T (dP^T - D),
+//   dQ^T += K^T dS^T  (K^T through transposed LDS reads).
+// 8 wavefronts: wave w owns queries 32 (w % 4) .. +32 and keys 64 (w / 4) .. +64.
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
+    Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
+    const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
+    const __bf16* __restrict__ dop, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, float scale, float* __restrict__ dqp) {
+  __shared__ __align__(16) __bf16 sK[2][kTile];
+  __shared__ __align__(16) __bf16 sV[2][kTile];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = w & 3, kh = w >> 2;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t row = (size_t)h * L.M + i;
+  const int n = counts[row];
+  const int32_t* lst = idx + row * L.M;
+  const size_t head0 = (size_t)h * L.Np;
+  const int q = 32 * qg + l32;
+  const size_t qrow = head0 + (size_t)i * kB + q;
+  const bool q_real = (meta[i].mask[q >> 5] >> (q & 31)) & 1u;
+
+  if (n == 0) {
+    if (kh == 0)
+      for (int e = 8 * hi; e < kD; e += 16)
+        *reinterpret_cast<f32x4*>(dqp + qrow * kD + e) = f32x4{0.f, 0.f, 0.f, 0.f},
+        *reinterpret_cast<f32x4*>(dqp + qrow * kD + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const __bf16* kh0 = kp + head0 * kD;
+  const __bf16* vh0 = vp + head0 * kD;
+  dma_tile<8>(sK[0], kh0 + (size_t)lst[0] * kTile, w, lane);
+  dma_tile<8>(sV[0], vh0 + (size_t)lst[0] * kTile, w, lane);
+
+  bf16x8 qf[8], dof[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * kD + 16 * s + 8 * hi);
+    dof[s] = *reinterpret_cast<const bf16x8*>(dop + qrow * kD + 16 * s + 8 * hi);
+  }
+  const float c2 = scale * kLog2e;
+  const float lse2 = lse[qrow] * kLog2e;
+  const float dq_d = delta[qrow];
+
+  const int rowA = 64 * kh + l32;          // row-read operand rows (+32 kt)
+  const int fA = uswz_f(l32);
+  int o1[4], o2[4];
+  tr_offsets(o1, o2, 64 * kh, lane);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  for (int jj = 0; jj < n; ++jj) {
+    const int b = jj & 1;
+    wait_dma();
+    __syncthreads();
+    if (jj + 1 < n) {
+      dma_tile<8>(sK[b ^ 1], kh0 + (size_t)lst[jj + 1] * kTile, w, lane);
+      dma_tile<8>(sV[b ^ 1], vh0 + (size_t)lst[jj + 1] * kTile, w, lane);
+    }
+    const __bf16* sk = sK[b];
+    const __bf16* sv = sV[b];
+    f32x16 st[2], dpt[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[kt][r] = dpt[kt][r] = 0.f;
+      const int ro = (rowA + 32 * kt) * kD;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int off = ro + 8 * ((2 * s + hi) ^ fA);
+        st[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sk + off), qf[s], st[kt]);
+        dpt[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sv + off), dof[s], dpt[kt]);
+      }
+    }
+    const BlockMeta& mj = meta[lst[jj]];
+    const bool partial = mj.count < kB;
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t word = mj.mask[2 * kh + kt] >> (4 * hi);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_fast(fmaf(st[kt][r], c2, -lse2));
+        if (partial && !((word >> (8 * (r >> 2) + (r & 3))) & 1u)) p = 0.f;
+        dsf[2 * kt + (r >> 3)][r & 7] = (__bf16)(p * (dpt[kt][r] - dq_d));
+      }
+    }
+    // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x4 lo = tr_read(sk + o1[t] + 16 * c * kD);
+        const bf16x4 up = tr_read(sk + o2[t] + 16 * c * kD);
+        a[c] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[t] = mfma32x32x16(a[c], dsf[c], acc[t]);
+    }
+  }
+  wait_dma();
+  __syncthreads();
+  // sum the two key halves (waves w and w+4 share their 32 queries)
+  float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[16 * t + r] = acc[t][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float* out = dqp + qrow * kD;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          v[rr] = q_real ? (acc[t][4 * g + rr] + xo[16 * t + 4 * g + rr]) * scale : 0.f;
+        *reinterpret_cast<f32x4*>(out + 32 * t + 8 * g + 4 * hi) = v;
+      }
+  }
+}
+
+// dK and dV for one (key block, head): for every query block i whose list
+// holds the key block (key-major list),
+//   S = Q K^T, dP = dO V^T, P = exp(S scale - lse), dS = P (dP - D),
+//   dV += P^T dO, dK += dS^T Q   (dO and Q through transposed LDS reads).
+// 4 wavefronts (one per SIMD): wave w owns keys 32w .. +32; K and V fragments
+// stay in registers; Q_i, dO_i, lse_i and D_i stream through LDS.
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
+    Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
+    const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
+    const __bf16* __restrict__ dop, const float* __restrict__ lse,
+    const float* __restrict__ delta, const int32_t* __restrict__ tcounts,
+    const int32_t* __restrict__ tidx, float scale, float* __restrict__ dkp,
+    float* __restrict__ dvp) {
+  __shared__ __align__(16) __bf16 sQ[2][kTile];
+  __shared__ __align__(16) __bf16 sO[2][kTile];
+  __shared__ __align__(16) float sL[2][kB];
+  __shared__ __align__(16) float sD[2][kB];
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t row = (size_t)h * L.M + j;
+  const int n = tcounts[row];
+  const int32_t* lst = tidx + row * L.M;
+  const size_t head0 = (size_t)h * L.Np;
+  const size_t kbase = head0 + (size_t)j * kB;   // first slot of the key block
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+
+  if (n > 0) {
+    const __bf16* qh0 = qp + head0 * kD;
+    const __bf16* oh0 = dop + head0 * kD;
+    auto dma_rows = [&](int buf, int ib) {
+      dma_tile<4>(sQ[buf], qh0 + (size_t)ib * kTile, w, lane);
+      dma_tile<4>(sO[buf], oh0 + (size_t)ib * kTile, w, lane);
+      if (w == 0 && lane < 32) {
+        const size_t q0 = head0 + (size_t)ib * kB;
+        __builtin_amdgcn_global_load_lds(lse + q0 + 4 * lane, (lds_void*)&sL[buf][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(delta + q0 + 4 * lane, (lds_void*)&sD[buf][0], 16, 0, 0);
+      }
+    };
+    dma_rows(0, lst[0]);
+
+    // K and V fragments (B operands of S = Q K^T and dP = dO V^T):
+    // lane holds K[key 32w + l32][16s + 8hi .. +8].
+    bf16x8 kf[8], vf[8];
+    const size_t krow = (kbase + 32 * w + l32) * kD + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(kp + krow + 16 * s);
+      vf[s] = *reinterpret_cast<const bf16x8*>(vp + krow + 16 * s);
+    }
+    const float c2 = scale * kLog2e;
+    const int fA = uswz_f(l32);
+    int o1[4], o2[4];
+    tr_offsets(o1, o2, 0, lane);
+
+    for (int ii = 0; ii < n; ++ii) {
+      const int b = ii & 1;
+      wait_dma();
+      __syncthreads();
+      if (ii + 1 < n) dma_rows(b ^ 1, lst[ii + 1]);
+      const __bf16* sq = sQ[b];
+      const __bf16* so = sO[b];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        // S, dP tiles: queries 32qt + (0..31) x keys 32w + (0..31)
+        f32x16 sc, dpc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = dpc[r] = 0.f;
+        const int ro = (32 * qt + l32) * kD;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int off = ro + 8 * ((2 * s + hi) ^ fA);
+          sc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sq + off), kf[s], sc);
+          dpc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(so + off), vf[s], dpc);
+        }
+        // element r belongs to query 32qt + 8(r/4) + 4hi + r%4
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[b][32 * qt + 8 * g + 4 * hi]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[b][32 * qt + 8 * g + 4 * hi]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = 4 * g + rr;
+            const float p = exp2_fast(fmaf(sc[r], c2, -l4[rr] * kLog2e));
+            pf[r >> 3][r & 7] = (__bf16)p;
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dpc[r] - d4[rr]));
+          }
+        }
+        // dV (keys x d) += P^T (keys x queries) dO (queries x d), and
+        // dK += dS^T Q: k-step c covers queries 32qt + 16c + ..., read transposed.
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int base = (32 * qt + 16 * c) * kD;
+            const bf16x8 ob = __builtin_shufflevector(tr_read(so + base + o1[t]),
+                                                      tr_read(so + base + o2[t]), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
+            const bf16x8 qb = __builtin_shufflevector(tr_read(sq + base + o1[t]),
+                                                      tr_read(sq + base + o2[t]), 0, 1, 2, 3,
+                                                      4, 5, 6, 7);
+            dv[t] = mfma32x32x16(pf[c], ob, dv[t]);
+            dk[t] = mfma32x32x16(dsf[c], qb, dk[t]);
+          }
+        }
+      }
+    }
+  }
+  // lane holds rows key 32w + 8(r/4) + 4hi + r%4, column d = 32t + l32
+  const BlockMeta& mj = meta[j];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
+    const bool real = (mj.mask[key >> 5] >> (key & 31)) & 1u;
+    float* dkr = dkp + (kbase + key) * kD + l32;
+    float* dvr = dvp + (kbase + key) * kD + l32;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dkr[32 * t] = real ? dk[t][r] * scale : 0.f;
+      dvr[32 * t] = real ? dv[t][r] : 0.f;
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_scalar(const Lay& L, const int32_t* zs, const T* q, const T* k, const T* v,
                              const T* dO, const float* lse, const float* delta,
@@ -221,7 +536,8 @@ hipError_t launch_bwd_scalar(const Lay& L, const int32_t* zs, const T* q, const 
 
 }  // namespace
 
-// Workspace: delta [H, Np] f32 | bitmap [H, M, words] u32 | tcounts [H, M] | tidx [H, M, M]
+// Workspace: delta [H, Np] f32 | bitmap [H, M, words] u32 | tcounts [H, M] |
+// tidx [H, M, M] | block table [M]
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attn_bwd_workspace(const Lay& L, int heads, int d) {
@@ -230,7 +546,8 @@ size_t attn_bwd_workspace(const Lay& L, int heads, int d) {
   return align256((size_t)heads * L.Np * sizeof(float)) +
          align256((size_t)heads * L.M * words * sizeof(uint32_t)) +
          align256((size_t)heads * L.M * sizeof(int32_t)) +
-         align256((size_t)heads * L.M * L.M * sizeof(int32_t));
+         align256((size_t)heads * L.M * L.M * sizeof(int32_t)) +
+         align256((size_t)L.M * sizeof(BlockMeta));
 }
 
 hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* qp,
@@ -247,6 +564,8 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   int32_t* tcounts = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)heads * L.M * sizeof(int32_t));
   int32_t* tidx = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)heads * L.M * L.M * sizeof(int32_t));
+  BlockMeta* meta = reinterpret_cast<BlockMeta*>(p);
 
   const long long rows = (long long)heads * L.Np;
   const unsigned dgrid = (unsigned)((rows + 3) / 4);
@@ -260,6 +579,22 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   transpose_kernel<<<dim3(L.M, heads), 256, 0, st>>>(L, bitmap, words, tcounts, tidx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+
+  if (bf16 && d == kD && L.B == kB) {
+    e = launch_block_meta(L, zone_shape, meta, st);
+    if (e != hipSuccess) return e;
+    const __bf16* q = static_cast<const __bf16*>(qp);
+    const __bf16* k = static_cast<const __bf16*>(kp);
+    const __bf16* v = static_cast<const __bf16*>(vp);
+    const __bf16* dO = static_cast<const __bf16*>(dop);
+    attn_bwd_dkdv_mfma<<<dim3(L.M, heads), 256, 0, st>>>(L, meta, q, k, v, dO, lse, delta,
+                                                        tcounts, tidx, scale,
+                                                        static_cast<float*>(dkp),
+                                                        static_cast<float*>(dvp));
+    attn_bwd_dq_mfma<<<dim3(L.M, heads), 512, 0, st>>>(L, meta, q, k, v, dO, lse, delta, counts,
+                                                      idx, scale, static_cast<float*>(dqp));
+    return hipGetLastError();
+  }
 
 #define BSA_BWD(T, D)                                                                        \
   return launch_bwd_scalar<T, D>(                                                            \
