@@ -105,7 +105,8 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t pool_select_ws(const bsa::Lay& L, int heads, int d) {
   return 2 * al256((size_t)heads * L.M * d * sizeof(double)) +
-         al256((size_t)heads * L.M * L.M * sizeof(double));
+         al256((size_t)heads * L.M * L.M * sizeof(double)) +
+         al256((size_t)L.M * sizeof(bsa::BlockMeta));
 }
 
 bsa_status hip_status(hipError_t e, const char* what) {
@@ -248,14 +249,18 @@ bsa_status bsa_pool_select(const bsa_layout* in, const int32_t* zone_shape, cons
   double* kbar = reinterpret_cast<double*>(p);
   p += al256((size_t)heads * L.M * d * sizeof(double));
   double* logits = pooled_logits ? pooled_logits : reinterpret_cast<double*>(p);
+  p += al256((size_t)heads * L.M * L.M * sizeof(double));
+  bsa::BlockMeta* meta = reinterpret_cast<bsa::BlockMeta*>(p);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == BSA_BF16;
-  hipError_t e = bsa::launch_pool(L, zone_shape, qp, kp, heads, d, bf16, qbar, kbar, st);
+  hipError_t e = bsa::launch_block_meta(L, zone_shape, meta, st);
   if (e == hipSuccess)
-    e = bsa::launch_pooled_logits(L, zone_shape, qbar, kbar, heads, d, 1.0 / sqrt((double)d),
-                                  logits, st);
+    e = bsa::launch_pool(L, meta, qp, kp, heads, d, bf16, qbar, kbar, st);
   if (e == hipSuccess)
-    e = bsa::launch_select(L, zone_shape, logits, heads, sparsity_1e4, tau, counts, idx, st);
+    e = bsa::launch_pooled_logits(L, meta, qbar, kbar, heads, d, 1.0 / sqrt((double)d), logits,
+                                  st);
+  if (e == hipSuccess)
+    e = bsa::launch_select(L, meta, logits, heads, sparsity_1e4, tau, counts, idx, st);
   return hip_status(e, "pool_select");
 }
 

@@ -14,19 +14,8 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
                           const void* const* src, void* const* dst, int heads, int row_bytes,
                           bool inverse, hipStream_t st);
 
-// Block means of Q and K over real slots, fp64: [heads, M, d] each.
-hipError_t launch_pool(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
-                       int heads, int d, bool bf16, double* qbar, double* kbar, hipStream_t st);
 
-// Pooled logits l[h,i,j] = qbar_i . kbar_j * scale (fp64), -inf for empty key blocks.
-hipError_t launch_pooled_logits(const Lay& L, const int32_t* zone_shape, const double* qbar,
-                                const double* kbar, int heads, int d, double scale,
-                                double* logits, hipStream_t st);
 
-// Hybrid selection per (head, query block) from the pooled logits.
-hipError_t launch_select(const Lay& L, const int32_t* zone_shape, const double* logits,
-                         int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
-                         hipStream_t st);
 
 // Per-block facts the attention kernels need inside their loops: bit r of
 // mask (r < B, 32 slots per word) = slot r is real; count = real slots.
@@ -37,6 +26,20 @@ struct BlockMeta {
 };
 hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
                              hipStream_t st);
+
+// Block means of Q and K over real slots, fp64: [heads, M, d] each.
+hipError_t launch_pool(const Lay& L, const BlockMeta* meta, const void* qp, const void* kp,
+                       int heads, int d, bool bf16, double* qbar, double* kbar, hipStream_t st);
+
+// Pooled logits l[h,i,j] = qbar_i . kbar_j * scale (fp64), -inf for empty key blocks.
+hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const double* qbar,
+                                const double* kbar, int heads, int d, double scale,
+                                double* logits, hipStream_t st);
+
+// Hybrid selection per (head, query block) from the pooled logits.
+hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logits, int heads,
+                         int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
+                         hipStream_t st);
 
 // Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel, which
 // needs attn_fwd_workspace() bytes (the block table).

@@ -16,6 +16,7 @@
 #include <float.h>
 #include <math.h>
 
+#include "attn_common.hpp"
 #include "kernels.hpp"
 
 namespace bsa {
@@ -25,33 +26,43 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- pooling --
 template <typename T, int EPC>  // EPC: elements per 16-byte chunk
-__global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const int32_t* zone_shape,
-                                                        const T* qp, const T* kp, int d,
-                                                        double* qbar, double* kbar) {
+__global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const BlockMeta* __restrict__ meta,
+                                                        const T* __restrict__ qp,
+                                                        const T* __restrict__ kp, int d,
+                                                        double* __restrict__ qbar,
+                                                        double* __restrict__ kbar) {
   extern __shared__ double red[];  // [groups][d]
   const int b = blockIdx.x, h = blockIdx.y;
   const T* __restrict__ src = blockIdx.z ? kp : qp;
   double* __restrict__ out = blockIdx.z ? kbar : qbar;
-  const Box x = block_box(L, zone_shape, b);
-  const int cnt = x.count();
+  const BlockMeta& mb = meta[b];
+  const int cnt = mb.count;
   const int chunks = d / EPC;
   const int groups = kThreads / chunks;
   const int c = threadIdx.x % chunks, g = threadIdx.x / chunks;
   double acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  const T* base = src + ((size_t)h * L.Np + (size_t)b * L.B) * d;
-  for (int r = g; r < L.B; r += groups) {
-    if (!slot_real(x, r)) continue;
-    const uint4 raw = *reinterpret_cast<const uint4*>(base + (size_t)r * d + c * EPC);
-    const T* v = reinterpret_cast<const T*>(&raw);
+  const T* base = src + ((size_t)h * L.Np + (size_t)b * L.B) * d + c * EPC;
+  // all of this thread's rows are loaded before any is summed (latency overlap);
+  // pad slots are skipped by the block's real-slot mask
+  constexpr int kMaxRows = 16;
+  u32x4 raw[kMaxRows];
+  const int nrows = L.B / groups;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
-  }
-  if (g < groups) {
+  for (int k = 0; k < kMaxRows; ++k)
+    if (k < nrows) raw[k] = *reinterpret_cast<const u32x4*>(base + (size_t)(g + k * groups) * d);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) red[g * d + c * EPC + e] = acc[e];
+  for (int k = 0; k < kMaxRows; ++k) {
+    const int r = g + k * groups;
+    if (k < nrows && ((mb.mask[r >> 5] >> (r & 31)) & 1u)) {
+      const T* v = reinterpret_cast<const T*>(&raw[k]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
+    }
   }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[g * d + c * EPC + e] = acc[e];
   __syncthreads();
   for (int e = threadIdx.x; e < d; e += kThreads) {
     double s = 0.0;
@@ -64,10 +75,12 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const int32_t* zo
 constexpr int kLT = 64;  // output tile
 constexpr int kLE = 16;  // reduction chunk
 
-__global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L, const int32_t* zone_shape,
-                                                                 const double* qbar,
-                                                                 const double* kbar, int d,
-                                                                 double scale, double* logits) {
+__global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
+                                                                 const BlockMeta* __restrict__ meta,
+                                                                 const double* __restrict__ qbar,
+                                                                 const double* __restrict__ kbar,
+                                                                 int d, double scale,
+                                                                 double* __restrict__ logits) {
   __shared__ double qs[kLE][kLT + 1];
   __shared__ double ks[kLE][kLT + 1];
   const int i0 = blockIdx.x * kLT, j0 = blockIdx.y * kLT, h = blockIdx.z;
@@ -104,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L, const in
   for (int b = 0; b < 4; ++b) {
     const int j = j0 + tx + 16 * b;
     if (j >= L.M) continue;
-    const bool key_ok = block_box(L, zone_shape, j).count() > 0;
+    const bool key_ok = meta[j].count > 0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int i = i0 + ty + 16 * a;
@@ -133,12 +146,13 @@ __device__ inline double block_sum(double v, double* sh) {
 }
 
 template <int P2>
-__global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* zone_shape,
-                                                          const double* logits, int sparsity_1e4,
-                                                          double tau, int32_t* counts,
-                                                          int32_t* idx) {
+__global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const BlockMeta* __restrict__ meta,
+                                                          const double* __restrict__ logits,
+                                                          int sparsity_1e4, double tau,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ idx) {
   constexpr int E = P2 / kThreads;  // entries per thread in the scans
-  __shared__ double key[P2];
+  __shared__ double key[P2];        // logits, then (after the sort) exp(l - max)
   __shared__ int id[P2];
   __shared__ int flag[P2];
   __shared__ double part[kThreads];
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* 
 
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const size_t row = (size_t)h * L.M + i;
-  if (block_box(L, zone_shape, i).count() == 0) {  // empty query block: empty list
+  if (meta[i].count == 0) {  // empty query block: empty list
     if (tid == 0) counts[row] = 0;
     return;
   }
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* 
   int valid = 0;
   for (int j = tid; j < P2; j += kThreads) {
     double v = -INFINITY;
-    if (j < L.M && block_box(L, zone_shape, j).count() > 0) {
+    if (j < L.M && meta[j].count > 0) {
       v = lg[j];
       ++valid;
     }
@@ -193,17 +207,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* 
 
   // softmax mass in sorted order, prefix-summed; m = first prefix reaching tau
   const double mx = key[0];
+  __syncthreads();
   double z_loc = 0.0;
   for (int e = 0; e < E; ++e) {
     const int r = tid * E + e;
-    if (r < mv) z_loc += exp(key[r] - mx);
+    const double ex = r < mv ? exp(key[r] - mx) : 0.0;
+    key[r] = ex;
+    z_loc += ex;
   }
   const double Z = block_sum(z_loc, part);
   double run = 0.0;
-  for (int e = 0; e < E; ++e) {
-    const int r = tid * E + e;
-    if (r < mv) run += exp(key[r] - mx) / Z;
-  }
+  for (int e = 0; e < E; ++e) run += key[tid * E + e] / Z;
   part[tid] = run;
   __syncthreads();
   if (tid == 0) {
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* 
   for (int e = 0; e < E; ++e) {
     const int r = tid * E + e;
     if (r < mv) {
-      c += exp(key[r] - mx) / Z;
+      c += key[r] / Z;
       if (c >= tau) {
         atomicMin(&m_first, r + 1);
         break;
@@ -258,37 +272,35 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const int32_t* 
 
 }  // namespace
 
-hipError_t launch_pool(const Lay& L, const int32_t* zone_shape, const void* qp, const void* kp,
+hipError_t launch_pool(const Lay& L, const BlockMeta* meta, const void* qp, const void* kp,
                        int heads, int d, bool bf16, double* qbar, double* kbar, hipStream_t st) {
   dim3 grid(L.M, heads, 2);
   if (bf16) {
     const int groups = kThreads / (d / 8);
     pool_kernel<__bf16, 8><<<grid, kThreads, groups * d * sizeof(double), st>>>(
-        L, zone_shape, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp), d, qbar,
-        kbar);
+        L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp), d, qbar, kbar);
   } else {
     const int groups = kThreads / (d / 4);
     pool_kernel<float, 4><<<grid, kThreads, groups * d * sizeof(double), st>>>(
-        L, zone_shape, static_cast<const float*>(qp), static_cast<const float*>(kp), d, qbar,
-        kbar);
+        L, meta, static_cast<const float*>(qp), static_cast<const float*>(kp), d, qbar, kbar);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_pooled_logits(const Lay& L, const int32_t* zone_shape, const double* qbar,
+hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const double* qbar,
                                 const double* kbar, int heads, int d, double scale,
                                 double* logits, hipStream_t st) {
   dim3 grid((L.M + kLT - 1) / kLT, (L.M + kLT - 1) / kLT, heads);
-  pooled_logits_kernel<<<grid, kThreads, 0, st>>>(L, zone_shape, qbar, kbar, d, scale, logits);
+  pooled_logits_kernel<<<grid, kThreads, 0, st>>>(L, meta, qbar, kbar, d, scale, logits);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const Lay& L, const int32_t* zone_shape, const double* logits,
+hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logits,
                          int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
                          hipStream_t st) {
   dim3 grid(L.M, heads);
 #define BSA_SELECT(P)                                                                      \
-  select_kernel<P><<<grid, kThreads, 0, st>>>(L, zone_shape, logits, sparsity_1e4, tau, \
+  select_kernel<P><<<grid, kThreads, 0, st>>>(L, meta, logits, sparsity_1e4, tau,       \
                                               counts, idx)
   if (L.M <= 256) BSA_SELECT(256);
   else if (L.M <= 512) BSA_SELECT(512);

@@ -18,10 +18,11 @@
 //                  fp32 sums), softmax in fp32 registers (lane-local rows), then
 //                  g^2 = p^T G p as Y = G P^T on fp32 MFMA (32x32x2) and a
 //                  lane-local dot with P. Writes g [N] fp32.
-//  line_kernel     per (zone, 64-channel chunk): sum x^2 and the squared line
-//                  sums along t, h, w, all in fp64 (bf16 inputs make these sums
-//                  exact), so V_a = (sum x^2 - sum_lines S^2/len) / (C n_z).
-//                  The same kernel with one "channel" handles g.
+//  line_kernel     per (zone, 32-channel chunk): the zone's slice is staged in
+//                  LDS, then sum x^2 and the squared line sums along t, h, w in
+//                  fp64 (bf16 inputs make these sums exact), so
+//                  V_a = (sum x^2 - sum_lines S^2/len) / (C n_z).
+//                  The same kernel with one channel handles g.
 //  decide_kernel   one workgroup: reduce the partials in a fixed order, the
 //                  means, r, the costs and the tie rule; writes the shape ids.
 #include <math.h>
@@ -147,51 +148,71 @@ __global__ __launch_bounds__(256) void a2v_kernel(const __bf16* X, int C, long l
 }
 
 // ------------------------------------------------------- line sum partials --
-// Partials per (zone, chunk): [0] sum x^2, [1..3] sum over lines along t, h, w
-// of (line sum)^2 / line length. Thread (c, h): c = channel in chunk, h = row.
+// Partials per (zone, chunk of kLC channels): [0] sum x^2, [1..3] sum over the
+// lines along t, h, w of (line sum)^2 / line length, all in fp64 (bf16 and fp32
+// inputs make these sums exact). The zone's slice of kLC channels is staged in
+// LDS with 16-byte loads, then each line is summed by one thread (no atomics,
+// fixed summation order).
+constexpr int kLC = 32;  // channels per workgroup
+
 template <typename T>
-__global__ __launch_bounds__(1024) void line_kernel(Lay L, const T* X, int C, int chunk_w,
-                                                    double* part) {
-  __shared__ double sh_h[4 * 16 * 64];  // h-line sums [t][w][c]
-  __shared__ double red[4][1024 / 64];
+__global__ __launch_bounds__(256) void line_kernel(Lay L, const T* __restrict__ X, int C,
+                                                   double* __restrict__ part) {
+  __shared__ T xs[4 * 16 * 16 * kLC];  // [t][h][w][c]: 64 KB for bf16 (exact copies)
+  __shared__ double red[4][4];
   const int z = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
-  const int c = threadIdx.x % 64, hh = threadIdx.x / 64;
   const int zzt = z / (L.gzh * L.gzw), zzh = (z / L.gzw) % L.gzh, zzw = z % L.gzw;
   const int t0 = zzt * L.zt, h0 = zzh * L.zh, w0 = zzw * L.zw;
   const int vt = imax(0, imin(L.zt, L.T - t0));
   const int vh = imax(0, imin(L.zh, L.H - h0));
   const int vw = imax(0, imin(L.zw, L.W - w0));
-  const int ch = chunk * chunk_w + c;
-  const bool active = c < chunk_w && ch < C && hh < vh;
-  for (int e = threadIdx.x; e < 4 * 16 * 64; e += 1024) sh_h[e] = 0.0;
-  __syncthreads();
-  double q = 0.0, rt = 0.0, rw = 0.0;
-  if (active) {
-    double st[16];
-#pragma unroll
-    for (int w = 0; w < 16; ++w) st[w] = 0.0;
-    for (int t = 0; t < vt; ++t) {
-      double sw = 0.0;
-      for (int w = 0; w < vw; ++w) {
-        const long long n = ((long long)(t0 + t) * L.H + (h0 + hh)) * L.W + (w0 + w);
-        const double x = (double)(float)X[n * C + ch];
-        q += x * x;
-        sw += x;
-        st[w] += x;
-        atomicAdd(&sh_h[(t * 16 + w) * 64 + c], x);
-      }
-      rw += sw * sw / (double)vw;
+  const int c0 = chunk * kLC;
+  const int cw = imin(kLC, C - c0);            // channels in this chunk
+  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte load
+  const int nseg = kLC / EPC;                  // 16-byte segments per token
+  const int ntok = vt * vh * vw;
+  // stage: token k (raster inside the zone's real box), segment sg
+  for (int e = threadIdx.x; e < ntok * nseg; e += 256) {
+    const int k = e / nseg, sg = e - k * nseg;
+    const int tw = k % vw, th = (k / vw) % vh, tt = k / (vw * vh);
+    const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
+    T* dst = xs + ((tt * 16 + th) * 16 + tw) * kLC + sg * EPC;
+    const int cc = c0 + sg * EPC;
+    if (cc + EPC <= C && (C % EPC) == 0) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
+    } else {
+      for (int q = 0; q < EPC; ++q) dst[q] = cc + q < C ? X[n * C + cc + q] : (T)0.f;
     }
-    for (int w = 0; w < vw; ++w) rt += st[w] * st[w] / (double)vt;
   }
   __syncthreads();
-  double rh = 0.0;
-  if (hh == 0 && c < chunk_w && ch < C) {
-    for (int t = 0; t < vt; ++t)
-      for (int w = 0; w < vw; ++w) {
-        const double s = sh_h[(t * 16 + w) * 64 + c];
-        rh += s * s / (double)vh;
-      }
+  double q = 0.0, rt = 0.0, rh = 0.0, rw = 0.0;
+  // w-lines (t, h, c) and the squares
+  for (int e = threadIdx.x; e < vt * vh * cw; e += 256) {
+    const int c = e % cw, th = (e / cw) % vh, tt = e / (cw * vh);
+    const T* p = xs + ((tt * 16 + th) * 16) * kLC + c;
+    double sum = 0.0;
+    for (int tw = 0; tw < vw; ++tw) {
+      const double x = (double)(float)p[tw * kLC];
+      sum += x;
+      q += x * x;
+    }
+    rw += sum * sum / (double)vw;
+  }
+  // h-lines (t, w, c)
+  for (int e = threadIdx.x; e < vt * vw * cw; e += 256) {
+    const int c = e % cw, tw = (e / cw) % vw, tt = e / (cw * vw);
+    const T* p = xs + (tt * 16 * 16 + tw) * kLC + c;
+    double sum = 0.0;
+    for (int th = 0; th < vh; ++th) sum += (double)(float)p[th * 16 * kLC];
+    rh += sum * sum / (double)vh;
+  }
+  // t-lines (h, w, c)
+  for (int e = threadIdx.x; e < vh * vw * cw; e += 256) {
+    const int c = e % cw, tw = (e / cw) % vw, th = e / (cw * vw);
+    const T* p = xs + (th * 16 + tw) * kLC + c;
+    double sum = 0.0;
+    for (int tt = 0; tt < vt; ++tt) sum += (double)(float)p[tt * 16 * 16 * kLC];
+    rt += sum * sum / (double)vt;
   }
   // workgroup reduction in a fixed order (deterministic)
   double vals[4] = {q, rt, rh, rw};
@@ -199,13 +220,13 @@ __global__ __launch_bounds__(1024) void line_kernel(Lay L, const T* X, int C, in
   for (int k = 0; k < 4; ++k) {
     double v = vals[k];
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) red[k][threadIdx.x / 64] = v;
+    if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = v;
   }
   __syncthreads();
   if (threadIdx.x < 4) {
-    double s = 0.0;
-    for (int k = 0; k < 1024 / 64; ++k) s += red[threadIdx.x][k];
-    part[((size_t)z * nchunks + chunk) * 4 + threadIdx.x] = s;
+    const double sres = red[threadIdx.x][0] + red[threadIdx.x][1] + red[threadIdx.x][2] +
+                        red[threadIdx.x][3];
+    part[((size_t)z * nchunks + chunk) * 4 + threadIdx.x] = sres;
   }
 }
 
@@ -308,7 +329,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace: g [N] f32 | gram [pad^2] f32 | xpart [nZ][chunks][4] | gpart [nZ][4] | scratch [7 nZ]
 size_t zone_score_workspace(const Lay& L, int C, int n_audio) {
   const int pad = 32 * ((n_audio + 31) / 32);
-  const int chunks = (C + kCh - 1) / kCh;
+  const int chunks = (C + kLC - 1) / kLC;
   return al256((size_t)L.N * sizeof(float)) + al256((size_t)pad * pad * sizeof(float)) +
          al256((size_t)L.nZ * chunks * 4 * sizeof(double)) +
          al256((size_t)L.nZ * 4 * sizeof(double)) + al256((size_t)L.nZ * 7 * sizeof(double));
@@ -322,7 +343,7 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
     return hipGetLastError();
   }
   const int pad = 32 * ((n_audio + 31) / 32);
-  const int chunks = (C + kCh - 1) / kCh;
+  const int chunks = (C + kLC - 1) / kLC;
   char* p = static_cast<char*>(ws);
   float* g = reinterpret_cast<float*>(p);
   p += al256((size_t)L.N * sizeof(float));
@@ -348,9 +369,9 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
 #undef BSA_A2V
       default: return hipErrorInvalidValue;
     }
-    line_kernel<float><<<dim3(L.nZ, 1), 1024, 0, st>>>(L, g, 1, 1, gpart);
+    line_kernel<float><<<dim3(L.nZ, 1), 256, 0, st>>>(L, g, 1, gpart);
   }
-  line_kernel<__bf16><<<dim3(L.nZ, chunks), 1024, 0, st>>>(L, X, C, kCh, xpart);
+  line_kernel<__bf16><<<dim3(L.nZ, chunks), 256, 0, st>>>(L, X, C, xpart);
   decide_kernel<<<1, 256, 0, st>>>(L, C, chunks, xpart, gpart, use_audio ? 1 : 0, zone_shape,
                                    zone_stats, scratch);
   return hipGetLastError();
