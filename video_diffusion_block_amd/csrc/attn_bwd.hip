@@ -272,7 +272,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   const size_t head0 = (size_t)h * L.Np;
   const int q = 32 * qg + l32;
   const size_t qrow = head0 + (size_t)i * kB + q;
-  const bool q_real = (meta[i].mask[q >> 5] >> (q & 31)) & 1u;
+  const bool q_real = (meta[i].mask(q >> 5) >> (q & 31)) & 1u;
 
   if (n == 0) {
     if (kh == 0)
@@ -331,11 +331,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
       }
     }
     const BlockMeta& mj = meta[lst[jj]];
-    const bool partial = mj.count < kB;
+    const bool partial = mj.count() < kB;
     bf16x8 dsf[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint32_t word = mj.mask[2 * kh + kt] >> (4 * hi);
+      const uint32_t word = mj.mask(2 * kh + kt) >> (4 * hi);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = exp2_fast(fmaf(st[kt][r], c2, -lse2));
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
-    const bool real = (mj.mask[key >> 5] >> (key & 31)) & 1u;
+    const bool real = (mj.mask(key >> 5) >> (key & 31)) & 1u;
     float* dkr = dkp + (kbase + key) * kD + l32;
     float* dvr = dvp + (kbase + key) * kD + l32;
 #pragma unroll

@@ -38,4 +38,62 @@ __device__ inline f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- direct global -> LDS loads through a buffer resource -------------------
+// The buffer form (buffer_load_dwordx4 ... lds) is counted by vmcnt only; the
+// flat/global form is also treated by the compiler as a possible LDS access of
+// unknown order, which turns every later LDS-read wait into a full wait.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+extern "C" __device__ void bsa_raw_buffer_load_lds(i32x4 rsrc, lds_void* lds, int size,
+                                                   int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw (unformatted, stride 0) buffer resource over `bytes` bytes at `base`.
+__device__ inline i32x4 make_buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;  // raw 32-bit data format
+  return r;
+}
+
+// Lane l's 16 bytes at rsrc + soffset + voffset land at LDS address lds + 16 l.
+__device__ inline void dma16(const i32x4& rsrc, lds_void* lds, int voffset, int soffset) {
+  bsa_raw_buffer_load_lds(rsrc, lds, 16, voffset, soffset, 0, 0);
+}
+
+// The same load written out by hand, for loops that wait for their tile loads
+// themselves. The compiler does not see it as a memory request: it inserts no
+// waits for it (a compiler-tracked LDS load makes every later LDS read wait
+// for all loads in flight, since it cannot tell the target buffers apart), so
+// the caller must wait (s_waitcnt vmcnt) and synchronise before reading the
+// data. M0 holds the LDS destination; the s_nop covers the wait states the
+// hardware requires after M0 and SGPR-operand writes.
+__device__ inline void dma16_manual(const i32x4& rsrc, uint32_t lds_addr, int voffset,
+                                    int soffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_addr),
+      "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+// 4 bytes per lane: lane l's dword lands at lds_addr + 4 l.
+__device__ inline void dma4_manual(const i32x4& rsrc, uint32_t lds_addr, int voffset,
+                                   int soffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 4\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds" ::"s"(lds_addr),
+      "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+__device__ inline uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
 }  // namespace bsa

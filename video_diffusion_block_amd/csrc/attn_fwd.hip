@@ -23,6 +23,7 @@
 //    One thread per query slot, fp32 online softmax, K/V staged through LDS as
 //    fp32. This is the exact-parity path (fp32 inputs) and the fallback.
 #include "attn_common.hpp"
+#include "bsa.h"
 #include "kernels.hpp"
 
 namespace bsa {
@@ -89,10 +90,10 @@ constexpr int kB = 128;          // tokens per block (queries and keys)
 constexpr int kTile = kB * kD;   // bf16 elements of one K or V tile (32 KB)
 constexpr int kThreads = 512;    // 8 wavefronts
 constexpr float kLazy = 8.f;     // log2 headroom of the lazily updated softmax max
+constexpr int kMaxList = BSA_MAX_BLOCKS;  // longest key-block list of a row
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS tiles are row-major (row = token, 256 bytes = 16 chunks of 16 bytes) with
 // an XOR swizzle of the chunk index: K chunk q of row r sits at q ^ (r & 15),
@@ -105,19 +106,60 @@ __device__ inline int vswz(int r, int q) { return q ^ ((r & 3) << 2); }
 // Tiles arrive by direct global->LDS loads (16 bytes per lane): load m
 // (0..3) of wave w fills LDS slots (8m + w) * 64 + lane, i.e. row
 // 4 (8m + w) + lane / 16, physical chunk lane % 16; the lane therefore fetches
-// the logical chunk that the swizzle puts there.
+// the logical chunk that the swizzle puts there. `src` is the byte offset of
+// the block inside the head's tensor (the buffer resource covers the head).
 template <bool kIsV>
-__device__ inline void dma_tile(__bf16* tile, const __bf16* gtile, int w, int lane) {
+__device__ inline void dma_part(__bf16* tile, const i32x4& rsrc, int src, int w, int lane, int m) {
+  const int r = 4 * (8 * m + w) + (lane >> 4);
+  const int q = kIsV ? vswz(r, lane & 15) : kswz(r, lane & 15);
+  dma16_manual(rsrc, lds_addr_of(tile + (8 * m + w) * 512), 2 * (r * kD + 8 * q), src);
+}
+template <bool kIsV>
+__device__ inline void dma_tile(__bf16* tile, const i32x4& rsrc, int src, int w, int lane) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int r = 4 * (8 * m + w) + (lane >> 4);
-    const int q = kIsV ? vswz(r, lane & 15) : kswz(r, lane & 15);
-    __builtin_amdgcn_global_load_lds(gtile + r * kD + 8 * q, (lds_void*)(tile + (8 * m + w) * 512),
-                                     16, 0, 0);
-  }
+  for (int m = 0; m < 4; ++m) dma_part<kIsV>(tile, rsrc, src, w, lane, m);
 }
 
-__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained), as a builtin so that the
+// compiler's own wait-count tracking sees it.
+__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vmcnt(0), vmcnt(4), lgkmcnt(0), each leaving the others free.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm4 = 0x0F74;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// would also wait for every tile load still in flight. Each wave waits for the
+// loads the next phase needs before arriving here; the "memory" clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Keeps the compiler's scheduler from moving instructions across this point, so
+// that a phase's LDS reads are all issued before its matrix instructions.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// A zero that the compiler cannot prove uniform: a load indexed with it stays
+// on the vector memory path (counted by vmcnt, drained with the tile loads at
+// the end of an iteration) instead of becoming a scalar load, whose completion
+// shares lgkmcnt with the LDS reads and would force full waits on them.
+__device__ inline int vzero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// max / sum of a value over the lane pair (l, l ^ 32)
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline bf16x4 tr_read(const __bf16* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -125,38 +167,81 @@ __device__ inline bf16x4 tr_read(const __bf16* p) {
 }
 
 // S^T = K Q^T for this wave's 64 keys of the block in `sk` (two 32x32 tiles).
-// The eight K fragments of a tile are loaded in one batch before its MFMAs so
-// that LDS latency overlaps the other tile's matrix work.
+// The K fragments are requested four k-steps (eight products) ahead of the
+// products that consume them.
+template <typename Hook>
 __device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int kswz_lane,
-                                const bf16x8 (&qf)[8], int hi) {
-  bf16x8 a[2][8];
+                                const bf16x8 (&qf)[8], int hi, Hook hook) {
+  bf16x8 a[8][2];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      a[st][kt] = *reinterpret_cast<const bf16x8*>(sk + koff + 32 * kt * kD +
+                                                   8 * ((2 * st + hi) ^ kswz_lane));
+  };
+#pragma unroll
+  for (int st = 0; st < 4; ++st) load(st);
+  sched_fence();
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
-      a[kt][st] = *reinterpret_cast<const bf16x8*>(sk + koff + 32 * kt * kD +
-                                                   8 * ((2 * st + hi) ^ kswz_lane));
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
     for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[st][kt], qf[st], s[kt]);
+    if (st + 4 < 8) load(st + 4);
+    hook(st);
+    sched_fence();
   }
-#pragma unroll
-  for (int st = 0; st < 8; ++st)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[kt][st], qf[st], s[kt]);
 }
+
+// The validity words of one key block for this wave's 64 keys.
+struct HalfMeta {
+  uint32_t w0, w1;  // bits of keys 64kh + 0..31 and 64kh + 32..63
+  int count;        // real slots of the block (128 = full, no masking)
+};
 
 // Pad keys of a partial key block: bit r of the block's mask = slot r real.
 // Lane (l32, hi) holds keys 64kh + 32kt + 8(r/4) + 4hi + r%4 in element r.
-__device__ inline void mask_pad_keys(f32x16 (&s)[2], const BlockMeta& m, int kh, int hi) {
-  if (m.count >= 128) return;
+__device__ inline void mask_pad_keys(f32x16 (&s)[2], const HalfMeta& m, int hi) {
+  if (__builtin_amdgcn_readfirstlane(m.count) >= 128) return;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const uint32_t word = m.mask[2 * kh + kt] >> (4 * hi);
+    const uint32_t word = (kt ? m.w1 : m.w0) >> (4 * hi);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (!((word >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = -INFINITY;
+  }
+}
+
+// O^T (d x queries) += V^T (d x keys) P^T (keys x queries) over this wave's 64
+// keys. P^T fragment c (c = 0..3) holds keys 16c + 8(jj/4) + 4hi + jj%4
+// (jj = 0..7); the transposed V reads produce the same key order. The reads of
+// two d-tiles are in flight ahead of the products that use them.
+template <typename Hook>
+__device__ inline void pv_tiles(f32x16 (&o)[4], const __bf16* sv, const int (&voff)[4],
+                                const bf16x8 (&pf8)[4], Hook hook) {
+  bf16x8 a[4][4];
+  auto load = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const __bf16* p0 = sv + voff[t] + 16 * c * kD;
+      const bf16x4 lo = tr_read(p0);
+      const bf16x4 up = tr_read(p0 + 8 * kD);
+      a[t][c] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  load(0);
+  load(1);
+  sched_fence();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t + 2 < 4) load(t + 2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[t] = mfma32x32x16(a[t][c], pf8[c], o[t]);
+    hook(t);
+    sched_fence();
   }
 }
 
@@ -165,8 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ idx, float scale_log2,
     __bf16* __restrict__ op, float* __restrict__ lse) {
-  __shared__ __align__(16) __bf16 sK[3][kTile];  // 3 x 32 KB
-  __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB: 160 KB in all
+  __shared__ __align__(16) __bf16 sK[2][kTile];  // 2 x 32 KB
+  __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB
+  __shared__ int32_t sL[kMaxList];               // the row's key-block list (16 KB)
+  __shared__ __align__(16) uint32_t sM[2][64];   // block facts of blocks j, j+1 (8 copies each)
   const int i = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,14 +273,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
     return;
   }
-  const __bf16* kh0 = kp + head0 * kD;
-  const __bf16* vh0 = vp + head0 * kD;
+  const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
+  const i32x4 krs = make_buffer_rsrc(kp + head0 * kD, head_bytes);
+  const i32x4 vrs = make_buffer_rsrc(vp + head0 * kD, head_bytes);
+  const i32x4 mrs = make_buffer_rsrc(meta, (uint32_t)L.M * sizeof(BlockMeta));
+  constexpr int kTileBytes = kTile * 2;
 
-  // prologue DMA: K0, K1, V0
-  dma_tile<false>(sK[0], kh0 + (size_t)lst[0] * kTile, w, lane);
-  if (n > 1) dma_tile<false>(sK[1], kh0 + (size_t)lst[1] * kTile, w, lane);
-  dma_tile<true>(sV[0], vh0 + (size_t)lst[0] * kTile, w, lane);
+  // Block facts travel like the tiles: wave 0 copies block blk's 32-byte
+  // record into slot sM[slot] (each lane one dword; eight copies), and every
+  // wave reads its half (validity words of its 64 keys, real-slot count) from
+  // there after the barrier that follows the wait.
+  auto fetch_meta = [&](int blk, int slot) {
+    if (w == 0) dma4_manual(mrs, lds_addr_of(&sM[slot][0]), 4 * (lane & 7), blk * 32);
+  };
+  auto read_meta = [&](int slot) {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = *reinterpret_cast<const u32x3*>(&sM[slot][4 * kh]);
+    return HalfMeta{v.x, v.y, (int)v.z};
+  };
+  auto uniform = [](const HalfMeta& m) {
+    return HalfMeta{(uint32_t)__builtin_amdgcn_readfirstlane(m.w0),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(m.w1),
+                    __builtin_amdgcn_readfirstlane(m.count)};
+  };
 
+  // prologue: the list into LDS; tiles K0, V0 (and K1), block 0's mask words
+  for (int e = tid; e < n; e += kThreads) sL[e] = lst[e];
+  const int blk0 = lst[0];
+  const int blk1 = n > 1 ? lst[1] : 0;
+  dma_tile<false>(sK[0], krs, blk0 * kTileBytes, w, lane);
+  dma_tile<true>(sV[0], vrs, blk0 * kTileBytes, w, lane);
   // Q^T fragments (B operand of S^T = K Q^T): lane holds Q[q][16s + 8hi .. +8].
   bf16x8 qf[8];
   {
@@ -201,6 +310,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
+  fetch_meta(blk0, 0);
+  dma_tile<false>(sK[1], krs, blk1 * kTileBytes, w, lane);  // (block 0 again if n = 1)
+  __builtin_amdgcn_s_waitcnt(kWaitVm4);                     // all but K1
 
   // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
   const int koff = (64 * kh + l32) * kD;
@@ -222,40 +334,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = -INFINITY;  // reference max of s * scale * log2(e)
   float l_run = 0.f;        // this lane's share of the running sum
-
-  // The two wavefronts of each SIMD (kh = 0 and kh = 1) walk the blocks in
-  // opposite phase orders so that one's matrix work overlaps the other's
-  // exponentials: kh = 0 runs S_j -> softmax_j -> PV_j, kh = 1 runs
-  // softmax_j -> PV_j -> S_{j+1}. K is triple-buffered (K_j, K_{j+1} in use,
-  // K_{j+2} streaming in), V double-buffered.
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   f32x16 s_cur[2];
-  wait_dma();
-  __syncthreads();
-  if (kh == 1) {
-    qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi);
-    mask_pad_keys(s_cur, meta[lst[0]], kh, hi);
-  }
-  int kb = 0;  // K buffer of block j (j mod 3)
-  for (int j = 0; j < n; ++j) {
-    const int kb1 = kb == 2 ? 0 : kb + 1;   // block j+1
-    const int kb2 = kb1 == 2 ? 0 : kb1 + 1; // block j+2
-    const int vb = j & 1;
-    if (j + 2 < n) dma_tile<false>(sK[kb2], kh0 + (size_t)lst[j + 2] * kTile, w, lane);
-    if (j + 1 < n) dma_tile<true>(sV[vb ^ 1], vh0 + (size_t)lst[j + 1] * kTile, w, lane);
-    if (kh == 0) {
-      qk_tiles(s_cur, sK[kb], koff, kswz_lane, qf, hi);
-      mask_pad_keys(s_cur, meta[lst[j]], kh, hi);
-    }
 
+  // nothing from the scalar path may be outstanding inside the loop: there
+  // the LDS reads are waited for by count, in issue order
+  asm volatile("" ::"s"(scale_log2));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __syncthreads();
+  HalfMeta meta_j = uniform(read_meta(0));
+
+  auto softmax = [&](bf16x8 (&pf8)[4]) {
     // Online softmax (log2 domain) with a lazily updated reference max: the
     // exponent base m_run moves only when a row max exceeds it by more than
-    // kLazy (then p <= 2^kLazy, safe in bf16 and fp32), so O is rarely rescaled.
-    float mx = -INFINITY;
+    // kLazy (then p <= 2^kLazy, safe in bf16 and fp32), so O is rarely
+    // rescaled.
+    float mxa = fmaxf(s_cur[0][0], s_cur[0][1]), mxb = fmaxf(s_cur[1][0], s_cur[1][1]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    for (int r = 2; r < 16; ++r) {
+      mxa = fmaxf(mxa, s_cur[0][r]);
+      mxb = fmaxf(mxb, s_cur[1][r]);
+    }
+    const float mx = pair_max(fmaxf(mxa, mxb)) * scale_log2;
     if (__ballot(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2_fast(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -267,47 +368,102 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    bf16x8 pf8[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s_cur[kt][r], scale_log2, -m_use));
-        psum += p;
-        pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r)
+        pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)exp2_fast(fmaf(s_cur[kt][r], scale_log2, -m_use));
+    // row sum of the rounded probabilities (the weights the products use)
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ps[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf8[c], pf8[c], 0, 1), ones,
+                                              ps[c], false);
+      ps[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf8[c], pf8[c], 2, 3), ones,
+                                              ps[c], false);
+      ps[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf8[c], pf8[c], 4, 5), ones,
+                                              ps[c], false);
+      ps[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf8[c], pf8[c], 6, 7), ones,
+                                              ps[c], false);
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  auto no_hook = [](int) {};
 
-    // O^T (d x queries) += V^T (d x keys) P^T (keys x queries).
-    // P^T fragment c (c = 0..3) holds keys 16c + 8(jj/4) + 4hi + jj%4 (jj = 0..7)
-    // of this wave's 64 keys; the transposed V reads produce the same key order.
-    // The four V^T fragments of a d-tile are read in one batch.
-    const __bf16* sv = sV[vb];
+  // Schedule. The two wavefronts of each SIMD (kh = 0 and kh = 1) run the
+  // three phases of a key block in rotated orders so that one's matrix work
+  // overlaps the other's exponentials, with two workgroup barriers per block:
+  //            phase 1       phase 2   | X |  phase 3        | Y |
+  //   kh = 0:  S_j           softmax_j |   |  PV_j           |   |
+  //   kh = 1:  softmax_j     PV_j      |   |  S_{j+1}        |   |
+  // K and V are double-buffered. V_{j+1} is requested in phases 1-2 and waited
+  // for at Y; K_{j+2} is requested in phase 3, into the buffer K_j has left,
+  // and waited for at X of the next block. Each wave spreads its requests over
+  // its matrix steps, so that no wave stalls long on a full memory queue.
+  // Every iteration issues the same requests (past the end of the list they
+  // repeat the last block into a buffer nobody reads again), so the waits are
+  // fixed counts: loads complete in issue order, and at X and at Y exactly the
+  // four tile loads issued after the awaited ones may still be in flight.
+  auto walk = [&](auto khc) {
+    constexpr int KH = decltype(khc)::value;
+    if (KH == 1) {
+      qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi, no_hook);
+      mask_pad_keys(s_cur, meta_j, hi);
+    }
+    for (int j = 0; j < n; ++j) {
+      const int cb = j & 1, nb = cb ^ 1;
+      const bool more1 = j + 1 < n;
+      const int b1 = __builtin_amdgcn_readfirstlane(sL[min(j + 1, n - 1)]);
+      const int b2 = __builtin_amdgcn_readfirstlane(sL[min(j + 2, n - 1)]);
+      auto vdma = [&](int m) { dma_part<true>(sV[nb], vrs, b1 * kTileBytes, w, lane, m); };
+      auto kdma = [&](int m) { dma_part<false>(sK[cb], krs, b2 * kTileBytes, w, lane, m); };
+      fetch_meta(b1, nb);
+      bf16x8 pf8[4];
+      if (KH == 0) {
+        qk_tiles(s_cur, sK[cb], koff, kswz_lane, qf, hi, [&](int st) {
+          if (st & 1) vdma(st >> 1);
+        });
+        mask_pad_keys(s_cur, meta_j, hi);
+        softmax(pf8);
+      } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 a[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const __bf16* p0 = sv + voff[t] + 16 * c * kD;
-        const bf16x4 lo = tr_read(p0);
-        const bf16x4 up = tr_read(p0 + 8 * kD);
-        a[c] = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int m = 0; m < 4; ++m) vdma(m);
+        softmax(pf8);
+        pv_tiles(o, sV[cb], voff, pf8, no_hook);
       }
+      // X: K_{j+1} and the facts of block j+1 have landed (V_{j+1} may not)
+      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      barrier();
+      const HalfMeta meta_n = uniform(read_meta(nb));
+      if (KH == 0) {
+        pv_tiles(o, sV[cb], voff, pf8, kdma);
+      } else {
+        if (more1) {
+          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, [&](int st) {
+            if (st & 1) kdma(st >> 1);
+          });
+          mask_pad_keys(s_cur, meta_n, hi);
+        } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[t] = mfma32x32x16(a[c], pf8[c], o[t]);
+          for (int m = 0; m < 4; ++m) kdma(m);
+        }
+      }
+      // Y: V_{j+1} has landed (K_{j+2} may not)
+      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      barrier();
+      meta_j = meta_n;
     }
-    if (kh == 1 && j + 1 < n) {
-      qk_tiles(s_cur, sK[kb1], koff, kswz_lane, qf, hi);
-      mask_pad_keys(s_cur, meta[lst[j + 1]], kh, hi);
-    }
-    kb = kb1;
-    wait_dma();
-    __syncthreads();
-  }
+  };
+  if (kh == 0)
+    walk(std::integral_constant<int, 0>());
+  else
+    walk(std::integral_constant<int, 1>());
+  // the last iteration's (unused) K requests must land before LDS is reused
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
 
   // merge the two key halves (waves w and w+4 share their 32 queries)
-  l_run += __shfl_xor(l_run, 32);
+  l_run = pair_sum(l_run);
   float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;  // 64 KB
   float* xm = reinterpret_cast<float*>(&sV[0][0]) + (qg * 64 + lane) * 2;
   if (kh == 1) {

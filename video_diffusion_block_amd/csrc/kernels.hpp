@@ -18,11 +18,13 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
 
 
 // Per-block facts the attention kernels need inside their loops: bit r of
-// mask (r < B, 32 slots per word) = slot r is real; count = real slots.
+// mask word r / 32 (r < B) = slot r is real; count = real slots. Stored as two
+// 16-byte halves, half h = {word 2h, word 2h + 1, count, 0}, so that a reader
+// of slots 64h .. 64h + 63 gets its words and the count in one load.
 struct BlockMeta {
-  uint32_t mask[4];
-  int32_t count;
-  int32_t pad[3];
+  uint32_t half[2][4];
+  __host__ __device__ uint32_t mask(int k) const { return half[k >> 1][k & 1]; }
+  __host__ __device__ int count() const { return (int)half[0][2]; }
 };
 hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
                              hipStream_t st);

@@ -49,12 +49,16 @@ __global__ __launch_bounds__(256) void block_meta_kernel(Lay L, const int32_t* z
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= L.M) return;
   const Box x = block_box(L, zone_shape, b);
-  BlockMeta m;
-  for (int w = 0; w < 4; ++w) m.mask[w] = 0u;
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
   for (int r = 0; r < L.B && r < 128; ++r)
-    if (slot_real(x, r)) m.mask[r >> 5] |= 1u << (r & 31);
-  m.count = x.count();
-  m.pad[0] = m.pad[1] = m.pad[2] = 0;
+    if (slot_real(x, r)) words[r >> 5] |= 1u << (r & 31);
+  BlockMeta m;
+  for (int h = 0; h < 2; ++h) {
+    m.half[h][0] = words[2 * h];
+    m.half[h][1] = words[2 * h + 1];
+    m.half[h][2] = (uint32_t)x.count();
+    m.half[h][3] = 0u;
+  }
   meta[b] = m;
 }
 

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const BlockMeta* 
   const T* __restrict__ src = blockIdx.z ? kp : qp;
   double* __restrict__ out = blockIdx.z ? kbar : qbar;
   const BlockMeta& mb = meta[b];
-  const int cnt = mb.count;
+  const int cnt = mb.count();
   const int chunks = d / EPC;
   const int groups = kThreads / chunks;
   const int c = threadIdx.x % chunks, g = threadIdx.x / chunks;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const BlockMeta* 
 #pragma unroll
   for (int k = 0; k < kMaxRows; ++k) {
     const int r = g + k * groups;
-    if (k < nrows && ((mb.mask[r >> 5] >> (r & 31)) & 1u)) {
+    if (k < nrows && ((mb.mask(r >> 5) >> (r & 31)) & 1u)) {
       const T* v = reinterpret_cast<const T*>(&raw[k]);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)v[e];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
   for (int b = 0; b < 4; ++b) {
     const int j = j0 + tx + 16 * b;
     if (j >= L.M) continue;
-    const bool key_ok = meta[j].count > 0;
+    const bool key_ok = meta[j].count() > 0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int i = i0 + ty + 16 * a;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const BlockMeta
 
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const size_t row = (size_t)h * L.M + i;
-  if (meta[i].count == 0) {  // empty query block: empty list
+  if (meta[i].count() == 0) {  // empty query block: empty list
     if (tid == 0) counts[row] = 0;
     return;
   }
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const BlockMeta
   int valid = 0;
   for (int j = tid; j < P2; j += kThreads) {
     double v = -INFINITY;
-    if (j < L.M && meta[j].count > 0) {
+    if (j < L.M && meta[j].count() > 0) {
       v = lg[j];
       ++valid;
     }
