@@ -44,29 +44,29 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
   }
 }
 
-__global__ __launch_bounds__(256) void block_meta_kernel(Lay L, const int32_t* zone_shape,
+// One workgroup of two wavefronts per block: wavefront v evaluates slots
+// 64v .. 64v + 63, one per lane, and a ballot forms the two validity words.
+__global__ __launch_bounds__(128) void block_meta_kernel(Lay L, const int32_t* zone_shape,
                                                          BlockMeta* meta) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= L.M) return;
+  const int b = blockIdx.x, r = threadIdx.x, v = r >> 6;
   const Box x = block_box(L, zone_shape, b);
-  uint32_t words[4] = {0u, 0u, 0u, 0u};
-  for (int r = 0; r < L.B && r < 128; ++r)
-    if (slot_real(x, r)) words[r >> 5] |= 1u << (r & 31);
-  BlockMeta m;
-  for (int h = 0; h < 2; ++h) {
-    m.half[h][0] = words[2 * h];
-    m.half[h][1] = words[2 * h + 1];
-    m.half[h][2] = (uint32_t)x.count();
-    m.half[h][3] = 0u;
+  const bool real = r < L.B && slot_real(x, r);
+  const uint64_t word = __ballot(real);
+  if ((r & 63) == 0) {
+    const uint32_t count = (uint32_t)x.count();
+    uint32_t* half = meta[b].half[v];
+    half[0] = (uint32_t)word;
+    half[1] = (uint32_t)(word >> 32);
+    half[2] = count;
+    half[3] = 0u;
   }
-  meta[b] = m;
 }
 
 }  // namespace
 
 hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
                              hipStream_t st) {
-  block_meta_kernel<<<(L.M + 255) / 256, 256, 0, st>>>(L, zone_shape, meta);
+  block_meta_kernel<<<L.M, 128, 0, st>>>(L, zone_shape, meta);
   return hipGetLastError();
 }
 

@@ -132,142 +132,175 @@ __device__ inline bool before(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// Block-wide sums over kThreads threads (fp64 / int).
-__device__ inline double block_sum(double v, double* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
-    __syncthreads();
+// Wave-level sum / exclusive prefix sum / min over the 64 lanes, in a fixed
+// order (the result does not depend on timing).
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename T>
+__device__ inline T wave_exclusive_scan(T v, int lane) {
+  T incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
   }
-  const double r = sh[0];
-  __syncthreads();
-  return r;
+  return incl - v;
 }
 
-template <int P2>
-__global__ __launch_bounds__(kThreads) void select_kernel(Lay L, const BlockMeta* __restrict__ meta,
-                                                          const double* __restrict__ logits,
-                                                          int sparsity_1e4, double tau,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ idx) {
-  constexpr int E = P2 / kThreads;  // entries per thread in the scans
-  __shared__ double key[P2];        // logits, then (after the sort) exp(l - max)
-  __shared__ int id[P2];
-  __shared__ int flag[P2];
-  __shared__ double part[kThreads];
-  __shared__ int ipart[kThreads];
-  __shared__ int m_first;
+// Bitonic compare-exchange steps on a row held in registers: lane l holds
+// sorted positions C l .. C l + C - 1 (element e at position C l + e). Within
+// a lane the partner of e is e ^ JJ (JJ < C, known at compile time); across
+// lanes the partner of lane l is lane l ^ (jj / C), same e. Positions whose
+// bit k is clear are sorted into "before" order, the others reversed.
+template <int C, int JJ>
+__device__ inline void bitonic_in_lane(double (&key)[C], int (&id)[C], int lane, int k) {
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    if (e & JJ) continue;
+    const int f = e | JJ;
+    const bool up = ((lane * C + e) & k) == 0;
+    const bool swap = up ? before(key[f], id[f], key[e], id[e])
+                         : before(key[e], id[e], key[f], id[f]);
+    const double ke = key[e], kf = key[f];
+    const int ie = id[e], jf = id[f];
+    key[e] = swap ? kf : ke;
+    key[f] = swap ? ke : kf;
+    id[e] = swap ? jf : ie;
+    id[f] = swap ? ie : jf;
+  }
+}
+template <int C>
+__device__ inline void bitonic_cross_lane(double (&key)[C], int (&id)[C], int lane, int k, int jj) {
+  const int lm = jj / C;
+  const bool lower = (lane & lm) == 0;
+  const bool up = ((lane * C) & k) == 0;  // bit k of the position (k > jj >= C)
+  const bool keep_first = lower == up;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const double ko = __shfl_xor(key[e], lm);
+    const int io = __shfl_xor(id[e], lm);
+    const bool mine_first = before(key[e], id[e], ko, io);
+    if (mine_first != keep_first) {
+      key[e] = ko;
+      id[e] = io;
+    }
+  }
+}
 
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+// One wavefront per (head, query block) row, WAVES rows per workgroup. The
+// row's P2 = 64 C entries (logit, block id) are sorted in registers by a
+// bitonic network (lane-local steps and cross-lane exchanges), then scanned.
+template <int P2, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMeta* __restrict__ meta,
+                                                             const double* __restrict__ logits,
+                                                             int sparsity_1e4, double tau,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ idx) {
+  constexpr int C = P2 / 64;  // entries per lane
+  __shared__ uint32_t sbits[WAVES][P2 / 32];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * WAVES + w, h = blockIdx.y;
+  if (i >= L.M) return;  // (whole wavefront)
   const size_t row = (size_t)h * L.M + i;
   if (meta[i].count() == 0) {  // empty query block: empty list
-    if (tid == 0) counts[row] = 0;
+    if (lane == 0) counts[row] = 0;
     return;
   }
+  uint32_t* bits = sbits[w];
   const double* lg = logits + row * L.M;
+
+  // candidates are the non-empty key blocks, whose pooled logits are finite
+  double key[C];
+  int id[C];
   int valid = 0;
-  for (int j = tid; j < P2; j += kThreads) {
-    double v = -INFINITY;
-    if (j < L.M && meta[j].count() > 0) {
-      v = lg[j];
-      ++valid;
-    }
-    key[j] = v;
-    id[j] = j;
-    flag[j] = 0;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int j = lane * C + e;
+    key[e] = j < L.M ? lg[j] : -INFINITY;
+    id[e] = j;
+    valid += key[e] != -INFINITY;
   }
-  ipart[tid] = valid;
-  if (tid == 0) m_first = INT_MAX;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) ipart[tid] += ipart[tid + s];
-    __syncthreads();
-  }
-  const int mv = ipart[0];
+#pragma unroll
+  for (int e = lane; e < P2 / 32; e += 64) bits[e] = 0u;
+  const int mv = wave_sum(valid);
 
   // bitonic sort: logit descending, then block id ascending
   for (int k = 2; k <= P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = tid; t < P2; t += kThreads) {
-        const int u = t ^ j;
-        if (u > t) {
-          const double ka = key[t], kb = key[u];
-          const int ia = id[t], ib = id[u];
-          const bool up = (t & k) == 0;
-          if (up ? before(kb, ib, ka, ia) : before(ka, ia, kb, ib)) {
-            key[t] = kb; key[u] = ka;
-            id[t] = ib; id[u] = ia;
-          }
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= C) {
+        bitonic_cross_lane<C>(key, id, lane, k, jj);
+      } else {
+        switch (jj) {
+          case 1: bitonic_in_lane<C, 1>(key, id, lane, k); break;
+          case 2: bitonic_in_lane<C, (C > 2 ? 2 : 1)>(key, id, lane, k); break;
+          case 4: bitonic_in_lane<C, (C > 4 ? 4 : 1)>(key, id, lane, k); break;
+          case 8: bitonic_in_lane<C, (C > 8 ? 8 : 1)>(key, id, lane, k); break;
+          case 16: bitonic_in_lane<C, (C > 16 ? 16 : 1)>(key, id, lane, k); break;
+          default: bitonic_in_lane<C, (C > 32 ? 32 : 1)>(key, id, lane, k); break;
         }
       }
-      __syncthreads();
     }
   }
 
   // softmax mass in sorted order, prefix-summed; m = first prefix reaching tau
-  const double mx = key[0];
-  __syncthreads();
+  const double mx = __shfl(key[0], 0);
+  double* ex = key;  // exp(l - max) replaces the logits
   double z_loc = 0.0;
-  for (int e = 0; e < E; ++e) {
-    const int r = tid * E + e;
-    const double ex = r < mv ? exp(key[r] - mx) : 0.0;
-    key[r] = ex;
-    z_loc += ex;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    ex[e] = lane * C + e < mv ? exp(key[e] - mx) : 0.0;
+    z_loc += ex[e];
   }
-  const double Z = block_sum(z_loc, part);
+  const double Z = wave_sum(z_loc);
   double run = 0.0;
-  for (int e = 0; e < E; ++e) run += key[tid * E + e] / Z;
-  part[tid] = run;
-  __syncthreads();
-  if (tid == 0) {
-    double acc = 0.0;
-    for (int t = 0; t < kThreads; ++t) {
-      const double v = part[t];
-      part[t] = acc;
-      acc += v;
+#pragma unroll
+  for (int e = 0; e < C; ++e) run += ex[e] / Z;
+  double c = wave_exclusive_scan(run, lane);
+  int m_loc = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int r = lane * C + e;
+    if (r < mv && m_loc == INT_MAX) {
+      c += ex[e] / Z;
+      if (c >= tau) m_loc = r + 1;
     }
   }
-  __syncthreads();
-  double c = part[tid];
-  for (int e = 0; e < E; ++e) {
-    const int r = tid * E + e;
-    if (r < mv) {
-      c += key[r] / Z;
-      if (c >= tau) {
-        atomicMin(&m_first, r + 1);
-        break;
-      }
-    }
-  }
-  __syncthreads();
+  const int m_first = wave_min(m_loc);
   const int m = m_first == INT_MAX ? mv : m_first;
   const int k = max(1, (mv * (10000 - sparsity_1e4) + 9999) / 10000);
   const int n = min(max(k, m), mv);
-  for (int r = tid; r < n; r += kThreads) flag[id[r]] = 1;
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < C; ++e)
+    if (lane * C + e < n) atomicOr(&bits[id[e] >> 5], 1u << (id[e] & 31));
 
-  // ascending compaction of the flagged block ids
+  // ascending compaction of the selected block ids (lane l: ids C l .. C l + C - 1)
   int cnt = 0;
-  for (int e = 0; e < E; ++e) cnt += flag[tid * E + e];
-  ipart[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int v = ipart[t];
-      ipart[t] = acc;
-      acc += v;
-    }
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int b = lane * C + e;
+    cnt += (bits[b >> 5] >> (b & 31)) & 1u;
   }
-  __syncthreads();
-  int pos = ipart[tid];
+  int pos = wave_exclusive_scan(cnt, lane);
   int32_t* out = idx + row * L.M;
-  for (int e = 0; e < E; ++e) {
-    const int j = tid * E + e;
-    if (flag[j]) out[pos++] = j;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int b = lane * C + e;
+    if ((bits[b >> 5] >> (b & 31)) & 1u) out[pos++] = b;
   }
-  if (tid == 0) counts[row] = n;
+  if (lane == 0) counts[row] = n;
 }
 
 }  // namespace
@@ -298,15 +331,14 @@ hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const doubl
 hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logits,
                          int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
                          hipStream_t st) {
-  dim3 grid(L.M, heads);
-#define BSA_SELECT(P)                                                                      \
-  select_kernel<P><<<grid, kThreads, 0, st>>>(L, meta, logits, sparsity_1e4, tau,       \
-                                              counts, idx)
-  if (L.M <= 256) BSA_SELECT(256);
-  else if (L.M <= 512) BSA_SELECT(512);
-  else if (L.M <= 1024) BSA_SELECT(1024);
-  else if (L.M <= 2048) BSA_SELECT(2048);
-  else BSA_SELECT(4096);
+#define BSA_SELECT(P, W)                                                                   \
+  select_kernel<P, W><<<dim3((L.M + (W) - 1) / (W), heads), 64 * (W), 0, st>>>(            \
+      L, meta, logits, sparsity_1e4, tau, counts, idx)
+  if (L.M <= 256) BSA_SELECT(256, 4);
+  else if (L.M <= 512) BSA_SELECT(512, 4);
+  else if (L.M <= 1024) BSA_SELECT(1024, 4);
+  else if (L.M <= 2048) BSA_SELECT(2048, 4);
+  else BSA_SELECT(4096, 2);
 #undef BSA_SELECT
   return hipGetLastError();
 }
