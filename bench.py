@@ -43,6 +43,52 @@ def parse():
     return ap.parse_args()
 
 
+def hbm_stages(wl, sizes, stage_ms):
+    """Algorithmic HBM bytes of the data-movement stages and the rate they reach
+    in the event-timed stage time, against the 8 TB/s HBM peak."""
+    N, Np, H, d = sizes["n_tokens"], sizes["n_padded"], wl.heads, wl.d
+    e = 2  # bf16
+    alg = {
+        "permute": 3 * H * (N + Np) * d * e,           # Q, K, V: read real rows, write padded
+        "pool_select": 2 * H * N * d * e,              # pooling reads the real rows of Qp, Kp
+        "unpermute": 2 * H * N * d * e,                # O: read real slots, write raster rows
+    }
+    if wl.mode == "dynamic":
+        alg["zone_score"] = N * wl.video_channels * e + wl.n_audio * wl.video_channels * e
+    if wl.backward:
+        alg["permute_dO"] = H * (N + Np) * d * e
+        alg["unpermute_grads"] = 3 * 2 * H * N * d * 4  # fp32 dQ, dK, dV
+    out = {}
+    for stage, nbytes in alg.items():
+        ms = stage_ms[stage]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[stage] = {"ms": round(ms, 4), "alg_GB": round(nbytes / 1e9, 4), "alg_GBps": round(gbs, 1),
+                      "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 3)}
+    return out
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention-forward launch from the committed counter runs
+    (profiles/attn_fwd_720p_traffic.md), or None when they do not apply: another
+    workload, or kernel sources changed since the counters were taken."""
+    import hashlib
+    if workload != "720p":
+        return None
+    path = os.path.join(ROOT, "profiles", "attn_fwd_720p_traffic.md")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for src in ("attn_fwd.hip", "attn_common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "video_diffusion_block_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def copy_calib():
     import torch
     n = 1 << 30
@@ -188,8 +234,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
         },
+        "hbm_stages": hbm_stages(wl, sizes, stage_ms),
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
