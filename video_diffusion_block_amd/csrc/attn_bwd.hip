@@ -13,6 +13,7 @@
 // it), through a per-head bitmap, so every gradient row is owned by exactly
 // one thread and summed in a fixed order (no atomics, bitwise reproducible).
 #include "attn_common.hpp"
+#include "bsa.h"
 #include "kernels.hpp"
 
 namespace bsa {
@@ -388,7 +389,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
 //   S = Q K^T, dP = dO V^T, P = exp(S scale - lse), dS = P (dP - D),
 //   dV += P^T dO, dK += dS^T Q   (dO and Q through transposed LDS reads).
 // 4 wavefronts (one per SIMD): wave w owns keys 32w .. +32; K and V fragments
-// stay in registers; Q_i, dO_i, lse_i and D_i stream through LDS.
+// stay in registers; Q_i, dO_i, lse_i and D_i stream through LDS. Within a
+// query block the four 32-query tiles are software-pipelined: the S and dP
+// products of tile qt+1 are issued before the exponentials of tile qt, so the
+// matrix pipe works while the vector unit computes P and dS.
+// Tile loads are issued by hand (buffer loads into LDS, see dma16_manual): the
+// kernel waits for them itself (vmcnt(0) before the per-block barrier) and the
+// barrier is a bare s_barrier.
+constexpr int kMaxList = BSA_MAX_BLOCKS;
+
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
@@ -400,6 +409,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
   __shared__ __align__(16) __bf16 sO[2][kTile];
   __shared__ __align__(16) float sL[2][kB];
   __shared__ __align__(16) float sD[2][kB];
+  __shared__ int32_t sList[kMaxList];
   const int j = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,18 +427,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
 
   if (n > 0) {
-    const __bf16* qh0 = qp + head0 * kD;
-    const __bf16* oh0 = dop + head0 * kD;
-    auto dma_rows = [&](int buf, int ib) {
-      dma_tile<4>(sQ[buf], qh0 + (size_t)ib * kTile, w, lane);
-      dma_tile<4>(sO[buf], oh0 + (size_t)ib * kTile, w, lane);
-      if (w == 0 && lane < 32) {
-        const size_t q0 = head0 + (size_t)ib * kB;
-        __builtin_amdgcn_global_load_lds(lse + q0 + 4 * lane, (lds_void*)&sL[buf][0], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(delta + q0 + 4 * lane, (lds_void*)&sD[buf][0], 16, 0, 0);
-      }
+    const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
+    const i32x4 qrs = make_buffer_rsrc(qp + head0 * kD, head_bytes);
+    const i32x4 ors = make_buffer_rsrc(dop + head0 * kD, head_bytes);
+    const i32x4 lrs = make_buffer_rsrc(lse + head0, (uint32_t)L.Np * 4);
+    const i32x4 drs = make_buffer_rsrc(delta + head0, (uint32_t)L.Np * 4);
+    // tile load m (0..7) of wave w: LDS slots (4m + w) * 64 + lane, i.e. row
+    // 4 (4m + w) + lane / 16, physical chunk lane % 16 (swizzled fetch)
+    auto dma_part = [&](__bf16* tile, const i32x4& rs, int src, int m) {
+      const int r = 4 * (4 * m + w) + (lane >> 4);
+      const int q = (lane & 15) ^ uswz_f(r);
+      dma16_manual(rs, lds_addr_of(tile + (4 * m + w) * 512), 2 * (r * kD + 8 * q), src);
     };
-    dma_rows(0, lst[0]);
+    // the 128 lse and delta values of query block ib (512 bytes each): waves 0, 1, lanes 0..31
+    auto dma_stats = [&](int buf, int ib) {
+      if (w < 2 && lane < 32)
+        dma16_manual(w == 0 ? lrs : drs, lds_addr_of(w == 0 ? &sL[buf][0] : &sD[buf][0]),
+                     16 * lane, ib * kB * 4);
+    };
+    for (int e = tid; e < n; e += 256) sList[e] = lst[e];
+    {
+      const int ib = lst[0];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        dma_part(sQ[0], qrs, ib * kTile * 2, m);
+        dma_part(sO[0], ors, ib * kTile * 2, m);
+      }
+      dma_stats(0, ib);
+    }
 
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T):
     // lane holds K[key 32w + l32][16s + 8hi .. +8].
@@ -443,27 +469,50 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     const int fA = uswz_f(l32);
     int o1[4], o2[4];
     tr_offsets(o1, o2, 0, lane);
+    asm volatile("" ::"s"(c2));
+    __builtin_amdgcn_s_waitcnt(0);  // everything, the hand-issued loads included
+    __syncthreads();
+
+    // S and dP tiles of queries 32qt + (0..31) x keys 32w + (0..31)
+    auto sdp = [&](const __bf16* sq, const __bf16* so, int qt, f32x16& sc, f32x16& dpc) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = dpc[r] = 0.f;
+      const int ro = (32 * qt + l32) * kD;
+      bf16x8 a[8], b[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int off = ro + 8 * ((2 * s + hi) ^ fA);
+        a[s] = *reinterpret_cast<const bf16x8*>(sq + off);
+        b[s] = *reinterpret_cast<const bf16x8*>(so + off);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sc = mfma32x32x16(a[s], kf[s], sc);
+        dpc = mfma32x32x16(b[s], vf[s], dpc);
+      }
+    };
 
     for (int ii = 0; ii < n; ++ii) {
       const int b = ii & 1;
-      wait_dma();
-      __syncthreads();
-      if (ii + 1 < n) dma_rows(b ^ 1, lst[ii + 1]);
+      const bool more = ii + 1 < n;
+      const int ib1 = more ? __builtin_amdgcn_readfirstlane(sList[ii + 1]) : 0;
       const __bf16* sq = sQ[b];
       const __bf16* so = sO[b];
+      f32x16 sc, dpc;
+      sdp(sq, so, 0, sc, dpc);
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        // S, dP tiles: queries 32qt + (0..31) x keys 32w + (0..31)
-        f32x16 sc, dpc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = dpc[r] = 0.f;
-        const int ro = (32 * qt + l32) * kD;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int off = ro + 8 * ((2 * s + hi) ^ fA);
-          sc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sq + off), kf[s], sc);
-          dpc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(so + off), vf[s], dpc);
+        // next block's tiles, two loads of each per query tile
+        if (more) {
+          dma_part(sQ[b ^ 1], qrs, ib1 * kTile * 2, 2 * qt);
+          dma_part(sQ[b ^ 1], qrs, ib1 * kTile * 2, 2 * qt + 1);
+          dma_part(sO[b ^ 1], ors, ib1 * kTile * 2, 2 * qt);
+          dma_part(sO[b ^ 1], ors, ib1 * kTile * 2, 2 * qt + 1);
+          if (qt == 0) dma_stats(b ^ 1, ib1);
         }
+        f32x16 sn, dpn;
+        if (qt < 3) sdp(sq, so, qt + 1, sn, dpn);
+        __builtin_amdgcn_sched_barrier(0);
         // element r belongs to query 32qt + 8(r/4) + 4hi + r%4
         bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -495,7 +544,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
             dk[t] = mfma32x32x16(dsf[c], qb, dk[t]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (qt < 3) {
+          sc = sn;
+          dpc = dpn;
+        }
       }
+      // the next block's tiles have landed (every wave its own part) before
+      // anyone reads them; this block's buffers are free after the barrier
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
     }
   }
   // lane holds rows key 32w + 8(r/4) + 4hi + r%4, column d = 32t + l32
