@@ -475,20 +475,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
 
     // S and dP tiles of queries 32qt + (0..31) x keys 32w + (0..31)
     auto sdp = [&](const __bf16* sq, const __bf16* so, int qt, f32x16& sc, f32x16& dpc) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = dpc[r] = 0.f;
       const int ro = (32 * qt + l32) * kD;
       bf16x8 a[8], b[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      auto load = [&](int s) {
         const int off = ro + 8 * ((2 * s + hi) ^ fA);
         a[s] = *reinterpret_cast<const bf16x8*>(sq + off);
         b[s] = *reinterpret_cast<const bf16x8*>(so + off);
-      }
+      };
+      // fragments requested four k-steps (eight products) ahead of their use
+#pragma unroll
+      for (int s = 0; s < 4; ++s) load(s);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16 zero = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sc = mfma32x32x16(a[s], kf[s], sc);
-        dpc = mfma32x32x16(b[s], vf[s], dpc);
+        sc = mfma32x32x16(a[s], kf[s], s == 0 ? zero : sc);
+        dpc = mfma32x32x16(b[s], vf[s], s == 0 ? zero : dpc);
+        if (s + 4 < 8) load(s + 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -510,39 +514,86 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
           dma_part(sO[b ^ 1], ors, ib1 * kTile * 2, 2 * qt + 1);
           if (qt == 0) dma_stats(b ^ 1, ib1);
         }
+        // S and dP of the next query tile: all sixteen fragments requested
+        // first, then the products interleaved one by one with the vector
+        // work of this tile (a wavefront issues in order, so the matrix pipe
+        // stays busy only if its instructions are spread through the VALU ones)
         f32x16 sn, dpn;
-        if (qt < 3) sdp(sq, so, qt + 1, sn, dpn);
+        bf16x8 na[8], nb[8];
+        f32x4 l4[4], d4[4];
+        const int nro = (32 * (qt + 1) + l32) * kD;
+        auto nload = [&](int s) {
+          const int off = nro + 8 * ((2 * s + hi) ^ fA);
+          na[s] = *reinterpret_cast<const bf16x8*>(sq + off);
+          nb[s] = *reinterpret_cast<const bf16x8*>(so + off);
+        };
+        if (qt < 3) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) nload(s);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          l4[g] = *reinterpret_cast<const f32x4*>(&sL[b][32 * qt + 8 * g + 4 * hi]);
+          d4[g] = *reinterpret_cast<const f32x4*>(&sD[b][32 * qt + 8 * g + 4 * hi]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        if (qt < 3) {
+          const f32x16 zero = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            sn = mfma32x32x16(na[s], kf[s], s == 0 ? zero : sn);
+            dpn = mfma32x32x16(nb[s], vf[s], s == 0 ? zero : dpn);
+            if (s + 4 < 8) nload(s + 4);
+          }
+        }
         // element r belongs to query 32qt + 8(r/4) + 4hi + r%4
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[b][32 * qt + 8 * g + 4 * hi]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[b][32 * qt + 8 * g + 4 * hi]);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int r = 4 * g + rr;
-            const float p = exp2_fast(fmaf(sc[r], c2, -l4[rr] * kLog2e));
+            const float p = exp2_fast(fmaf(sc[r], c2, -l4[g][rr] * kLog2e));
             pf[r >> 3][r & 7] = (__bf16)p;
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dpc[r] - d4[rr]));
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dpc[r] - d4[g][rr]));
           }
         }
+        if (qt < 3) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+            if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // dV (keys x d) += P^T (keys x queries) dO (queries x d), and
         // dK += dS^T Q: k-step c covers queries 32qt + 16c + ..., read transposed.
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        bf16x8 ob[4][2], qb[4][2];
+        auto tload = [&](int t) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int base = (32 * qt + 16 * c) * kD;
-            const bf16x8 ob = __builtin_shufflevector(tr_read(so + base + o1[t]),
-                                                      tr_read(so + base + o2[t]), 0, 1, 2, 3,
-                                                      4, 5, 6, 7);
-            const bf16x8 qb = __builtin_shufflevector(tr_read(sq + base + o1[t]),
-                                                      tr_read(sq + base + o2[t]), 0, 1, 2, 3,
-                                                      4, 5, 6, 7);
-            dv[t] = mfma32x32x16(pf[c], ob, dv[t]);
-            dk[t] = mfma32x32x16(dsf[c], qb, dk[t]);
+            ob[t][c] = __builtin_shufflevector(tr_read(so + base + o1[t]),
+                                               tr_read(so + base + o2[t]), 0, 1, 2, 3, 4, 5, 6, 7);
+            qb[t][c] = __builtin_shufflevector(tr_read(sq + base + o1[t]),
+                                               tr_read(sq + base + o2[t]), 0, 1, 2, 3, 4, 5, 6, 7);
           }
+        };
+        // transposed fragments requested one d-tile (four products) ahead
+        tload(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t + 1 < 4) tload(t + 1);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            dv[t] = mfma32x32x16(pf[c], ob[t][c], dv[t]);
+            dk[t] = mfma32x32x16(dsf[c], qb[t][c], dk[t]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (qt < 3) {
