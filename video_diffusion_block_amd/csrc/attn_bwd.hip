@@ -262,6 +262,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dqp) {
   __shared__ __align__(16) __bf16 sK[2][kTile];
   __shared__ __align__(16) __bf16 sV[2][kTile];
+  __shared__ int32_t sList[BSA_MAX_BLOCKS];      // the row's key-block list
+  __shared__ __align__(16) uint32_t sM[2][64];   // block facts of the current/next block
   const int i = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,10 +284,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
         *reinterpret_cast<f32x4*>(dqp + qrow * kD + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  const __bf16* kh0 = kp + head0 * kD;
-  const __bf16* vh0 = vp + head0 * kD;
-  dma_tile<8>(sK[0], kh0 + (size_t)lst[0] * kTile, w, lane);
-  dma_tile<8>(sV[0], vh0 + (size_t)lst[0] * kTile, w, lane);
+  const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
+  const i32x4 krs = make_buffer_rsrc(kp + head0 * kD, head_bytes);
+  const i32x4 vrs = make_buffer_rsrc(vp + head0 * kD, head_bytes);
+  const i32x4 mrs = make_buffer_rsrc(meta, (uint32_t)L.M * sizeof(BlockMeta));
+  // tile load m (0..3) of wave w: LDS slots (8m + w) * 64 + lane (swizzled fetch)
+  auto dma_part = [&](__bf16* tile, const i32x4& rs, int src, int m) {
+    const int r = 4 * (8 * m + w) + (lane >> 4);
+    const int qq = (lane & 15) ^ uswz_f(r);
+    dma16_manual(rs, lds_addr_of(tile + (8 * m + w) * 512), 2 * (r * kD + 8 * qq), src);
+  };
+  // block blk's 32-byte record into slot sM[slot] (wave 0, one dword per lane)
+  auto fetch_meta = [&](int blk, int slot) {
+    if (w == 0) dma4_manual(mrs, lds_addr_of(&sM[slot][0]), 4 * (lane & 7), blk * 32);
+  };
+  for (int e = tid; e < n; e += 512) sList[e] = lst[e];
+  {
+    const int b0 = lst[0];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      dma_part(sK[0], krs, b0 * kTile * 2, m);
+      dma_part(sV[0], vrs, b0 * kTile * 2, m);
+    }
+    fetch_meta(b0, 0);
+  }
 
   bf16x8 qf[8], dof[8];
 #pragma unroll
@@ -307,36 +329,48 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  asm volatile("" ::"s"(c2));
+  __builtin_amdgcn_s_waitcnt(0);  // everything, the hand-issued loads included
+  __syncthreads();
 
   for (int jj = 0; jj < n; ++jj) {
     const int b = jj & 1;
-    wait_dma();
-    __syncthreads();
-    if (jj + 1 < n) {
-      dma_tile<8>(sK[b ^ 1], kh0 + (size_t)lst[jj + 1] * kTile, w, lane);
-      dma_tile<8>(sV[b ^ 1], vh0 + (size_t)lst[jj + 1] * kTile, w, lane);
-    }
+    const bool more = jj + 1 < n;
+    const int bn = more ? __builtin_amdgcn_readfirstlane(sList[jj + 1]) : 0;
+    // this block's validity words (this wave's 64 keys) and real-slot count
+    const uint32_t mw0 = sM[b][4 * kh], mw1 = sM[b][4 * kh + 1];
+    const bool partial = __builtin_amdgcn_readfirstlane((int)sM[b][2]) < kB;
     const __bf16* sk = sK[b];
     const __bf16* sv = sV[b];
     f32x16 st[2], dpt[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      // the next block's tiles and facts, spread over the products
+      if (more) {
+        dma_part(sK[b ^ 1], krs, bn * kTile * 2, 2 * kt);
+        dma_part(sK[b ^ 1], krs, bn * kTile * 2, 2 * kt + 1);
+        if (kt == 0) fetch_meta(bn, b ^ 1);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = dpt[kt][r] = 0.f;
       const int ro = (rowA + 32 * kt) * kD;
+      bf16x8 fa[8], fb[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int off = ro + 8 * ((2 * s + hi) ^ fA);
-        st[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sk + off), qf[s], st[kt]);
-        dpt[kt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(sv + off), dof[s], dpt[kt]);
+        fa[s] = *reinterpret_cast<const bf16x8*>(sk + off);
+        fb[s] = *reinterpret_cast<const bf16x8*>(sv + off);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st[kt] = mfma32x32x16(fa[s], qf[s], st[kt]);
+        dpt[kt] = mfma32x32x16(fb[s], dof[s], dpt[kt]);
       }
     }
-    const BlockMeta& mj = meta[lst[jj]];
-    const bool partial = mj.count() < kB;
     bf16x8 dsf[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint32_t word = mj.mask(2 * kh + kt) >> (4 * hi);
+      const uint32_t word = (kt ? mw1 : mw0) >> (4 * hi);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = exp2_fast(fmaf(st[kt][r], c2, -lse2));
@@ -347,6 +381,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     // dQ^T (d x queries) += K^T (d x keys) dS^T (keys x queries)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      if (more) dma_part(sV[b ^ 1], vrs, bn * kTile * 2, t);
       bf16x8 a[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -357,9 +392,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[t] = mfma32x32x16(a[c], dsf[c], acc[t]);
     }
+    // the next block's tiles and facts have landed (every wave its own part)
+    // before anyone reads them; this block's buffers are free after the barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
   }
-  wait_dma();
-  __syncthreads();
   // sum the two key halves (waves w and w+4 share their 32 queries)
   float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;
   if (kh == 1) {
