@@ -13,14 +13,15 @@
 // minimises the predicted within-block variance sum_a r_a (b_a^2-1)/(Z_a^2-1).
 //
 // Kernels:
-//  gram_kernel     G = A A^T (fp64 accumulation, stored fp32), tiny.
-//  a2v_kernel      per 128 tokens: logits^T = A X^T on bf16 MFMA (exact products,
+//  gram_kernel     G = A A^T on bf16 MFMA (exact products, fp32 sums), tiny.
+//  a2v_kernel      per 256 tokens: logits^T = A X^T on bf16 MFMA (exact products,
 //                  fp32 sums), softmax in fp32 registers (lane-local rows), then
-//                  g^2 = p^T G p as Y = G P^T on fp32 MFMA (32x32x2) and a
-//                  lane-local dot with P. Writes g [N] fp32.
-//  line_kernel     per (zone, 32-channel chunk): the zone's slice is staged in
-//                  LDS, then sum x^2 and the squared line sums along t, h, w in
-//                  fp64 (bf16 inputs make these sums exact), so
+//                  g^2 = p^T G p as Y = G P^T on fp32 MFMA (32x32x2) over the
+//                  upper tile pairs of the symmetric G and a lane-local dot
+//                  with P. Writes g [N] fp32.
+//  line_kernel     per (zone, 32-channel chunk): the zone is streamed through
+//                  LDS one t-slice at a time; sum x^2 and the squared line sums
+//                  along t, h, w in fp64 (bf16 inputs make these sums exact), so
 //                  V_a = (sum x^2 - sum_lines S^2/len) / (C n_z).
 //                  The same kernel with one channel handles g.
 //  decide_kernel   one workgroup: reduce the partials in a fixed order, the
@@ -36,35 +37,88 @@ namespace {
 constexpr double kTieRel = 1e-6;
 
 // ------------------------------------------------------------- Gram matrix --
-__global__ __launch_bounds__(256) void gram_kernel(const __bf16* A, int Na, int na_pad, int C,
-                                                   float* gram) {
-  const int j = blockIdx.x;  // row
-  for (int k = threadIdx.x; k < na_pad; k += 256) {
-    double s = 0.0;
-    if (j < Na && k < Na)
-      for (int c = 0; c < C; ++c)
-        s += (double)(float)A[(size_t)j * C + c] * (double)(float)A[(size_t)k * C + c];
-    gram[(size_t)j * na_pad + k] = (float)s;
+// One wavefront per 32 x 32 tile of G = A A^T on bf16 MFMA: the products of
+// bf16 values are exact and accumulate in fp32. Rows past Na read as zero.
+__global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int na_pad, int C,
+                                                  float* gram) {
+  const int ti = blockIdx.x, tj = blockIdx.y, lane = threadIdx.x;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int ra = 32 * ti + l32, rb = 32 * tj + l32;
+  const __bf16* pa = A + (size_t)ra * C + 8 * hi;
+  const __bf16* pb = A + (size_t)rb * C + 8 * hi;
+  f32x16 acc = {};
+  const bf16x8 zero = {};
+  for (int c = 0; c < C; c += 64) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // C is a multiple of 64
+      a[s] = ra < Na ? *reinterpret_cast<const bf16x8*>(pa + c + 16 * s) : zero;
+      b[s] = rb < Na ? *reinterpret_cast<const bf16x8*>(pb + c + 16 * s) : zero;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma32x32x16(a[s], b[s], acc);
   }
+  // lane holds G[32 ti + 8(r/4) + 4hi + r%4][32 tj + l32]
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    gram[(size_t)(32 * ti + 8 * (r >> 2) + 4 * hi + (r & 3)) * na_pad + 32 * tj + l32] = acc[r];
 }
 
 // --------------------------------------------------------------- A2V norm --
-constexpr int kTok = 128;        // tokens per workgroup (4 waves x 32)
-constexpr int kCh = 64;          // channels per LDS stage
-constexpr int kXS = kCh + 8;     // LDS row stride (bf16 elements)
-constexpr int kMaxMT = 8;        // audio tiles of 32 (n_audio <= 256)
+// 8 wavefronts x 32 tokens per workgroup. Phase 1, logits^T = A X^T on bf16
+// MFMA: X fragments are loaded straight into registers (each token row is read
+// once, by its own wavefront) one channel chunk ahead; A, shared by the
+// wavefronts, streams through LDS in 64-channel chunks, double-buffered, with
+// hand-issued buffer loads (rows past Na read as zero) laid out piece-major
+// ([8-channel piece][audio row]) so the fragment reads are conflict free.
+// Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p on fp32 MFMA over
+// the tile pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice),
+// G's row blocks staged in LDS over the (then free) A buffers.
+constexpr int kA2vWaves = 8;
+constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
+constexpr int kCh = 64;               // channels per A chunk
+constexpr int kMaxMT = 8;             // audio tiles of 32 (n_audio <= 256)
 
 template <int MT>
-__global__ __launch_bounds__(256) void a2v_kernel(const __bf16* X, int C, long long N,
-                                                  const __bf16* A, int Na, const float* gram,
-                                                  float inv_sqrt_c, float* gout) {
-  __shared__ __align__(16) __bf16 xs[kTok * kXS];
-  __shared__ __align__(16) __bf16 as[32 * MT * kXS];
-  __shared__ float gs[32 * (32 * MT + 1)];
+__global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, int C, long long N,
+                                                             const __bf16* A, int Na,
+                                                             const float* gram, float inv_sqrt_c,
+                                                             float* gout) {
   constexpr int NA_PAD = 32 * MT;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int SLOTS = 8 * NA_PAD;               // 16-byte slots per A chunk
+  constexpr int ABUF = SLOTS * 8;                  // bf16 elements per A buffer
+  constexpr int GS = 32 * (NA_PAD + 1);            // floats of one staged G row block
+  constexpr int LDS_BYTES = (2 * ABUF * 2 > GS * 4) ? 2 * ABUF * 2 : GS * 4;
+  __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+  __bf16* abuf = reinterpret_cast<__bf16*>(smem);  // [2][piece][row][8]
+  float* gs = reinterpret_cast<float*>(smem);      // [32][NA_PAD + 1] (phase 2)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const long long n0 = (long long)blockIdx.x * kTok;
+  const long long n0 = (long long)blockIdx.x * kTok + 32 * w;  // this wave's first token
+  const long long tok = n0 + l32;
+  const bool tok_ok = tok < N;
+  const int nchunks = C / kCh;
+
+  const i32x4 ars = make_buffer_rsrc(A, (uint32_t)Na * C * 2);
+  // A chunk ch into buffer bf: slot s = piece * NA_PAD + row <- A[row][64 ch + 8 piece ..]
+  auto load_a = [&](int ch, int bf) {
+    for (int u = w; u * 64 < SLOTS; u += kA2vWaves) {
+      const int sl = u * 64 + lane;
+      const int piece = sl / NA_PAD, r = sl - piece * NA_PAD;
+      const int voff = sl < SLOTS ? (r * C + kCh * ch + 8 * piece) * 2 : 0;
+      dma16_manual(ars, lds_addr_of(abuf + bf * ABUF + u * 64 * 8),
+                   sl < SLOTS ? voff : (int)(0x7fffffff & ~15), 0);
+    }
+  };
+  // X fragments of chunk ch: lane holds X[tok][64 ch + 16 ks + 8 hi .. +8]
+  const bf16x8 zero8 = {};
+  auto load_x = [&](int ch, bf16x8 (&xf)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      xf[ks] = tok_ok ? *reinterpret_cast<const bf16x8*>(X + tok * C + kCh * ch + 16 * ks + 8 * hi)
+                      : zero8;
+  };
 
   f32x16 acc[MT];
 #pragma unroll
@@ -72,30 +126,34 @@ __global__ __launch_bounds__(256) void a2v_kernel(const __bf16* X, int C, long l
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  for (int c0 = 0; c0 < C; c0 += kCh) {
-    __syncthreads();
-    for (int e = tid; e < kTok * (kCh / 8); e += 256) {
-      const int r = e >> 3, c = e & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + r < N) v = *reinterpret_cast<const uint4*>(X + (size_t)(n0 + r) * C + c0 + 8 * c);
-      *reinterpret_cast<uint4*>(xs + r * kXS + 8 * c) = v;
+  bf16x8 xa[4];
+  load_a(0, 0);
+  load_x(0, xa);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int bf = ch & 1;
+    // the next chunk's A (into the other buffer) and X fragments, in flight
+    // while this chunk is multiplied
+    bf16x8 xn[4];
+    if (ch + 1 < nchunks) {
+      load_a(ch + 1, bf ^ 1);
+      load_x(ch + 1, xn);
     }
-    for (int e = tid; e < NA_PAD * (kCh / 8); e += 256) {
-      const int r = e >> 3, c = e & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < Na) v = *reinterpret_cast<const uint4*>(A + (size_t)r * C + c0 + 8 * c);
-      *reinterpret_cast<uint4*>(as + r * kXS + 8 * c) = v;
-    }
-    __syncthreads();
+    const __bf16* ab = abuf + bf * ABUF;
 #pragma unroll
-    for (int ks = 0; ks < kCh / 16; ++ks) {
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(xs + (32 * w + l32) * kXS + 16 * ks + 8 * hi);
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + (32 * mt + l32) * kXS + 16 * ks + 8 * hi);
-        acc[mt] = mfma32x32x16(a, b, acc[mt]);
+        const bf16x8 af =
+            *reinterpret_cast<const bf16x8*>(ab + ((2 * ks + hi) * NA_PAD + 32 * mt + l32) * 8);
+        acc[mt] = mfma32x32x16(af, xa[ks], acc[mt]);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk has landed
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xa[ks] = xn[ks];
   }
 
   // softmax over the audio axis; lane holds audio 32mt + 8(r/4) + 4hi + r%4
@@ -120,113 +178,127 @@ __global__ __launch_bounds__(256) void a2v_kernel(const __bf16* X, int C, long l
     }
   z += __shfl_xor(z, 32);
 
-  // g^2 * z^2 = sum_m p_m (G p)_m, with (G p) from fp32 MFMA per 32-row tile of G
+  // g^2 z^2 = sum over tile pairs of p_mt . (G[mt][kt] p_kt), kt >= mt, the
+  // off-diagonal pairs twice (G is symmetric)
   float gsq = 0.f;
+#pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     __syncthreads();
-    for (int e = tid; e < 32 * NA_PAD; e += 256) {
-      const int r = e / NA_PAD, c = e % NA_PAD;
+    for (int e = tid; e < 32 * NA_PAD; e += 64 * kA2vWaves) {
+      const int r = e / NA_PAD, c = e - r * NA_PAD;
       gs[r * (NA_PAD + 1) + c] = gram[(size_t)(32 * mt + r) * NA_PAD + c];
     }
     __syncthreads();
-    f32x16 y;
+    float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) y[r] = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < MT; ++kt)
+    for (int kt = mt; kt < MT; ++kt) {
+      f32x16 y = {};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int a = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        y = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[l32 * (NA_PAD + 1) + a], acc[kt][r], y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[l32 * (NA_PAD + 1) + a], acc[kt][r], y, 0,
+                                                 0, 0);
       }
+      float d = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) gsq = fmaf(y[r], acc[mt][r], gsq);
+      for (int r = 0; r < 16; ++r) d = fmaf(y[r], acc[mt][r], d);
+      part += kt == mt ? d : 2.f * d;
+    }
+    gsq += part;
   }
   gsq += __shfl_xor(gsq, 32);
-  const long long n = n0 + 32 * w + l32;
-  if (hi == 0 && n < N) gout[n] = sqrtf(fmaxf(gsq, 0.f)) / z;
+  if (hi == 0 && tok_ok) gout[tok] = sqrtf(fmaxf(gsq, 0.f)) / z;
 }
 
 // ------------------------------------------------------- line sum partials --
 // Partials per (zone, chunk of kLC channels): [0] sum x^2, [1..3] sum over the
-// lines along t, h, w of (line sum)^2 / line length, all in fp64 (bf16 and fp32
-// inputs make these sums exact). The zone's slice of kLC channels is staged in
-// LDS with 16-byte loads, then each line is summed by one thread (no atomics,
-// fixed summation order).
-constexpr int kLC = 32;  // channels per workgroup
+// lines along t, h, w of (line sum)^2 / line length, in fp64 (for bf16 inputs
+// the sums and squares are exact; the division by the length is a multiply by
+// its rounded reciprocal). The zone is streamed one t-slice (16 x 16 tokens x
+// kLC channels) at a time through LDS: w- and h-lines are complete inside a
+// slice, t-lines accumulate in registers across slices. Each thread owns fixed
+// lines and the workgroup reduction has a fixed order (deterministic).
+constexpr int kLC = 32;   // channels per workgroup
+constexpr int kLT = 512;  // threads per workgroup
+constexpr int kTI = 256 * kLC / kLT;  // t-line items per thread
 
 template <typename T>
-__global__ __launch_bounds__(256) void line_kernel(Lay L, const T* __restrict__ X, int C,
+__global__ __launch_bounds__(kLT) void line_kernel(Lay L, const T* __restrict__ X, int C,
                                                    double* __restrict__ part) {
-  __shared__ T xs[4 * 16 * 16 * kLC];  // [t][h][w][c]: 64 KB for bf16 (exact copies)
-  __shared__ double red[4][4];
-  const int z = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
+  __shared__ T xs[16 * 16 * kLC];  // one t-slice: [h][w][c]
+  __shared__ double red[4][kLT / 64];
+  const int z = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y, tid = threadIdx.x;
   const int zzt = z / (L.gzh * L.gzw), zzh = (z / L.gzw) % L.gzh, zzw = z % L.gzw;
   const int t0 = zzt * L.zt, h0 = zzh * L.zh, w0 = zzw * L.zw;
   const int vt = imax(0, imin(L.zt, L.T - t0));
   const int vh = imax(0, imin(L.zh, L.H - h0));
   const int vw = imax(0, imin(L.zw, L.W - w0));
   const int c0 = chunk * kLC;
-  const int cw = imin(kLC, C - c0);            // channels in this chunk
-  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte load
-  const int nseg = kLC / EPC;                  // 16-byte segments per token
-  const int ntok = vt * vh * vw;
-  // stage: token k (raster inside the zone's real box), segment sg
-  for (int e = threadIdx.x; e < ntok * nseg; e += 256) {
-    const int k = e / nseg, sg = e - k * nseg;
-    const int tw = k % vw, th = (k / vw) % vh, tt = k / (vw * vh);
-    const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
-    T* dst = xs + ((tt * 16 + th) * 16 + tw) * kLC + sg * EPC;
-    const int cc = c0 + sg * EPC;
-    if (cc + EPC <= C && (C % EPC) == 0) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
-    } else {
-      for (int q = 0; q < EPC; ++q) dst[q] = cc + q < C ? X[n * C + cc + q] : (T)0.f;
+  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int NSEG = kLC / EPC;       // 16-byte segments per token
+  const bool vec = (C % EPC) == 0;
+  const double inv_vw = vw ? 1.0 / vw : 0.0, inv_vh = vh ? 1.0 / vh : 0.0;
+  const double inv_vt = vt ? 1.0 / vt : 0.0;
+  double q = 0.0, rh = 0.0, rw = 0.0;
+  double tacc[kTI];  // t-line sums of items tid + kLT j: channel item % 32, token item / 32
+#pragma unroll
+  for (int j = 0; j < kTI; ++j) tacc[j] = 0.0;
+  for (int tt = 0; tt < vt; ++tt) {
+    __syncthreads();
+    // stage the slice: token k = 16 th + tw, segment sg
+    for (int e = tid; e < 256 * NSEG; e += kLT) {
+      const int k = e / NSEG, sg = e % NSEG;
+      const int th = k >> 4, tw = k & 15;
+      T* dst = xs + k * kLC + sg * EPC;
+      const int cc = c0 + sg * EPC;
+      if (th < vh && tw < vw) {
+        const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
+        if (vec && cc + EPC <= C) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
+        } else {
+          for (int qq = 0; qq < EPC; ++qq) dst[qq] = cc + qq < C ? X[n * C + cc + qq] : (T)0.f;
+        }
+      } else {
+        for (int qq = 0; qq < EPC; ++qq) dst[qq] = (T)0.f;
+      }
+    }
+    __syncthreads();
+    // w-lines (th, c) and h-lines (tw, c) of this slice, one of each per thread
+    {
+      const int item = tid, c = item & 31, l = item >> 5;
+      double sw = 0.0, sh = 0.0;
+      for (int u = 0; u < 16; ++u) {
+        const double xw = (double)(float)xs[(l * 16 + u) * kLC + c];  // (th = l, tw = u)
+        const double xh = (double)(float)xs[(u * 16 + l) * kLC + c];  // (th = u, tw = l)
+        sw += xw;
+        q += xw * xw;
+        sh += xh;
+      }
+      rw += l < vh ? sw * sw * inv_vw : 0.0;
+      rh += l < vw ? sh * sh * inv_vh : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < kTI; ++j) {
+      const int item = tid + kLT * j;
+      tacc[j] += (double)(float)xs[(item >> 5) * kLC + (item & 31)];
     }
   }
-  __syncthreads();
-  double q = 0.0, rt = 0.0, rh = 0.0, rw = 0.0;
-  // w-lines (t, h, c) and the squares
-  for (int e = threadIdx.x; e < vt * vh * cw; e += 256) {
-    const int c = e % cw, th = (e / cw) % vh, tt = e / (cw * vh);
-    const T* p = xs + ((tt * 16 + th) * 16) * kLC + c;
-    double sum = 0.0;
-    for (int tw = 0; tw < vw; ++tw) {
-      const double x = (double)(float)p[tw * kLC];
-      sum += x;
-      q += x * x;
-    }
-    rw += sum * sum / (double)vw;
-  }
-  // h-lines (t, w, c)
-  for (int e = threadIdx.x; e < vt * vw * cw; e += 256) {
-    const int c = e % cw, tw = (e / cw) % vw, tt = e / (cw * vw);
-    const T* p = xs + (tt * 16 * 16 + tw) * kLC + c;
-    double sum = 0.0;
-    for (int th = 0; th < vh; ++th) sum += (double)(float)p[th * 16 * kLC];
-    rh += sum * sum / (double)vh;
-  }
-  // t-lines (h, w, c)
-  for (int e = threadIdx.x; e < vh * vw * cw; e += 256) {
-    const int c = e % cw, tw = (e / cw) % vw, th = e / (cw * vw);
-    const T* p = xs + (th * 16 + tw) * kLC + c;
-    double sum = 0.0;
-    for (int tt = 0; tt < vt; ++tt) sum += (double)(float)p[tt * 16 * 16 * kLC];
-    rt += sum * sum / (double)vt;
-  }
+  double rt = 0.0;
+#pragma unroll
+  for (int j = 0; j < kTI; ++j) rt += tacc[j] * tacc[j] * inv_vt;
   // workgroup reduction in a fixed order (deterministic)
   double vals[4] = {q, rt, rh, rw};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     double v = vals[k];
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = v;
+    if ((tid & 63) == 0) red[k][tid >> 6] = v;
   }
   __syncthreads();
-  if (threadIdx.x < 4) {
-    const double sres = red[threadIdx.x][0] + red[threadIdx.x][1] + red[threadIdx.x][2] +
-                        red[threadIdx.x][3];
-    part[((size_t)z * nchunks + chunk) * 4 + threadIdx.x] = sres;
+  if (tid < 4) {
+    double sres = 0.0;
+    for (int v = 0; v < kLT / 64; ++v) sres += red[tid][v];
+    part[((size_t)z * nchunks + chunk) * 4 + tid] = sres;
   }
 }
 
@@ -359,19 +431,19 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
   const bool use_audio = audio != nullptr && n_audio > 0;
   if (use_audio) {
     const __bf16* A = static_cast<const __bf16*>(audio);
-    gram_kernel<<<pad, 256, 0, st>>>(A, n_audio, pad, C, gram);
-    const unsigned grid = (unsigned)((L.N + kTok - 1) / kTok);
+    gram_kernel<<<dim3(pad / 32, pad / 32), 64, 0, st>>>(A, n_audio, pad, C, gram);
+    const unsigned grid = (unsigned)((L.N + kTok - 1) / kTok);  // C % 64 == 0 (checked)
     const float isc = 1.0f / sqrtf((float)C);
     switch (pad / 32) {
 #define BSA_A2V(MT) \
-  case MT: a2v_kernel<MT><<<grid, 256, 0, st>>>(X, C, L.N, A, n_audio, gram, isc, g); break;
+  case MT: a2v_kernel<MT><<<grid, 64 * kA2vWaves, 0, st>>>(X, C, L.N, A, n_audio, gram, isc, g); break;
       BSA_A2V(1) BSA_A2V(2) BSA_A2V(3) BSA_A2V(4) BSA_A2V(5) BSA_A2V(6) BSA_A2V(7) BSA_A2V(8)
 #undef BSA_A2V
       default: return hipErrorInvalidValue;
     }
-    line_kernel<float><<<dim3(L.nZ, 1), 256, 0, st>>>(L, g, 1, gpart);
+    line_kernel<float><<<dim3(L.nZ, 1), kLT, 0, st>>>(L, g, 1, gpart);
   }
-  line_kernel<__bf16><<<dim3(L.nZ, chunks), 256, 0, st>>>(L, X, C, xpart);
+  line_kernel<__bf16><<<dim3(L.nZ, chunks), kLT, 0, st>>>(L, X, C, xpart);
   decide_kernel<<<1, 256, 0, st>>>(L, C, chunks, xpart, gpart, use_audio ? 1 : 0, zone_shape,
                                    zone_stats, scratch);
   return hipGetLastError();
