@@ -51,7 +51,7 @@ extern "C" {
 
 #define BSA_ABI_VERSION 1
 #define BSA_MAX_SHAPES 4
-#define BSA_MAX_BLOCKS 4096   /* per layout: bound of the in-LDS selection sort */
+#define BSA_MAX_BLOCKS 4096   /* per layout: one selection row lives in one wavefront's registers, and the attention block lists are staged in LDS */
 
 typedef enum {
   BSA_OK = 0,

@@ -149,6 +149,18 @@ __device__ inline int wave_min(int v) {
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
   return v;
 }
+__device__ inline double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+// Order-preserving map of a finite double to uint64, reversed: a smaller key
+// is a larger logit.
+__device__ inline uint64_t rank_key(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t mono = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return ~mono;
+}
 template <typename T>
 __device__ inline T wave_exclusive_scan(T v, int lane) {
   T incl = v;
@@ -160,49 +172,16 @@ __device__ inline T wave_exclusive_scan(T v, int lane) {
   return incl - v;
 }
 
-// Bitonic compare-exchange steps on a row held in registers: lane l holds
-// sorted positions C l .. C l + C - 1 (element e at position C l + e). Within
-// a lane the partner of e is e ^ JJ (JJ < C, known at compile time); across
-// lanes the partner of lane l is lane l ^ (jj / C), same e. Positions whose
-// bit k is clear are sorted into "before" order, the others reversed.
-template <int C, int JJ>
-__device__ inline void bitonic_in_lane(double (&key)[C], int (&id)[C], int lane, int k) {
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    if (e & JJ) continue;
-    const int f = e | JJ;
-    const bool up = ((lane * C + e) & k) == 0;
-    const bool swap = up ? before(key[f], id[f], key[e], id[e])
-                         : before(key[e], id[e], key[f], id[f]);
-    const double ke = key[e], kf = key[f];
-    const int ie = id[e], jf = id[f];
-    key[e] = swap ? kf : ke;
-    key[f] = swap ? ke : kf;
-    id[e] = swap ? jf : ie;
-    id[f] = swap ? ie : jf;
-  }
-}
-template <int C>
-__device__ inline void bitonic_cross_lane(double (&key)[C], int (&id)[C], int lane, int k, int jj) {
-  const int lm = jj / C;
-  const bool lower = (lane & lm) == 0;
-  const bool up = ((lane * C) & k) == 0;  // bit k of the position (k > jj >= C)
-  const bool keep_first = lower == up;
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    const double ko = __shfl_xor(key[e], lm);
-    const int io = __shfl_xor(id[e], lm);
-    const bool mine_first = before(key[e], id[e], ko, io);
-    if (mine_first != keep_first) {
-      key[e] = ko;
-      id[e] = io;
-    }
-  }
-}
-
-// One wavefront per (head, query block) row, WAVES rows per workgroup. The
-// row's P2 = 64 C entries (logit, block id) are sorted in registers by a
-// bitonic network (lane-local steps and cross-lane exchanges), then scanned.
+// One wavefront per (head, query block) row, WAVES rows per workgroup; lane l
+// holds the row's logits of key blocks P2/64 l .. P2/64 (l + 1) - 1 in
+// registers. No sort: the cut of the order (logit descending, id ascending) is
+// found by MSB-first radix selection on an order-preserving 64-bit key (eight
+// 8-bit digits, LDS histograms, wave scans), first for rank k; when the top-k
+// set already holds probability mass >= tau it is the list, otherwise a second
+// selection finds the element at which the mass in that order reaches tau (bins
+// carry the mass as well), and the list is everything up to it. Equal logits at
+// a cut are taken in id order. The selected ids are compacted in ascending
+// order through an LDS bitmap and a wave scan.
 template <int P2, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMeta* __restrict__ meta,
                                                              const double* __restrict__ logits,
@@ -211,6 +190,8 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
                                                              int32_t* __restrict__ idx) {
   constexpr int C = P2 / 64;  // entries per lane
   __shared__ uint32_t sbits[WAVES][P2 / 32];
+  __shared__ uint32_t shist[WAVES][256];
+  __shared__ double smass[WAVES][256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * WAVES + w, h = blockIdx.y;
   if (i >= L.M) return;  // (whole wavefront)
@@ -236,71 +217,216 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
 #pragma unroll
   for (int e = lane; e < P2 / 32; e += 64) bits[e] = 0u;
   const int mv = wave_sum(valid);
+  const int k_top = max(1, (mv * (10000 - sparsity_1e4) + 9999) / 10000);
 
-  // bitonic sort: logit descending, then block id ascending
-  for (int k = 2; k <= P2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      if (jj >= C) {
-        bitonic_cross_lane<C>(key, id, lane, k, jj);
-      } else {
-        switch (jj) {
-          case 1: bitonic_in_lane<C, 1>(key, id, lane, k); break;
-          case 2: bitonic_in_lane<C, (C > 2 ? 2 : 1)>(key, id, lane, k); break;
-          case 4: bitonic_in_lane<C, (C > 4 ? 4 : 1)>(key, id, lane, k); break;
-          case 8: bitonic_in_lane<C, (C > 8 ? 8 : 1)>(key, id, lane, k); break;
-          case 16: bitonic_in_lane<C, (C > 16 ? 16 : 1)>(key, id, lane, k); break;
-          default: bitonic_in_lane<C, (C > 32 ? 32 : 1)>(key, id, lane, k); break;
+  // The top-k set from a radix select of the k-th best (logit descending,
+  // then id ascending); when its softmax mass reaches tau the CDF prefix is
+  // inside it and the list is the top-k set.
+  {
+    uint32_t* hist = shist[w];
+    double mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < C; ++e) mloc = fmax(mloc, key[e]);
+    const double mx = wave_max(mloc);
+    uint64_t prefix = 0;
+    int remaining = k_top;  // rank still to find inside the current prefix
+    int count_eq = 0;       // elements equal to the final prefix
+#pragma unroll 1
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      const uint64_t above = pass ? ~0ull << (shift + 8) : 0ull;
+#pragma unroll
+      for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        if (key[e] != -INFINITY) {
+          const uint64_t u = rank_key(key[e]);
+          if ((u & above) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
         }
       }
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const int local = (int)(c0 + c1 + c2 + c3);
+      const int before = wave_exclusive_scan(local, lane);
+      // the lane whose four bins hold the rank
+      const bool here = before < remaining && remaining <= before + local;
+      const uint64_t ball = __ballot(here);
+      const int src = __ffsll((long long)ball) - 1;
+      // within the lane: the first bin whose cumulative count reaches the rank
+      int digit = 0, cb = 0, ce = 0;
+      {
+        const int cs[4] = {(int)c0, (int)c1, (int)c2, (int)c3};
+        int acc = before;
+        bool got = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (!got && remaining <= acc + cs[q]) {
+            got = true;
+            digit = 4 * lane + q;
+            cb = acc;
+            ce = cs[q];
+          }
+          acc += cs[q];
+        }
+      }
+      digit = __shfl(digit, src);
+      cb = __shfl(cb, src);
+      ce = __shfl(ce, src);
+      prefix |= (uint64_t)digit << shift;
+      remaining -= cb;
+      count_eq = ce;
+    }
+    // ties on the logit: the `remaining` smallest ids among the equal ones
+    int id_cut = INT_MAX;
+    if (remaining < count_eq) {
+      int cur = -1;
+#pragma unroll 1
+      for (int r = 0; r < remaining; ++r) {
+        int mn = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < C; ++e)
+          if (key[e] != -INFINITY && rank_key(key[e]) == prefix && id[e] > cur) mn = min(mn, id[e]);
+        cur = wave_min(mn);
+      }
+      id_cut = cur;
+    }
+    double zl = 0.0, ml = 0.0;
+#pragma unroll
+    for (int e = 0; e < C; ++e) {
+      if (key[e] != -INFINITY) {
+        const double ex = exp(key[e] - mx);
+        const uint64_t u = rank_key(key[e]);
+        zl += ex;
+        if (u < prefix || (u == prefix && id[e] <= id_cut)) ml += ex;
+      }
+    }
+    const double Z = wave_sum(zl);
+    const double mass = wave_sum(ml) / Z;
+    int n_sel = k_top;
+    if (mass < tau) {
+      // The CDF prefix is longer than k: a second radix select, now of the
+      // first element at which the mass in (logit desc, id asc) order reaches
+      // tau; bins carry counts and probability mass.
+      double* hm = smass[w];
+      prefix = 0;
+      double mbefore = 0.0;  // mass of the elements ranked before the prefix range
+      int cbefore = 0;       // their count
+      count_eq = 0;
+#pragma unroll 1
+      for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        const uint64_t above = pass ? ~0ull << (shift + 8) : 0ull;
+#pragma unroll
+        for (int b = lane; b < 256; b += 64) {
+          hist[b] = 0u;
+          hm[b] = 0.0;
+        }
+#pragma unroll
+        for (int e = 0; e < C; ++e) {
+          if (key[e] != -INFINITY) {
+            const uint64_t u = rank_key(key[e]);
+            if ((u & above) == prefix) {
+              atomicAdd(&hist[(u >> shift) & 255], 1u);
+              atomicAdd(&hm[(u >> shift) & 255], exp(key[e] - mx) / Z);
+            }
+          }
+        }
+        const int cs[4] = {(int)hist[4 * lane], (int)hist[4 * lane + 1], (int)hist[4 * lane + 2],
+                           (int)hist[4 * lane + 3]};
+        const double ms[4] = {hm[4 * lane], hm[4 * lane + 1], hm[4 * lane + 2], hm[4 * lane + 3]};
+        const double lm = (ms[0] + ms[1]) + (ms[2] + ms[3]);
+        const int lc = cs[0] + cs[1] + cs[2] + cs[3];
+        const double bm = mbefore + wave_exclusive_scan(lm, lane);
+        const int bc = cbefore + wave_exclusive_scan(lc, lane);
+        // the bin holding the crossing: the first whose cumulative mass reaches
+        // tau; if rounding left this range's total just under tau (the bins'
+        // sums regroup the previous pass's), its last non-empty bin
+        const bool here = bm < tau && tau <= bm + lm;
+        const uint64_t ball = __ballot(here);
+        const uint64_t nonempty = __ballot(lc > 0);
+        const int src = ball ? __ffsll((long long)ball) - 1 : 63 - __clzll((long long)nonempty);
+        int digit = 0, cbin = bc, ceq = 0;
+        double mbin = bm;
+        {
+          double acc = bm;
+          int accc = bc;
+          bool got = false;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool take = ball ? (!got && cs[q] > 0 && tau <= acc + ms[q]) : cs[q] > 0;
+            if (take) {
+              got = true;
+              digit = 4 * lane + q;
+              mbin = acc;
+              cbin = accc;
+              ceq = cs[q];
+            }
+            acc += ms[q];
+            accc += cs[q];
+          }
+        }
+        digit = __shfl(digit, src);
+        mbefore = __shfl(mbin, src);
+        cbefore = __shfl(cbin, src);
+        count_eq = __shfl(ceq, src);
+        prefix |= (uint64_t)digit << shift;
+      }
+      // equal logits at the crossing: take them in id order until tau
+      int cut = INT_MAX, taken = count_eq;
+      if (count_eq > 1) {
+        int cur = -1;
+        double acc = mbefore;
+        taken = 0;
+#pragma unroll 1
+        for (int r = 0; r < count_eq; ++r) {
+          int mn = INT_MAX;
+          double pe = 0.0;
+#pragma unroll
+          for (int e = 0; e < C; ++e)
+            if (key[e] != -INFINITY && rank_key(key[e]) == prefix && id[e] > cur && id[e] < mn) {
+              mn = id[e];
+              pe = exp(key[e] - mx) / Z;
+            }
+          const int mw = wave_min(mn);
+          const uint64_t own = __ballot(mn == mw && mn != INT_MAX);
+          pe = __shfl(pe, __ffsll((long long)own) - 1);
+          cur = mw;
+          acc += pe;
+          ++taken;
+          if (acc >= tau) break;
+        }
+        cut = cur;
+      }
+      const int m_cdf = cbefore + taken;
+      n_sel = min(max(k_top, m_cdf), mv);
+      id_cut = cut;  // the list: every element ranked up to the crossing
+    }
+    {
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        if (key[e] != -INFINITY) {
+          const uint64_t u = rank_key(key[e]);
+          if (u < prefix || (u == prefix && id[e] <= id_cut))
+            atomicOr(&bits[id[e] >> 5], 1u << (id[e] & 31));
+        }
+      }
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        const int b = lane * C + e;
+        cnt += (bits[b >> 5] >> (b & 31)) & 1u;
+      }
+      int pos = wave_exclusive_scan(cnt, lane);
+      int32_t* out = idx + row * L.M;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        const int b = lane * C + e;
+        if ((bits[b >> 5] >> (b & 31)) & 1u) out[pos++] = b;
+      }
+      if (lane == 0) counts[row] = n_sel;
     }
   }
 
-  // softmax mass in sorted order, prefix-summed; m = first prefix reaching tau
-  const double mx = __shfl(key[0], 0);
-  double* ex = key;  // exp(l - max) replaces the logits
-  double z_loc = 0.0;
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    ex[e] = lane * C + e < mv ? exp(key[e] - mx) : 0.0;
-    z_loc += ex[e];
-  }
-  const double Z = wave_sum(z_loc);
-  double run = 0.0;
-#pragma unroll
-  for (int e = 0; e < C; ++e) run += ex[e] / Z;
-  double c = wave_exclusive_scan(run, lane);
-  int m_loc = INT_MAX;
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    const int r = lane * C + e;
-    if (r < mv && m_loc == INT_MAX) {
-      c += ex[e] / Z;
-      if (c >= tau) m_loc = r + 1;
-    }
-  }
-  const int m_first = wave_min(m_loc);
-  const int m = m_first == INT_MAX ? mv : m_first;
-  const int k = max(1, (mv * (10000 - sparsity_1e4) + 9999) / 10000);
-  const int n = min(max(k, m), mv);
-#pragma unroll
-  for (int e = 0; e < C; ++e)
-    if (lane * C + e < n) atomicOr(&bits[id[e] >> 5], 1u << (id[e] & 31));
-
-  // ascending compaction of the selected block ids (lane l: ids C l .. C l + C - 1)
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    const int b = lane * C + e;
-    cnt += (bits[b >> 5] >> (b & 31)) & 1u;
-  }
-  int pos = wave_exclusive_scan(cnt, lane);
-  int32_t* out = idx + row * L.M;
-#pragma unroll
-  for (int e = 0; e < C; ++e) {
-    const int b = lane * C + e;
-    if ((bits[b >> 5] >> (b & 31)) & 1u) out[pos++] = b;
-  }
-  if (lane == 0) counts[row] = n;
 }
 
 }  // namespace
