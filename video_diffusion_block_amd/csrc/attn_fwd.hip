@@ -120,13 +120,10 @@ __device__ inline void dma_tile(__bf16* tile, const i32x4& rsrc, int src, int w,
   for (int m = 0; m < 4; ++m) dma_part<kIsV>(tile, rsrc, src, w, lane, m);
 }
 
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained), as a builtin so that the
-// compiler's own wait-count tracking sees it.
-__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): vmcnt(0), vmcnt(4), lgkmcnt(0), each leaving the others free.
+// lgkmcnt 11:8): vmcnt(0) and lgkmcnt(0), each leaving the others free. Issued
+// as builtins so that the compiler's own wait-count tracking sees them.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
 constexpr int kWaitLgkm0 = 0xC07F;
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
@@ -311,8 +308,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
   fetch_meta(blk0, 0);
+  fetch_meta(blk1, 1);
   dma_tile<false>(sK[1], krs, blk1 * kTileBytes, w, lane);  // (block 0 again if n = 1)
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);                     // all but K1
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
   const int koff = (64 * kh + l32) * kD;
@@ -345,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   __syncthreads();
   HalfMeta meta_j = uniform(read_meta(0));
 
-  auto softmax = [&](bf16x8 (&pf8)[4]) {
+  auto softmax = [&](bf16x8 (&pf8)[4], auto hook) {
     // Online softmax (log2 domain) with a lazily updated reference max: the
     // exponent base m_run moves only when a row max exceeds it by more than
     // kLazy (then p <= 2^kLazy, safe in bf16 and fp32), so O is rarely
@@ -371,8 +369,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
         pf8[2 * kt + (r >> 3)][r & 7] = (__bf16)exp2_fast(fmaf(s_cur[kt][r], scale_log2, -m_use));
+        if (r & 1) {  // a fixed spot in the instruction stream for the caller's loads
+          sched_fence();
+          hook(8 * kt + (r >> 1));
+          sched_fence();
+        }
+      }
     // row sum of the rounded probabilities (the weights the products use)
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -390,68 +394,68 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   };
   auto no_hook = [](int) {};
 
-  // Schedule. The two wavefronts of each SIMD (kh = 0 and kh = 1) run the
-  // three phases of a key block in rotated orders so that one's matrix work
-  // overlaps the other's exponentials, with two workgroup barriers per block:
-  //            phase 1       phase 2   | X |  phase 3        | Y |
-  //   kh = 0:  S_j           softmax_j |   |  PV_j           |   |
-  //   kh = 1:  softmax_j     PV_j      |   |  S_{j+1}        |   |
-  // K and V are double-buffered. V_{j+1} is requested in phases 1-2 and waited
-  // for at Y; K_{j+2} is requested in phase 3, into the buffer K_j has left,
-  // and waited for at X of the next block. Each wave spreads its requests over
-  // its matrix steps, so that no wave stalls long on a full memory queue.
-  // Every iteration issues the same requests (past the end of the list they
-  // repeat the last block into a buffer nobody reads again), so the waits are
-  // fixed counts: loads complete in issue order, and at X and at Y exactly the
-  // four tile loads issued after the awaited ones may still be in flight.
+  // Ping-pong schedule. Each SIMD runs one wave of each key half (kh = 0, 1).
+  // Iteration j has a matrix half (PV_j, then S_{j+1}) and an exponential half
+  // (the softmax of one block); the two waves run them in opposite orders, with
+  // a workgroup barrier between the halves, so that while one wave
+  // exponentiates, the other keeps the SIMD's matrix unit busy:
+  //   kh = 0:  softmax_j           | PV_j, S_{j+1}
+  //   kh = 1:  PV_j, S_{j+1}       | softmax_{j+1}
+  // Iteration j reads K_{j+1} and V_j, and requests K_{j+2} and V_{j+1} (into
+  // the buffers that K_j and V_{j-1} left in iteration j-1) and the facts of
+  // block j+2; all of them are waited for at its end. Only the kh = 0 waves
+  // issue these loads, spread over their exponentials: the global-to-LDS path
+  // drains about 64 bytes per clock per CU, a wave that issues into a full
+  // queue stalls, and the exponentiating wave has slack where the matrix wave
+  // has none.
   auto walk = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
-    if (KH == 1) {
-      qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi, no_hook);
-      mask_pad_keys(s_cur, meta_j, hi);
-    }
+    qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi, no_hook);
+    mask_pad_keys(s_cur, meta_j, hi);
+    bf16x8 pf8[4];
+    if (KH == 1) softmax(pf8, no_hook);
+    // ids of blocks j+1 and j+2 (carried in scalar registers; the next one is
+    // read from LDS an iteration ahead)
+    int b1 = __builtin_amdgcn_readfirstlane(sL[min(1, n - 1)]);
+    int b2 = __builtin_amdgcn_readfirstlane(sL[min(2, n - 1)]);
     for (int j = 0; j < n; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
-      const bool more1 = j + 1 < n;
-      const int b1 = __builtin_amdgcn_readfirstlane(sL[min(j + 1, n - 1)]);
-      const int b2 = __builtin_amdgcn_readfirstlane(sL[min(j + 2, n - 1)]);
-      auto vdma = [&](int m) { dma_part<true>(sV[nb], vrs, b1 * kTileBytes, w, lane, m); };
-      auto kdma = [&](int m) { dma_part<false>(sK[cb], krs, b2 * kTileBytes, w, lane, m); };
-      fetch_meta(b1, nb);
-      bf16x8 pf8[4];
-      if (KH == 0) {
-        qk_tiles(s_cur, sK[cb], koff, kswz_lane, qf, hi, [&](int st) {
-          if (st & 1) vdma(st >> 1);
-        });
-        mask_pad_keys(s_cur, meta_j, hi);
-        softmax(pf8);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) vdma(m);
-        softmax(pf8);
-        pv_tiles(o, sV[cb], voff, pf8, no_hook);
-      }
-      // X: K_{j+1} and the facts of block j+1 have landed (V_{j+1} may not)
-      __builtin_amdgcn_s_waitcnt(kWaitVm4);
-      barrier();
-      const HalfMeta meta_n = uniform(read_meta(nb));
-      if (KH == 0) {
-        pv_tiles(o, sV[cb], voff, pf8, kdma);
-      } else {
-        if (more1) {
-          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, [&](int st) {
-            if (st & 1) kdma(st >> 1);
-          });
-          mask_pad_keys(s_cur, meta_n, hi);
+      const bool more1 = j + 1 < n, more2 = j + 2 < n;
+      const int b3 = sL[min(j + 3, n - 1)];
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 mraw = *reinterpret_cast<const u32x3*>(&sM[nb][4 * kh]);
+      // wave w (kh = 0) fills parts (w, m) and (w + 4, m) of K_{j+2} and V_{j+1}
+      auto dma_hook = [&](int k) {
+        const int ww = w + 4 * (k & 1), m = (k >> 1) & 3;
+        if (k < 8) {
+          if (more2) dma_part<false>(sK[cb], krs, b2 * kTileBytes, ww, lane, m);
         } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) kdma(m);
+          if (more1) dma_part<true>(sV[nb], vrs, b1 * kTileBytes, ww, lane, m);
         }
+      };
+      if (KH == 0 && more2) fetch_meta(b2, cb);
+      const HalfMeta meta_n{mraw.x, mraw.y, (int)mraw.z};
+      if (KH == 0) {
+        softmax(pf8, dma_hook);
+        barrier();
+        pv_tiles(o, sV[cb], voff, pf8, no_hook);
+        if (more1) {
+          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, no_hook);
+          mask_pad_keys(s_cur, meta_n, hi);
+        }
+      } else {
+        pv_tiles(o, sV[cb], voff, pf8, no_hook);
+        if (more1) {
+          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, no_hook);
+          mask_pad_keys(s_cur, meta_n, hi);
+        }
+        barrier();
+        if (more1) softmax(pf8, no_hook);
       }
-      // Y: V_{j+1} has landed (K_{j+2} may not)
-      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      b1 = b2;
+      b2 = __builtin_amdgcn_readfirstlane(b3);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       barrier();
-      meta_j = meta_n;
     }
   };
   if (kh == 0)
