@@ -43,9 +43,31 @@ def parse():
     return ap.parse_args()
 
 
-def hbm_stages(wl, sizes, stage_ms):
+def device_copy_gbps():
+    """Read + write rate of a plain 1 GiB device-to-device copy (event-timed),
+    the practical ceiling of a stage that reads and writes every byte once."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def hbm_stages(wl, sizes, stage_ms, copy_gbps):
     """Algorithmic HBM bytes of the data-movement stages and the rate they reach
-    in the event-timed stage time, against the 8 TB/s HBM peak."""
+    in the event-timed stage time, against the 8 TB/s HBM peak and against the
+    measured rate of a plain device copy."""
     N, Np, H, d = sizes["n_tokens"], sizes["n_padded"], wl.heads, wl.d
     e = 2  # bf16
     alg = {
@@ -63,7 +85,9 @@ def hbm_stages(wl, sizes, stage_ms):
         ms = stage_ms[stage]
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[stage] = {"ms": round(ms, 4), "alg_GB": round(nbytes / 1e9, 4), "alg_GBps": round(gbs, 1),
-                      "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 3)}
+                      "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 3),
+                      "frac_of_copy": round(gbs / copy_gbps, 3)}
+    out["device_copy_GBps"] = round(copy_gbps, 1)
     return out
 
 
@@ -236,7 +260,7 @@ def main():
             "frac": round(fwd_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(wl.name),
         },
-        "hbm_stages": hbm_stages(wl, sizes, stage_ms),
+        "hbm_stages": hbm_stages(wl, sizes, stage_ms, device_copy_gbps()),
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
@@ -254,7 +278,7 @@ def cpu_baseline(wl, inp, counts_gpu):
     from oracle import pipeline as opipe
 
     threads = len(os.sched_getaffinity(0))
-    hs = 4  # heads of the sample (about 10 s of oracle work at 720p)
+    hs = 6  # heads of the sample (about 10 s of oracle work at 720p)
     q = synth.bf16_bits_to_f64(inp["q"][:hs])
     k = synth.bf16_bits_to_f64(inp["k"][:hs])
     v = synth.bf16_bits_to_f64(inp["v"][:hs])
@@ -264,7 +288,7 @@ def cpu_baseline(wl, inp, counts_gpu):
     L = r["layout"]
     rng = np.random.default_rng(0)
     nonempty = np.nonzero(r["counts"] > 0)[0]
-    per_head = min(400, len(nonempty))
+    per_head = min(420, len(nonempty))
     pairs = [(h, int(i)) for h in range(hs) for i in rng.choice(nonempty, per_head, replace=False)]
     t0 = time.perf_counter()
     oatt.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], 1 / np.sqrt(wl.d), pairs=pairs)

@@ -143,6 +143,35 @@ def test_small_pipeline_forced_shapes(wl):
             assert np.abs(a - b).max() <= F32_TOL, name
 
 
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[1], SMALL[2]], ids=lambda w: w.name)
+def test_pooled_logits(wl):
+    """The fp64 pooled logits (debug output of bsa_pool_select) against the
+    oracle's block means: l = qbar kbar^T / sqrt(d), -inf for empty key blocks.
+    Both sides are fp64 sums of the same exactly-upcast inputs in different
+    orders, so they agree to a few ulps of the largest term."""
+    inp = synth.make_inputs(wl, parts=("q", "k"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(7)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    lay = layout_of(wl)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k = (to_dev(inp[p], wl.dtype) for p in "qk")
+    qp, kp = ops.permute(lay, zs_dev, [q, k])
+    _, _, logits = ops.pool_select(lay, zs_dev, qp, kp, wl.sparsity_1e4, wl.tau, return_logits=True)
+    got = logits.cpu().numpy()
+    qf, kf = (host_f64(inp[p], wl.dtype) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, wl.sparsity_1e4, wl.tau,
+                            zone_shape=zs)
+    real = r["counts"] > 0
+    assert r["layout"].n_blocks % 64 != 0  # a ragged last tile
+    for h in range(wl.heads):
+        want = r["qbar"][h][real] @ r["kbar"][h][real].T / np.sqrt(wl.d)
+        g = got[h][np.ix_(real, real)]
+        tol = 1e-13 * np.abs(r["qbar"][h][real]).max() * np.abs(r["kbar"][h][real]).max() * wl.d
+        assert np.abs(g - want).max() <= tol
+        assert np.all(np.isneginf(got[h][np.ix_(real, ~real)]))
+
+
 def test_cdf_branch_lists():
     """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
     top-k (s = 0.93), so most lists have n = m > k."""

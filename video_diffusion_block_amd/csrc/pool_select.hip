@@ -72,8 +72,17 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Lay L, const BlockMeta* 
 }
 
 // --------------------------------------------------------- pooled logits --
-constexpr int kLT = 64;  // output tile
-constexpr int kLE = 16;  // reduction chunk
+// l[h,i,j] = qbar_i . kbar_j * scale on fp64 MFMA (v_mfma_f64_16x16x4_f64).
+// One workgroup of 4 wavefronts per 64 x 64 tile of (query block, key block);
+// wavefront w owns the 32 x 32 sub-tile (w / 2, w % 2) as 2 x 2 MFMA tiles.
+// The reduction over d runs in chunks of 16 staged in LDS ([k][row] layout,
+// padded rows) and in k-steps of 4 inside a chunk.
+// Operand layout of the 16x16x4 fp64 product: lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; accumulator element r of lane l is D[4 r + l / 16][l % 16]
+// (probed on gfx950).
+constexpr int kPT = 64;  // output tile
+constexpr int kPE = 16;  // reduction chunk
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
                                                                  const BlockMeta* __restrict__ meta,
@@ -81,49 +90,57 @@ __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
                                                                  const double* __restrict__ kbar,
                                                                  int d, double scale,
                                                                  double* __restrict__ logits) {
-  __shared__ double qs[kLE][kLT + 1];
-  __shared__ double ks[kLE][kLT + 1];
-  const int i0 = blockIdx.x * kLT, j0 = blockIdx.y * kLT, h = blockIdx.z;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  __shared__ double sq[kPE][kPT + 1];
+  __shared__ double sk[kPE][kPT + 1];
+  const int i0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT, h = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wi = 32 * (w >> 1), wj = 32 * (w & 1);
+  const int l16 = lane & 15, kq = lane >> 4;
   const double* qh = qbar + (size_t)h * L.M * d;
   const double* kh = kbar + (size_t)h * L.M * d;
-  double acc[4][4];
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int e0 = 0; e0 < d; e0 += kLE) {
-    for (int t = threadIdx.x; t < kLT * kLE; t += kThreads) {
-      const int r = t / kLE, e = t % kLE;
-      qs[e][r] = (i0 + r < L.M) ? qh[(size_t)(i0 + r) * d + e0 + e] : 0.0;
-      ks[e][r] = (j0 + r < L.M) ? kh[(size_t)(j0 + r) * d + e0 + e] : 0.0;
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int le = threadIdx.x & (kPE - 1), lr = threadIdx.x / kPE;  // loader: element, row
+  for (int e0 = 0; e0 < d; e0 += kPE) {
+#pragma unroll
+    for (int u = 0; u < kPT * kPE / kThreads; ++u) {
+      const int r = lr + (kThreads / kPE) * u;
+      sq[le][r] = (i0 + r < L.M) ? qh[(size_t)(i0 + r) * d + e0 + le] : 0.0;
+      sk[le][r] = (j0 + r < L.M) ? kh[(size_t)(j0 + r) * d + e0 + le] : 0.0;
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < kLE; ++e) {
-      double av[4], bv[4];
+    for (int ks = 0; ks < kPE / 4; ++ks) {
+      const int kk = 4 * ks + kq;
+      double av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = qs[e][ty + 16 * a];
+      for (int t = 0; t < 2; ++t) {
+        av[t] = sq[kk][wi + 16 * t + l16];
+        bv[t] = sk[kk][wj + 16 * t + l16];
+      }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = ks[e][tx + 16 * b];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int j = j0 + tx + 16 * b;
+  for (int b = 0; b < 2; ++b) {
+    const int j = j0 + wj + 16 * b + l16;
     if (j >= L.M) continue;
     const bool key_ok = meta[j].count() > 0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int i = i0 + ty + 16 * a;
-      if (i >= L.M) continue;
-      logits[((size_t)h * L.M + i) * L.M + j] = key_ok ? acc[a][b] * scale : -INFINITY;
-    }
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + wi + 16 * a + 4 * r + kq;
+        if (i < L.M) logits[((size_t)h * L.M + i) * L.M + j] = key_ok ? acc[a][b][r] * scale : -INFINITY;
+      }
   }
 }
 
@@ -449,7 +466,7 @@ hipError_t launch_pool(const Lay& L, const BlockMeta* meta, const void* qp, cons
 hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const double* qbar,
                                 const double* kbar, int heads, int d, double scale,
                                 double* logits, hipStream_t st) {
-  dim3 grid((L.M + kLT - 1) / kLT, (L.M + kLT - 1) / kLT, heads);
+  dim3 grid((L.M + kPT - 1) / kPT, (L.M + kPT - 1) / kPT, heads);
   pooled_logits_kernel<<<grid, kThreads, 0, st>>>(L, meta, qbar, kbar, d, scale, logits);
   return hipGetLastError();
 }
