@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     return ap.parse_args()
 
 
@@ -70,11 +72,13 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
     measured rate of a plain device copy."""
     N, Np, H, d = sizes["n_tokens"], sizes["n_padded"], wl.heads, wl.d
     e = 2  # bf16
-    alg = {
-        "permute": 3 * H * (N + Np) * d * e,           # Q, K, V: read real rows, write padded
-        "pool_select": 2 * H * N * d * e,              # pooling reads the real rows of Qp, Kp
-        "unpermute": 2 * H * N * d * e,                # O: read real slots, write raster rows
-    }
+    M = sizes["n_blocks"]
+    alg = {"unpermute": 2 * H * N * d * e}             # O: read real slots, write raster rows
+    if "permute" in stage_ms:
+        alg["permute"] = 3 * H * (N + Np) * d * e      # Q, K, V: read real rows, write padded
+        alg["pool_select"] = 2 * H * N * d * e         # pooling reads the real rows of Qp, Kp
+    else:                                              # + the fp64 block means of Q and K
+        alg["permute_pool"] = 3 * H * (N + Np) * d * e + 2 * H * M * d * 8
     if wl.mode == "dynamic":
         alg["zone_score"] = N * wl.video_channels * e + wl.n_audio * wl.video_channels * e
     if wl.backward:
@@ -166,7 +170,10 @@ def main():
            else ops.BSALayout.dynamic(wl.grid, wl.block))
     sizes = lay.sizes()
 
-    stages = ["zone_score", "permute", "pool_select", "attn_fwd", "unpermute"]
+    if args.unfused:  # separate permute and pool+select calls
+        stages = ["zone_score", "permute", "pool_select", "attn_fwd", "unpermute"]
+    else:             # pooling fused into the gather; selection from its block means
+        stages = ["zone_score", "permute_pool", "select", "attn_fwd", "unpermute"]
     if wl.backward:
         stages += ["permute_dO", "attn_bwd", "unpermute_grads"]
     ev = {s: [] for s in stages}
@@ -185,9 +192,14 @@ def main():
         mark()
         zs = ops.zone_score(lay, video, audio)
         mark()
-        qp, kp, vp = ops.permute(lay, zs, [q, k, v])
-        mark()
-        counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+        if args.unfused:
+            qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+            mark()
+            counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+        else:
+            (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
+            mark()
+            counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
         mark()
         op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
         mark()

@@ -70,7 +70,8 @@ typedef enum {
   BSA_CALL_ZONE_SCORE = 0,
   BSA_CALL_POOL_SELECT = 1,
   BSA_CALL_ATTN_FWD = 2,
-  BSA_CALL_ATTN_BWD = 3
+  BSA_CALL_ATTN_BWD = 3,
+  BSA_CALL_SELECT = 4
 } bsa_call;
 
 /* [host] Description of the token layout (plain data, read during a call only).
@@ -152,6 +153,18 @@ bsa_status bsa_permute(const bsa_layout* L, const int32_t* zone_shape, int ntens
                        const void* const* src, void* const* dst, int heads, int d, int dtype,
                        void* stream);
 
+/* bsa_permute that also pools [Prism §Blocks: block-level features]: while
+ * gathering, it sums the real rows of every block of the first npool tensors
+ * in fp64 and writes their means, the q̄ / k̄ that block selection scores
+ * (so that selection need not read Qp and Kp again).
+ *  npool   0..ntensors tensors to pool (0 = plain bsa_permute)
+ *  means   [host] array of npool device pointers, each [heads, n_blocks, d]
+ *          double out: mean of the block's real slots (0 for an empty block)
+ *  Other arguments as bsa_permute; pooling needs d in {64, 128}. */
+bsa_status bsa_permute_pool(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
+                            const void* const* src, void* const* dst, int heads, int d,
+                            int dtype, int npool, double* const* means, void* stream);
+
 /* Inverse of bsa_permute: src [heads, Np, d] -> dst [heads, N, d], reading
  * real slots only. Same arguments as bsa_permute. */
 bsa_status bsa_unpermute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
@@ -180,6 +193,16 @@ bsa_status bsa_pool_select(const bsa_layout* L, const int32_t* zone_shape, const
                            const void* kp, int heads, int d, int dtype, int32_t sparsity_1e4,
                            double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* The selection half of bsa_pool_select, from block means the caller already
+ * has (bsa_permute_pool writes them): same rule, arguments and outputs, with
+ *  qbar, kbar  [heads, n_blocks, d] double block means of Q and K (any value
+ *              for empty blocks: they are never scored)
+ *  ws          workspace of bsa_workspace_size(BSA_CALL_SELECT, ...) bytes */
+bsa_status bsa_select(const bsa_layout* L, const int32_t* zone_shape, const double* qbar,
+                      const double* kbar, int heads, int d, int32_t sparsity_1e4, double tau,
+                      int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* Block-sparse attention forward [Prism §Blocks: Prism Block Sparse Attention].
  * For every real query slot n of block i: O[n] = sum over real key slots m of

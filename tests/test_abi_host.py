@@ -162,6 +162,44 @@ def test_permute_validation(lib):
     assert lib.bsa_permute(ctypes.byref(d), None, 1, arr, arr, 2, 128, 1, None) == _lib.BSA_INVALID_ARG
 
 
+def test_permute_pool_validation(lib):
+    c = LAY.c()
+    arr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    means = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    half = (ctypes.c_void_p * 2)(FAKE, None)
+
+    def call(nt=3, npool=2, m=means, d=128, dt=1):
+        return lib.bsa_permute_pool(ctypes.byref(c), None, nt, arr, arr, 2, d, dt, npool, m, None)
+
+    assert call(npool=4) == _lib.BSA_INVALID_ARG         # more than ntensors
+    assert call(npool=-1) == _lib.BSA_INVALID_ARG
+    assert call(m=None) == _lib.BSA_INVALID_ARG
+    assert call(m=half) == _lib.BSA_INVALID_ARG
+    assert call(d=96) == _lib.BSA_UNSUPPORTED             # pooling needs d in {64, 128}
+    assert call(dt=5) == _lib.BSA_INVALID_ARG
+    assert "npool" in (call(npool=4) and lib.bsa_last_error().decode())
+
+
+def test_select_validation(lib):
+    c = LAY.c()
+
+    def call(qbar=FAKE, d=128, S=8500, tau=0.2, wsb=1 << 40, ws=FAKE, counts=FAKE, L=c, zs=FAKE):
+        return lib.bsa_select(ctypes.byref(L), zs, qbar, FAKE, 2, d, S, tau, counts, FAKE, None,
+                              ws, wsb, None)
+
+    assert call(qbar=None) == _lib.BSA_INVALID_ARG
+    assert call(counts=None) == _lib.BSA_INVALID_ARG
+    assert call(d=96) == _lib.BSA_UNSUPPORTED
+    assert call(S=10000) == _lib.BSA_INVALID_ARG
+    assert call(tau=0.0) == _lib.BSA_INVALID_ARG
+    assert call(wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert call(ws=None) == _lib.BSA_WORKSPACE_TOO_SMALL
+    dyn = DYN.c()
+    assert call(L=dyn, zs=None) == _lib.BSA_INVALID_ARG
+    need = lib.bsa_workspace_size(4, ctypes.byref(c), 2, 128)  # BSA_CALL_SELECT
+    assert 0 < need < lib.bsa_workspace_size(1, ctypes.byref(c), 2, 128)
+
+
 def test_zone_score_validation(lib):
     c = DYN.c()
 

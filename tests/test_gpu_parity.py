@@ -28,8 +28,10 @@ def layout_of(wl):
     return ops.BSALayout.dynamic(wl.grid, wl.block)
 
 
-def run_gpu(wl, inp, zone_shape=None, video=None, audio=None):
-    """The forward hot path through the C ABI; returns GPU tensors."""
+def run_gpu(wl, inp, zone_shape=None, video=None, audio=None, fused=False):
+    """The forward hot path through the C ABI; returns GPU tensors. fused: the
+    benchmark's launch sequence (bsa_permute_pool + bsa_select) instead of
+    bsa_permute + bsa_pool_select."""
     lay = layout_of(wl)
     q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
     if zone_shape is not None:
@@ -38,8 +40,12 @@ def run_gpu(wl, inp, zone_shape=None, video=None, audio=None):
         zs = ops.zone_score(lay, video, audio)
     else:
         zs = ops.zone_score(lay, None, None)
-    qp, kp, vp = ops.permute(lay, zs, [q, k, v])
-    counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+    if fused:
+        (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
+        counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
+    else:
+        qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+        counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
     op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
     (o,) = ops.unpermute(lay, zs, [op])
     torch.cuda.synchronize()
@@ -172,6 +178,36 @@ def test_pooled_logits(wl):
         assert np.all(np.isneginf(got[h][np.ix_(real, ~real)]))
 
 
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_permute_pool(wl):
+    """bsa_permute_pool gathers exactly what bsa_permute does and writes the
+    oracle's block means; bsa_select on them gives lists that meet the parity
+    rules."""
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(9)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    zs[-1] = len(L.shapes) - 1
+    lay = layout_of(wl)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    outs, means = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
+    for a, b in zip(outs, ops.permute(lay, zs_dev, [q, k, v])):
+        assert torch.equal(a, b)
+    qf, kf = (host_f64(inp[p], wl.dtype) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, wl.sparsity_1e4, wl.tau,
+                            zone_shape=zs)
+    real = r["counts"] > 0
+    for got, want in zip(means, (r["qbar"], r["kbar"])):
+        got = got.cpu().numpy()
+        assert np.abs(got[:, real] - want[:, real]).max() <= 1e-12 * np.abs(want[:, real]).max()
+        assert np.all(got[:, ~real] == 0.0)
+    counts, idx = ops.select(lay, zs_dev, means[0], means[1], wl.sparsity_1e4, wl.tau)
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, gpu_lists(counts, idx), r["lists"])
+    assert not fails, fails[:3]
+
+
 def test_cdf_branch_lists():
     """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
     top-k (s = 0.93), so most lists have n = m > k."""
@@ -268,7 +304,7 @@ def test_full_size_workload(name):
     video = to_dev(inp["video"], "bf16") if "video" in inp else None
     audio = to_dev(inp["audio"], "bf16") if "audio" in inp else None
     print(f"[{name}] gpu forward", flush=True)
-    g = run_gpu(wl, inp, video=video, audio=audio)
+    g = run_gpu(wl, inp, video=video, audio=audio, fused=True)
     L = oracle_layout(wl)
     zs_gpu = g["zs"].cpu().numpy()
     if wl.mode == "dynamic":

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
 BSA_OK, BSA_INVALID_ARG, BSA_UNSUPPORTED, BSA_WORKSPACE_TOO_SMALL, BSA_LAYOUT, BSA_HIP_ERROR = range(6)
 BSA_F32, BSA_BF16 = 0, 1
 BSA_MODE_FIXED, BSA_MODE_DYNAMIC = 0, 1
-BSA_CALL_ZONE_SCORE, BSA_CALL_POOL_SELECT, BSA_CALL_ATTN_FWD, BSA_CALL_ATTN_BWD = range(4)
+BSA_CALL_ZONE_SCORE, BSA_CALL_POOL_SELECT, BSA_CALL_ATTN_FWD, BSA_CALL_ATTN_BWD, BSA_CALL_SELECT = range(5)
 MAX_SHAPES = 4
 
 c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -46,6 +46,11 @@ SIGNATURES = {
     "bsa_permute": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    vp]),
+    "bsa_permute_pool": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
+    "bsa_select": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
+                                  ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]),
     "bsa_unpermute": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
                                      ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, vp]),

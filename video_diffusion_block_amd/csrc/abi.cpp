@@ -103,10 +103,13 @@ size_t esize(int dtype) { return dtype == BSA_BF16 ? 2 : 4; }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t pool_select_ws(const bsa::Lay& L, int heads, int d) {
-  return 2 * al256((size_t)heads * L.M * d * sizeof(double)) +
-         al256((size_t)heads * L.M * L.M * sizeof(double)) +
+size_t select_ws(const bsa::Lay& L, int heads) {
+  return al256((size_t)heads * L.M * L.M * sizeof(double)) +
          al256((size_t)L.M * sizeof(bsa::BlockMeta));
+}
+
+size_t pool_select_ws(const bsa::Lay& L, int heads, int d) {
+  return 2 * al256((size_t)heads * L.M * d * sizeof(double)) + select_ws(L, heads);
 }
 
 bsa_status hip_status(hipError_t e, const char* what) {
@@ -162,6 +165,7 @@ size_t bsa_workspace_size(bsa_call call, const bsa_layout* in, int heads, int d)
     case BSA_CALL_POOL_SELECT: return pool_select_ws(L, heads, d);
     case BSA_CALL_ATTN_FWD: return bsa::attn_fwd_workspace(L, d, true);
     case BSA_CALL_ATTN_BWD: return bsa::attn_bwd_workspace(L, heads, d);
+    case BSA_CALL_SELECT: return select_ws(L, heads);
   }
   fail(BSA_INVALID_ARG, "unknown call %d", (int)call);
   return 0;
@@ -195,7 +199,8 @@ bsa_status bsa_zone_score(const bsa_layout* in, const void* video, int C, const 
 
 static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
                                  const void* const* src, void* const* dst, int heads, int d,
-                                 int dtype, void* stream, bool inverse) {
+                                 int dtype, void* stream, bool inverse, int npool = 0,
+                                 double* const* means = nullptr) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
@@ -208,9 +213,24 @@ static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape
   if (row % 16 || d > 256) return fail(BSA_UNSUPPORTED, "row of %zu bytes (d = %d); need a multiple of 16 bytes and d <= 256", row, d);
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  if (npool < 0 || npool > ntensors) return fail(BSA_INVALID_ARG, "npool = %d out of [0, %d]", npool, ntensors);
+  if (npool > 0) {
+    if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "pooling needs d in {64, 128}, got %d", d);
+    if (!means) return fail(BSA_INVALID_ARG, "means pointer array is NULL");
+    for (int i = 0; i < npool; ++i)
+      if (!means[i]) return fail(BSA_INVALID_ARG, "means %d pointer is NULL", i);
+  }
   return hip_status(bsa::launch_permute(L, zone_shape, ntensors, src, dst, heads, (int)row,
-                                        inverse, static_cast<hipStream_t>(stream)),
+                                        inverse, static_cast<hipStream_t>(stream), npool, means,
+                                        dtype == BSA_BF16 ? 8 : 4),
                     inverse ? "unpermute" : "permute");
+}
+
+bsa_status bsa_permute_pool(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
+                            const void* const* src, void* const* dst, int heads, int d,
+                            int dtype, int npool, double* const* means, void* stream) {
+  return permute_common(in, zone_shape, ntensors, src, dst, heads, d, dtype, stream, false,
+                        npool, means);
 }
 
 bsa_status bsa_permute(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
@@ -225,21 +245,48 @@ bsa_status bsa_unpermute(const bsa_layout* in, const int32_t* zone_shape, int nt
   return permute_common(in, zone_shape, ntensors, src, dst, heads, d, dtype, stream, true);
 }
 
+static bsa_status check_select_args(const bsa_layout* in, const bsa::Lay& L,
+                                    const int32_t* zone_shape, int heads, int d,
+                                    int32_t sparsity_1e4, double tau, const void* counts,
+                                    const void* idx) {
+  (void)L;
+  BSA_TRY(check_heads(heads));
+  if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (!counts || !idx) return fail(BSA_INVALID_ARG, "counts/idx is NULL");
+  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
+    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
+  if (sparsity_1e4 < 0 || sparsity_1e4 > 9999)
+    return fail(BSA_INVALID_ARG, "sparsity_1e4 = %d out of [0, 9999]", sparsity_1e4);
+  if (!(tau > 0.0 && tau <= 1.0)) return fail(BSA_INVALID_ARG, "tau = %g out of (0, 1]", tau);
+  return ok();
+}
+
+// block facts, pooled logits and selection from block means (p: select_ws bytes)
+static hipError_t select_tail(const bsa::Lay& L, const int32_t* zone_shape, const double* qbar,
+                              const double* kbar, int heads, int d, int32_t sparsity_1e4,
+                              double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
+                              char* p, hipStream_t st, bool meta_ready) {
+  double* logits = pooled_logits ? pooled_logits : reinterpret_cast<double*>(p);
+  p += al256((size_t)heads * L.M * L.M * sizeof(double));
+  bsa::BlockMeta* meta = reinterpret_cast<bsa::BlockMeta*>(p);
+  hipError_t e = meta_ready ? hipSuccess : bsa::launch_block_meta(L, zone_shape, meta, st);
+  if (e == hipSuccess)
+    e = bsa::launch_pooled_logits(L, meta, qbar, kbar, heads, d, 1.0 / sqrt((double)d), logits,
+                                  st);
+  if (e == hipSuccess)
+    e = bsa::launch_select(L, meta, logits, heads, sparsity_1e4, tau, counts, idx, st);
+  return e;
+}
+
 bsa_status bsa_pool_select(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
                            const void* kp, int heads, int d, int dtype, int32_t sparsity_1e4,
                            double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
                            void* ws, size_t ws_bytes, void* stream) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
-  BSA_TRY(check_heads(heads));
   BSA_TRY(check_dtype_d(dtype, d));
-  if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
-  if (!qp || !kp || !counts || !idx) return fail(BSA_INVALID_ARG, "qp/kp/counts/idx is NULL");
-  if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
-    return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
-  if (sparsity_1e4 < 0 || sparsity_1e4 > 9999)
-    return fail(BSA_INVALID_ARG, "sparsity_1e4 = %d out of [0, 9999]", sparsity_1e4);
-  if (!(tau > 0.0 && tau <= 1.0)) return fail(BSA_INVALID_ARG, "tau = %g out of (0, 1]", tau);
+  BSA_TRY(check_select_args(in, L, zone_shape, heads, d, sparsity_1e4, tau, counts, idx));
+  if (!qp || !kp) return fail(BSA_INVALID_ARG, "qp/kp is NULL");
   const size_t need = pool_select_ws(L, heads, d);
   if (!ws || ws_bytes < need)
     return fail(BSA_WORKSPACE_TOO_SMALL, "pool_select needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -248,20 +295,33 @@ bsa_status bsa_pool_select(const bsa_layout* in, const int32_t* zone_shape, cons
   p += al256((size_t)heads * L.M * d * sizeof(double));
   double* kbar = reinterpret_cast<double*>(p);
   p += al256((size_t)heads * L.M * d * sizeof(double));
-  double* logits = pooled_logits ? pooled_logits : reinterpret_cast<double*>(p);
-  p += al256((size_t)heads * L.M * L.M * sizeof(double));
-  bsa::BlockMeta* meta = reinterpret_cast<bsa::BlockMeta*>(p);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf16 = dtype == BSA_BF16;
+  bsa::BlockMeta* meta = reinterpret_cast<bsa::BlockMeta*>(
+      p + al256((size_t)heads * L.M * L.M * sizeof(double)));
   hipError_t e = bsa::launch_block_meta(L, zone_shape, meta, st);
   if (e == hipSuccess)
-    e = bsa::launch_pool(L, meta, qp, kp, heads, d, bf16, qbar, kbar, st);
+    e = bsa::launch_pool(L, meta, qp, kp, heads, d, dtype == BSA_BF16, qbar, kbar, st);
   if (e == hipSuccess)
-    e = bsa::launch_pooled_logits(L, meta, qbar, kbar, heads, d, 1.0 / sqrt((double)d), logits,
-                                  st);
-  if (e == hipSuccess)
-    e = bsa::launch_select(L, meta, logits, heads, sparsity_1e4, tau, counts, idx, st);
+    e = select_tail(L, zone_shape, qbar, kbar, heads, d, sparsity_1e4, tau, counts, idx,
+                    pooled_logits, p, st, true);
   return hip_status(e, "pool_select");
+}
+
+bsa_status bsa_select(const bsa_layout* in, const int32_t* zone_shape, const double* qbar,
+                      const double* kbar, int heads, int d, int32_t sparsity_1e4, double tau,
+                      int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
+                      size_t ws_bytes, void* stream) {
+  bsa::Lay L;
+  BSA_TRY(make_lay(in, &L));
+  BSA_TRY(check_select_args(in, L, zone_shape, heads, d, sparsity_1e4, tau, counts, idx));
+  if (!qbar || !kbar) return fail(BSA_INVALID_ARG, "qbar/kbar is NULL");
+  const size_t need = select_ws(L, heads);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return hip_status(select_tail(L, zone_shape, qbar, kbar, heads, d, sparsity_1e4, tau, counts,
+                                idx, pooled_logits, static_cast<char*>(ws),
+                                static_cast<hipStream_t>(stream), false),
+                    "select");
 }
 
 bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,

@@ -10,9 +10,14 @@
 namespace bsa {
 
 // Gather [heads, N, d] -> [heads, Np, d] (inverse = false) or the reverse.
+// Gather (inverse = false) or scatter of up to four tensors. With npool > 0
+// (gather, d in {64, 128}, pool_epc = elements per 16 bytes: 8 bf16 / 4 fp32)
+// the block means of tensors 0 .. npool-1 over real slots are written to
+// pooled[t] [heads, M, d] fp64 (0 for empty blocks).
 hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
                           const void* const* src, void* const* dst, int heads, int row_bytes,
-                          bool inverse, hipStream_t st);
+                          bool inverse, hipStream_t st, int npool = 0,
+                          double* const* pooled = nullptr, int pool_epc = 0);
 
 
 

@@ -134,6 +134,46 @@ def permute(layout: BSALayout, zone_shape, tensors):
     return outs
 
 
+def permute_pool(layout: BSALayout, zone_shape, tensors, npool: int = 2):
+    """bsa_permute_pool: the gathered tensors (as permute) and the fp64 block
+    means [H, M, d] of the first npool of them, from one launch."""
+    lib = _lib.load()
+    _dev(zone_shape, *tensors)
+    sz = layout.sizes()
+    outs = [torch.empty((t.shape[0], sz["n_padded"], t.shape[2]), dtype=t.dtype, device=t.device)
+            for t in tensors]
+    means = [torch.empty((t.shape[0], sz["n_blocks"], t.shape[2]), dtype=torch.float64,
+                         device=t.device) for t in tensors[:npool]]
+    H, _, d = tensors[0].shape
+    n = len(tensors)
+    src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
+    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    mean_arr = (ctypes.c_void_p * max(npool, 1))(*[t.data_ptr() for t in means])
+    L = layout.c()
+    _lib.check("bsa_permute_pool", lib.bsa_permute_pool(
+        ctypes.byref(L), _ptr(zone_shape), n, src_arr, dst_arr, H, d, _dtype(tensors[0]), npool,
+        mean_arr, _stream()))
+    return outs, means
+
+
+def select(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, tau: float,
+           return_logits: bool = False):
+    """bsa_select: counts [H, M] int32, idx [H, M, M] int32 from fp64 block
+    means (and the fp64 pooled logits when asked)."""
+    lib = _lib.load()
+    _dev(zone_shape, qbar, kbar)
+    H, M, d = qbar.shape
+    counts = torch.empty((H, M), dtype=torch.int32, device=qbar.device)
+    idx = torch.empty((H, M, M), dtype=torch.int32, device=qbar.device)
+    logits = torch.empty((H, M, M), dtype=torch.float64, device=qbar.device) if return_logits else None
+    ws = _workspace(_lib.BSA_CALL_SELECT, layout, H, d, qbar.device)
+    L = layout.c()
+    _lib.check("bsa_select", lib.bsa_select(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qbar), _ptr(kbar), H, d, int(sparsity_1e4),
+        float(tau), _ptr(counts), _ptr(idx), _ptr(logits), _ptr(ws), ws.numel(), _stream()))
+    return (counts, idx, logits) if return_logits else (counts, idx)
+
+
 def unpermute(layout: BSALayout, zone_shape, tensors):
     """bsa_unpermute: list of [H, Np, d] -> list of [H, N, d] (one launch)."""
     _dev(zone_shape, *tensors)
