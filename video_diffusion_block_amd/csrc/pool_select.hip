@@ -104,14 +104,28 @@ __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   const int le = threadIdx.x & (kPE - 1), lr = threadIdx.x / kPE;  // loader: element, row
+  constexpr int kLd = kPT * kPE / kThreads;                         // loads per operand and lane
+  // the next chunk's operands are loaded into registers while this one is
+  // multiplied
+  double nq[kLd], nk[kLd];
+  auto gload = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int r = lr + (kThreads / kPE) * u;
+      nq[u] = (i0 + r < L.M) ? qh[(size_t)(i0 + r) * d + e0 + le] : 0.0;
+      nk[u] = (j0 + r < L.M) ? kh[(size_t)(j0 + r) * d + e0 + le] : 0.0;
+    }
+  };
+  gload(0);
   for (int e0 = 0; e0 < d; e0 += kPE) {
 #pragma unroll
-    for (int u = 0; u < kPT * kPE / kThreads; ++u) {
+    for (int u = 0; u < kLd; ++u) {
       const int r = lr + (kThreads / kPE) * u;
-      sq[le][r] = (i0 + r < L.M) ? qh[(size_t)(i0 + r) * d + e0 + le] : 0.0;
-      sk[le][r] = (j0 + r < L.M) ? kh[(size_t)(j0 + r) * d + e0 + le] : 0.0;
+      sq[le][r] = nq[u];
+      sk[le][r] = nk[u];
     }
     __syncthreads();
+    if (e0 + kPE < d) gload(e0 + kPE);
 #pragma unroll
     for (int ks = 0; ks < kPE / 4; ++ks) {
       const int kk = 4 * ks + kq;
