@@ -227,20 +227,22 @@ def test_cdf_branch_lists():
     assert (r["n"] > r["k"]).mean() > 0.5
 
 
-def test_max_blocks_lists():
-    """The largest layout the library takes (M = 4096 blocks): each selection
-    row spans 4096 logits, the widest register row, and the attention block
-    lists fill the whole LDS list buffer. Queries of the first 16 frames are
-    damped so that their pooled rows are near flat and take the CDF branch;
-    the rest are peaked and take the top-k branch."""
-    wl = synth.Workload("max-blocks", (32, 128, 128), 1, 128, "bf16", "fixed", (2, 8, 8), 8500,
-                        0.2)
+@pytest.mark.parametrize("grid,M", [((32, 128, 128), 4096), ((18, 128, 128), 2304),
+                                    ((24, 64, 128), 1536)])
+def test_max_blocks_lists(grid, M):
+    """Wide selection rows, up to the largest layout the library takes
+    (M = 4096 blocks: each row spans 4096 logits, the widest register row, and
+    the attention block lists fill the whole LDS list buffer); the other sizes
+    take the 3072- and 1536-wide row kernels. Queries of the first half of the
+    frames are damped so that their pooled rows are near flat and take the CDF
+    branch; the rest are peaked and take the top-k branch."""
+    wl = synth.Workload("wide-rows", grid, 1, 128, "bf16", "fixed", (2, 8, 8), 8500, 0.2)
     inp = synth.make_inputs(wl)
     qf = synth.bf16_bits_to_f64(inp["q"]).astype(np.float32)
     qf[:, : wl.n_tokens // 2] *= 0.02
     inp["q"] = synth.f32_to_bf16_bits(qf)
     g = run_gpu(wl, inp)
-    assert g["lay"].sizes()["n_blocks"] == 4096
+    assert g["lay"].sizes()["n_blocks"] == M
     q, k = (synth.bf16_bits_to_f64(inp[p]) for p in "qk")
     r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau)
     L = r["layout"]

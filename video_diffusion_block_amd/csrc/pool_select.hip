@@ -205,7 +205,7 @@ __device__ inline T wave_exclusive_scan(T v, int lane) {
 
 // One wavefront per (head, query block) row, WAVES rows per workgroup; lane l
 // holds the row's logits of key blocks P2/64 l .. P2/64 (l + 1) - 1 in
-// registers. No sort: the cut of the order (logit descending, id ascending) is
+// registers (P2: a multiple of 64 at least the block count). No sort: the cut of the order (logit descending, id ascending) is
 // found by MSB-first radix selection on an order-preserving 64-bit key (eight
 // 8-bit digits, LDS histograms, wave scans), first for rank k; when the top-k
 // set already holds probability mass >= tau it is the list, otherwise a second
@@ -491,10 +491,16 @@ hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logi
 #define BSA_SELECT(P, W)                                                                   \
   select_kernel<P, W><<<dim3((L.M + (W) - 1) / (W), heads), 64 * (W), 0, st>>>(            \
       L, meta, logits, sparsity_1e4, tau, counts, idx)
+  // row widths: multiples of 64 (one register slot per lane each), chosen
+  // to cover the common block counts with few empty slots
   if (L.M <= 256) BSA_SELECT(256, 4);
   else if (L.M <= 512) BSA_SELECT(512, 4);
   else if (L.M <= 1024) BSA_SELECT(1024, 4);
+  else if (L.M <= 1280) BSA_SELECT(1280, 4);
+  else if (L.M <= 1536) BSA_SELECT(1536, 4);
+  else if (L.M <= 1920) BSA_SELECT(1920, 4);
   else if (L.M <= 2048) BSA_SELECT(2048, 4);
+  else if (L.M <= 3072) BSA_SELECT(3072, 2);
   else BSA_SELECT(4096, 2);
 #undef BSA_SELECT
   return hipGetLastError();
