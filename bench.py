@@ -137,7 +137,7 @@ def copy_calib():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; the path shards by head "
+        print("bench.py: measures one GPU only; the path shards by head "
               "across GPUs but no multi-GPU run is provided (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import numpy as np

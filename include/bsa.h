@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   BSA_OK = 0,
   BSA_INVALID_ARG = 1,         /* null pointer, non-positive size, value out of range */
-  BSA_UNSUPPORTED = 2,         /* dtype / head dim / block size this build has no kernel for */
+  BSA_UNSUPPORTED = 2,         /* dtype / head dim / block size the library has no kernel for */
   BSA_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < bsa_workspace_size(...) */
   BSA_LAYOUT = 4,              /* a shape does not tile the zone, too many blocks, ... */
   BSA_HIP_ERROR = 5            /* a kernel launch failed */

@@ -5,7 +5,9 @@
 // zone's shape. One workgroup moves one (block, head, tensor) tile: B rows of
 // d elements, 16 bytes per lane per step. Source rows of a block come in runs
 // of bw consecutive raster tokens (bw*d*esize contiguous bytes), so every
-// wavefront load touches whole 256-byte-or-longer segments.
+// wavefront load touches whole 256-byte-or-longer segments. The gather can
+// also sum the block's real rows into its mean (the block-level features that
+// selection scores), so that pooling needs no second pass over Q and K.
 #include "kernels.hpp"
 
 namespace bsa {

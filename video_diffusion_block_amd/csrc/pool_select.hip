@@ -11,8 +11,8 @@
 //
 // All of it runs in fp64: pooled logits of neighbouring blocks can differ by
 // less than fp32 resolution, and the list must match an fp64 evaluation of the
-// rule except at near-ties. Cost is small next to attention (C5-size: 4 heads
-// x 1920^2 x 128 fp64 FMAs).
+// rule except at near-ties. Cost is small next to attention (2K workload: 4 heads
+// x 1920^2 x 128 fp64 FMAs, on the fp64 matrix cores).
 #include <float.h>
 #include <math.h>
 
