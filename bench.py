@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--norm-rope", action="store_true",
+                    help="fuse RMSNorm + 3-D RoPE of Q and K into the gather (bsa_permute_norm_rope)")
     ap.add_argument("--unfused", action="store_true",
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     return ap.parse_args()
@@ -78,7 +80,8 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
         alg["permute"] = 3 * H * (N + Np) * d * e      # Q, K, V: read real rows, write padded
         alg["pool_select"] = 2 * H * N * d * e         # pooling reads the real rows of Qp, Kp
     else:                                              # + the fp64 block means of Q and K
-        alg["permute_pool"] = 3 * H * (N + Np) * d * e + 2 * H * M * d * 8
+        name = "permute_norm_rope" if "permute_norm_rope" in stage_ms else "permute_pool"
+        alg[name] = 3 * H * (N + Np) * d * e + 2 * H * M * d * 8
     if wl.mode == "dynamic":
         alg["zone_score"] = N * wl.video_channels * e + wl.n_audio * wl.video_channels * e
     if wl.backward:
@@ -169,9 +172,15 @@ def main():
     lay = (ops.BSALayout.fixed(wl.grid, wl.block) if wl.mode == "fixed"
            else ops.BSALayout.dynamic(wl.grid, wl.block))
     sizes = lay.sizes()
+    # synthetic RMSNorm channel weights of Q and K (seeded; no trained weights)
+    grng = np.random.default_rng(7)
+    gammas = [torch.from_numpy(grng.uniform(0.5, 1.5, wl.d).astype(np.float32)).to(dev)
+              for _ in range(2)]
 
     if args.unfused:  # separate permute and pool+select calls
         stages = ["zone_score", "permute", "pool_select", "attn_fwd", "unpermute"]
+    elif args.norm_rope:  # Q, K normalized and rotated in the gather, then pooled
+        stages = ["zone_score", "permute_norm_rope", "select", "attn_fwd", "unpermute"]
     else:             # pooling fused into the gather; selection from its block means
         stages = ["zone_score", "permute_pool", "select", "attn_fwd", "unpermute"]
     if wl.backward:
@@ -196,6 +205,10 @@ def main():
             qp, kp, vp = ops.permute(lay, zs, [q, k, v])
             mark()
             counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+        elif args.norm_rope:
+            (qp, kp, vp), (qbar, kbar) = ops.permute_norm_rope(lay, zs, [q, k, v], gammas)
+            mark()
+            counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
         else:
             (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
             mark()
@@ -261,6 +274,8 @@ def main():
         "config": {"workload": wl.name, "grid": list(wl.grid), "tokens": N, "heads": H, "d": d,
                    "blocks": sizes["n_blocks"], "sparsity": wl.sparsity_1e4 / 1e4, "tau": wl.tau,
                    "mode": wl.mode, "backward": wl.backward,
+                   "sequence": ("unfused" if args.unfused else
+                                "norm_rope+pool" if args.norm_rope else "pool"),
                    "mean_list": round(pairs / max(1, int((counts > 0).sum())), 2)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {

@@ -165,6 +165,30 @@ bsa_status bsa_permute_pool(const bsa_layout* L, const int32_t* zone_shape, int 
                             const void* const* src, void* const* dst, int heads, int d,
                             int dtype, int npool, double* const* means, void* stream);
 
+/* bsa_permute_pool with the pre-attention transform of Q and K fused into the
+ * gather [Helios page (suanlab.com, Helios review), core contributions: fused
+ * normalization and RoPE kernels; Kaleido page (gist.science, paper
+ * 2607.13770), methodology: the rotary embedding splits a head's channels into
+ * a time group and two spatial groups, each at its own frequencies].
+ * Reading implemented (the pages give no formula), on each token's head
+ * vector of the first nrope tensors, in fp32, rounded once to the dtype:
+ *   y = x / sqrt(mean_c x_c^2 + eps) * gamma   (RMSNorm over the d channels);
+ *   channel groups t, h, w of d - 4 floor(d/6), 2 floor(d/6), 2 floor(d/6)
+ *   channels; the pair (2i, 2i+1) of a group of g channels turns by
+ *   pos * rope_base^(-2i/g), pos = the token's t, h or w:
+ *   (y0, y1) -> (y0 cos a - y1 sin a, y0 sin a + y1 cos a).
+ *  nrope      0..ntensors tensors to transform (Q and K: 2)
+ *  gamma      [host] array of nrope device pointers to [d] float weights, or
+ *             NULL (all weights 1); a NULL entry means weights 1 for that tensor
+ *  eps        > 0;  rope_base > 1 (10000 is usual)
+ *  npool/means as in bsa_permute_pool; the means are those of the stored
+ *             (transformed, rounded) rows.
+ *  Other arguments as bsa_permute; the transform needs d in {64, 128}. */
+bsa_status bsa_permute_norm_rope(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
+                                 const void* const* src, void* const* dst, int heads, int d,
+                                 int dtype, int nrope, const float* const* gamma, float eps,
+                                 float rope_base, int npool, double* const* means, void* stream);
+
 /* Inverse of bsa_permute: src [heads, Np, d] -> dst [heads, N, d], reading
  * real slots only. Same arguments as bsa_permute. */
 bsa_status bsa_unpermute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,

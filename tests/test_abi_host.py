@@ -180,6 +180,26 @@ def test_permute_pool_validation(lib):
     assert "npool" in (call(npool=4) and lib.bsa_last_error().decode())
 
 
+def test_permute_norm_rope_validation(lib):
+    c = LAY.c()
+    arr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    means = (ctypes.c_void_p * 2)(FAKE, FAKE)
+
+    def call(nrope=2, gamma=None, eps=1e-6, base=10000.0, d=128, npool=2):
+        return lib.bsa_permute_norm_rope(ctypes.byref(c), None, 3, arr, arr, 2, d, 1, nrope,
+                                         gamma, eps, base, npool, means, None)
+
+    assert call(nrope=4) == _lib.BSA_INVALID_ARG
+    assert call(nrope=-1) == _lib.BSA_INVALID_ARG
+    assert call(d=96, npool=0) == _lib.BSA_UNSUPPORTED
+    assert call(eps=0.0) == _lib.BSA_INVALID_ARG
+    assert call(eps=float("inf")) == _lib.BSA_INVALID_ARG
+    assert call(eps=float("nan")) == _lib.BSA_INVALID_ARG
+    assert call(base=1.0) == _lib.BSA_INVALID_ARG
+    assert call(base=float("inf")) == _lib.BSA_INVALID_ARG
+    assert "rope_base" in lib.bsa_last_error().decode()
+
+
 def test_select_validation(lib):
     c = LAY.c()
 

@@ -12,6 +12,7 @@ import torch
 import synth
 from oracle import attention as oatt
 from oracle import layout as olay
+from oracle import prenorm as opn
 from oracle import pipeline as opipe
 from oracle import select as osel
 from oracle import zones as ozon
@@ -206,6 +207,82 @@ def test_permute_pool(wl):
     exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
                                          wl.tau, gpu_lists(counts, idx), r["lists"])
     assert not fails, fails[:3]
+
+
+NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),
+                                   8500, 0.2)]
+
+
+@pytest.mark.parametrize("wl", NR_CASES, ids=lambda w: w.name)
+def test_permute_norm_rope(wl):
+    """bsa_permute_norm_rope: Q and K RMS-normalized and rotated against the
+    fp64 oracle (within the output dtype's rounding plus fp32 arithmetic), V
+    moved bitwise as bsa_permute does, pad slots zero, and block means equal to
+    the fp64 means of the rows the call stored. 'wide-w' puts tokens at w up
+    to 159 (rotation angles up to ~159 rad)."""
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(12)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    lay = layout_of(wl)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    gam = [rng.uniform(0.5, 1.5, wl.d).astype(np.float32) for _ in range(2)]
+    eps, base = 1e-6, 10000.0
+    outs, means = ops.permute_norm_rope(lay, zs_dev, [q, k, v],
+                                        [torch.from_numpy(g).cuda() for g in gam], eps, base)
+    perm = olay.permutation(L, zs)
+    pad = perm < 0
+    for t, name in enumerate("qk"):
+        x = host_f64(inp[name], wl.dtype)
+        ref = olay.permute(opn.norm_rope(x, gam[t].astype(np.float64), wl.grid, eps, base), perm)
+        got = to_f64(outs[t])
+        err = np.abs(got - ref)
+        # rounding of the output (bf16: half an ulp, 2^-9 relative) plus the
+        # fp32 angle: pos * rate carries ~2^-23 relative (about 2e-5 rad at the
+        # largest positions here), which moves each output by up to that times
+        # the norm of its channel pair (rotations keep pair norms)
+        pn2 = np.sqrt(ref[..., 0::2] ** 2 + ref[..., 1::2] ** 2)
+        pair = np.repeat(pn2, 2, axis=-1)
+        if wl.dtype == "bf16":
+            bound = 2.0 ** -8 * np.abs(ref) + 2e-5 * pair + 1e-6
+        else:
+            bound = 1e-5 * (np.abs(ref) + pair) + 1e-6
+        assert np.all(err <= bound), (name, err.max(), np.unravel_index(np.argmax(err - bound), err.shape))
+        assert np.all(got[:, pad] == 0.0)
+        # means of the stored rows
+        mb = osel.pool(L, got, perm)
+        real = olay.block_counts(L, perm) > 0
+        gm = means[t].cpu().numpy()
+        assert np.abs(gm[:, real] - mb[:, real]).max() <= 1e-12 * max(1.0, np.abs(mb[:, real]).max())
+    (vp,) = ops.permute(lay, zs_dev, [v])
+    assert torch.equal(outs[2], vp)
+
+
+def test_norm_rope_full_size():
+    """bsa_permute_norm_rope at the 720p size the benchmark's --norm-rope run
+    times (40 heads): heads 0 and 39 of Q and K against the oracle, V bitwise."""
+    wl = synth.WORKLOADS["720p"]
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    lay = layout_of(wl)
+    zs = torch.zeros(L.n_zones, dtype=torch.int32).cuda()
+    rng = np.random.default_rng(13)
+    gam = [rng.uniform(0.5, 1.5, wl.d).astype(np.float32) for _ in range(2)]
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    outs, means = ops.permute_norm_rope(lay, zs, [q, k, v], [torch.from_numpy(g).cuda() for g in gam])
+    perm = olay.permutation(L, np.zeros(L.n_zones, np.int32))
+    for t, name in enumerate("qk"):
+        for h in (0, wl.heads - 1):
+            x = synth.bf16_bits_to_f64(inp[name][h:h + 1])
+            ref = olay.permute(opn.norm_rope(x, gam[t].astype(np.float64), wl.grid), perm)
+            got = to_f64(outs[t][h:h + 1])
+            pair = np.repeat(np.sqrt(ref[..., 0::2] ** 2 + ref[..., 1::2] ** 2), 2, axis=-1)
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-5 * pair + 1e-6), (name, h)
+            mb = osel.pool(L, got, perm)
+            assert np.abs(means[t][h:h + 1].cpu().numpy() - mb).max() <= 1e-12 * np.abs(mb).max()
+    (vp,) = ops.permute(lay, zs, [v])
+    assert torch.equal(outs[2], vp)
 
 
 def test_cdf_branch_lists():

@@ -49,6 +49,11 @@ SIGNATURES = {
     "bsa_permute_pool": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
+    "bsa_permute_norm_rope": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
+                                             ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                             ctypes.POINTER(vp), vp]),
     "bsa_select": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                                   ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]),
     "bsa_unpermute": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),

@@ -200,7 +200,9 @@ bsa_status bsa_zone_score(const bsa_layout* in, const void* video, int C, const 
 static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
                                  const void* const* src, void* const* dst, int heads, int d,
                                  int dtype, void* stream, bool inverse, int npool = 0,
-                                 double* const* means = nullptr) {
+                                 double* const* means = nullptr, int nrope = 0,
+                                 const float* const* gamma = nullptr, float eps = 0.f,
+                                 float rope_base = 0.f) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
@@ -214,6 +216,13 @@ static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
   if (npool < 0 || npool > ntensors) return fail(BSA_INVALID_ARG, "npool = %d out of [0, %d]", npool, ntensors);
+  if (nrope < 0 || nrope > ntensors) return fail(BSA_INVALID_ARG, "nrope = %d out of [0, %d]", nrope, ntensors);
+  if (nrope > 0) {
+    if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "norm + RoPE needs d in {64, 128}, got %d", d);
+    if (!(eps > 0.f) || isinf(eps)) return fail(BSA_INVALID_ARG, "eps = %g must be finite and > 0", (double)eps);
+    if (!(rope_base > 1.f) || isinf(rope_base))
+      return fail(BSA_INVALID_ARG, "rope_base = %g must be finite and > 1", (double)rope_base);
+  }
   if (npool > 0) {
     if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "pooling needs d in {64, 128}, got %d", d);
     if (!means) return fail(BSA_INVALID_ARG, "means pointer array is NULL");
@@ -222,8 +231,16 @@ static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape
   }
   return hip_status(bsa::launch_permute(L, zone_shape, ntensors, src, dst, heads, (int)row,
                                         inverse, static_cast<hipStream_t>(stream), npool, means,
-                                        dtype == BSA_BF16 ? 8 : 4),
+                                        dtype == BSA_BF16 ? 8 : 4, nrope, gamma, eps, rope_base),
                     inverse ? "unpermute" : "permute");
+}
+
+bsa_status bsa_permute_norm_rope(const bsa_layout* in, const int32_t* zone_shape, int ntensors,
+                                 const void* const* src, void* const* dst, int heads, int d,
+                                 int dtype, int nrope, const float* const* gamma, float eps,
+                                 float rope_base, int npool, double* const* means, void* stream) {
+  return permute_common(in, zone_shape, ntensors, src, dst, heads, d, dtype, stream, false,
+                        npool, means, nrope, gamma, eps, rope_base);
 }
 
 bsa_status bsa_permute_pool(const bsa_layout* in, const int32_t* zone_shape, int ntensors,

@@ -10,14 +10,18 @@
 namespace bsa {
 
 // Gather [heads, N, d] -> [heads, Np, d] (inverse = false) or the reverse.
-// Gather (inverse = false) or scatter of up to four tensors. With npool > 0
-// (gather, d in {64, 128}, pool_epc = elements per 16 bytes: 8 bf16 / 4 fp32)
-// the block means of tensors 0 .. npool-1 over real slots are written to
+// Gather (inverse = false) or scatter of up to four tensors. Gather options
+// (d in {64, 128}; epc = elements per 16 bytes: 8 bf16 / 4 fp32): tensors
+// 0 .. nrope-1 get RMSNorm (weights gamma[t] [d] fp32 or null, eps) and the
+// 3-D rotary embedding (base rope_base) before they are stored; the block
+// means of tensors 0 .. npool-1 over real slots, of the stored values, go to
 // pooled[t] [heads, M, d] fp64 (0 for empty blocks).
 hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
                           const void* const* src, void* const* dst, int heads, int row_bytes,
                           bool inverse, hipStream_t st, int npool = 0,
-                          double* const* pooled = nullptr, int pool_epc = 0);
+                          double* const* pooled = nullptr, int epc = 0, int nrope = 0,
+                          const float* const* gamma = nullptr, float eps = 0.f,
+                          float rope_base = 0.f);
 
 
 

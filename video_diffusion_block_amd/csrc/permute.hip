@@ -24,17 +24,50 @@ struct PoolPack {
   int n;
 };
 
+// Pre-attention transform of the first n gathered tensors (Q and K): RMSNorm
+// over the head channels with a per-channel weight, then the 3-D rotary
+// embedding. Helios page (suanlab.com, Helios review), core contributions:
+// fused normalization and RoPE kernels; Kaleido page (gist.science, paper
+// 2607.13770), methodology: the rotary embedding splits a head's channels
+// into a time group and two spatial groups with their own frequencies.
+// Reading implemented: groups t, h, w of d - 4 floor(d/6), 2 floor(d/6) and
+// 2 floor(d/6) channels; pair (2i, 2i+1) of a group of g channels turns by
+// pos * base^(-2i/g), pos the token's coordinate on the group's axis.
+struct NormRope {
+  const float* gamma[4];  // per tensor: [d] channel weights, or null (all 1)
+  float eps;
+  float log2_base;
+  int n;
+};
+
+// The raster token of slot r of box x (-1 for a pad slot) and the slot's
+// coordinates (t, h, w) on the padded grid.
+__device__ inline long long slot_token_at(const Lay& L, const Box& x, int r, int& tt, int& hh,
+                                          int& ww) {
+  const int rw = r % x.bw;
+  const int rh = (r / x.bw) % x.bh;
+  const int rt = r / (x.bw * x.bh);
+  tt = x.t0 + rt;
+  hh = x.h0 + rh;
+  ww = x.w0 + rw;
+  if (rt >= x.vt || rh >= x.vh || rw >= x.vw) return -1;
+  return ((long long)tt * L.H + hh) * L.W + ww;
+}
+
 constexpr int kPermThreads = 256;
 
-// kEpc > 0 (gather only): the workgroup also sums the real rows of its block
-// (kEpc elements per 16-byte chunk: 8 for bf16, 4 for fp32) in fp64 and writes
-// the block mean, for tensors t < pool.n. Each lane keeps one chunk column
-// (256 is a multiple of the chunk count), so its partial sums need one LDS
-// reduction over the lanes of that column.
-template <bool kInverse, int kEpc>
+// kEpc (gather only; elements per 16-byte chunk: 8 for bf16, 4 for fp32, 0 for
+// a plain copy) enables the two optional stages of the gather: the
+// pre-attention transform (kNR, tensors t < nr.n) and pooling (tensors
+// t < pool.n): the workgroup sums the real rows of its block in fp64, from the
+// values it stores, and writes the block mean. A lane keeps one chunk column
+// (256 is a multiple of the chunk count), so the chunks of a row sit in
+// adjacent lanes (the row's sum of squares is a shuffle reduction) and a
+// lane's partial block sums need one LDS reduction over its column.
+template <bool kInverse, int kEpc, bool kNR>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int32_t* zone_shape,
                                                                PtrPack P, int chunks,
-                                                               PoolPack pool) {
+                                                               PoolPack pool, NormRope nr) {
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int t = blockIdx.z;
@@ -48,14 +81,82 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
   double acc[kAcc];
 #pragma unroll
   for (int e = 0; e < kAcc; ++e) acc[e] = 0.0;
-  const bool pooled = kEpc > 0 && t < pool.n;  // uniform over the workgroup
+  const bool pooled = kEpc > 0 && t < pool.n;   // uniform over the workgroup
+  const bool transformed = kNR && t < nr.n;     // uniform over the workgroup
+
+  // this lane's chunk column: channel weights and, per channel pair, the
+  // rotation axis and rate (revolutions per unit of position)
+  const int d = chunks * kAcc;
+  const int lc = threadIdx.x & (chunks - 1);
+  float gam[kAcc];
+  float rate[kAcc / 2 > 0 ? kAcc / 2 : 1];
+  int axis[kAcc / 2 > 0 ? kAcc / 2 : 1];
+  if (kNR && transformed) {
+    const float* g = nr.gamma[t];
+#pragma unroll
+    for (int k = 0; k < kAcc; ++k) gam[k] = g ? g[lc * kAcc + k] : 1.f;
+    const int dh = 2 * (d / 6), dt = d - 2 * dh;
+#pragma unroll
+    for (int p = 0; p < kAcc / 2; ++p) {
+      const int ch = lc * kAcc + 2 * p;
+      int i, gsz;
+      if (ch < dt) {
+        axis[p] = 0, i = ch / 2, gsz = dt;
+      } else if (ch < dt + dh) {
+        axis[p] = 1, i = (ch - dt) / 2, gsz = dh;
+      } else {
+        axis[p] = 2, i = (ch - dt - dh) / 2, gsz = dh;
+      }
+      rate[p] = exp2f(-(2.f * i / gsz) * nr.log2_base) * 0.15915494309189535f;  // / 2 pi
+    }
+  }
+
   for (int e = threadIdx.x; e < total; e += kPermThreads) {
     const int r = e / chunks;
     const int c = e - r * chunks;
-    const long long n = slot_token(L, x, r);
+    int tt = 0, hh = 0, ww = 0;
+    const long long n = kNR ? slot_token_at(L, x, r, tt, hh, ww) : slot_token(L, x, r);
     if (!kInverse) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (n >= 0) v = src[raster0 + n * chunks + c];
+      if (kNR && transformed) {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        float f[kAcc];
+#pragma unroll
+        for (int k = 0; k < kAcc; ++k)
+          f[k] = kEpc == 8 ? __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16))
+                           : __uint_as_float(wv[k]);
+        // RMSNorm: the row's chunks are the `chunks` adjacent lanes
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < kAcc; ++k) ss = fmaf(f[k], f[k], ss);
+        for (int o = chunks >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        const float inv = rsqrtf(ss / (float)d + nr.eps);
+#pragma unroll
+        for (int k = 0; k < kAcc; ++k) f[k] *= inv * gam[k];
+        // rotary embedding (pad rows are zero and stay zero)
+#pragma unroll
+        for (int p = 0; p < kAcc / 2; ++p) {
+          const int pos = axis[p] == 0 ? tt : axis[p] == 1 ? hh : ww;
+          float rev = (float)pos * rate[p];
+          rev -= floorf(rev);
+          const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+          const float a0 = f[2 * p], a1 = f[2 * p + 1];
+          f[2 * p] = a0 * cs - a1 * sn;
+          f[2 * p + 1] = a0 * sn + a1 * cs;
+        }
+        uint32_t ov[4];
+        if (kEpc == 8) {
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            ov[k] = __builtin_bit_cast(uint32_t, bf16x2v{(__bf16)f[2 * k], (__bf16)f[2 * k + 1]});
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ov[k] = __float_as_uint(f[k]);
+        }
+        v = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+      }
       dst[padded0 + e] = v;
       if (kEpc > 0 && pooled && n >= 0) {
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -78,7 +179,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
 #pragma unroll
     for (int k = 0; k < kAcc; ++k) red[threadIdx.x * kAcc + k] = acc[k];
     __syncthreads();
-    const int d = chunks * kEpc;
     const int groups = kPermThreads / chunks;
     for (int el = threadIdx.x; el < d; el += kPermThreads) {
       const int c = el / kAcc, k = el - c * kAcc;
@@ -119,7 +219,8 @@ hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta*
 hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
                           const void* const* src, void* const* dst, int heads, int row_bytes,
                           bool inverse, hipStream_t st, int npool, double* const* pooled,
-                          int pool_epc) {
+                          int epc, int nrope, const float* const* gamma, float eps,
+                          float rope_base) {
   PtrPack P{};
   for (int i = 0; i < ntensors; ++i) {
     P.src[i] = static_cast<const uint4*>(src[i]);
@@ -128,18 +229,30 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
   PoolPack Q{};
   Q.n = npool;
   for (int i = 0; i < npool; ++i) Q.out[i] = pooled[i];
+  NormRope R{};
+  R.n = nrope;
+  R.eps = eps;
+  R.log2_base = nrope > 0 ? log2f(rope_base) : 0.f;
+  for (int i = 0; i < nrope; ++i) R.gamma[i] = gamma ? gamma[i] : nullptr;
   const int chunks = row_bytes / 16;
   dim3 grid(L.M, heads, ntensors);
+#define BSA_PERMUTE(INV, EPC, NR) \
+  permute_kernel<INV, EPC, NR><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q, R)
   if (inverse)
-    permute_kernel<true, 0><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q);
-  else if (npool == 0)
-    permute_kernel<false, 0><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q);
-  else if (pool_epc == 8)
-    permute_kernel<false, 8><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q);
-  else if (pool_epc == 4)
-    permute_kernel<false, 4><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q);
+    BSA_PERMUTE(true, 0, false);
+  else if (npool == 0 && nrope == 0)
+    BSA_PERMUTE(false, 0, false);
+  else if (nrope == 0 && epc == 8)
+    BSA_PERMUTE(false, 8, false);
+  else if (nrope == 0 && epc == 4)
+    BSA_PERMUTE(false, 4, false);
+  else if (epc == 8)
+    BSA_PERMUTE(false, 8, true);
+  else if (epc == 4)
+    BSA_PERMUTE(false, 4, true);
   else
     return hipErrorInvalidValue;
+#undef BSA_PERMUTE
   return hipGetLastError();
 }
 

@@ -156,6 +156,39 @@ def permute_pool(layout: BSALayout, zone_shape, tensors, npool: int = 2):
     return outs, means
 
 
+def permute_norm_rope(layout: BSALayout, zone_shape, tensors, gammas=None, eps: float = 1e-6,
+                      rope_base: float = 10000.0, nrope: int = 2, npool: int = 2):
+    """bsa_permute_norm_rope: the gathered tensors, the first nrope of them
+    RMS-normalized (channel weights gammas[t], float32 [d] tensors or None) and
+    rotated by the 3-D RoPE, plus the fp64 block means [H, M, d] of the first
+    npool stored tensors, from one launch."""
+    lib = _lib.load()
+    _dev(zone_shape, *tensors)
+    gammas = list(gammas) if gammas is not None else [None] * nrope
+    for g in gammas:
+        if g is not None:
+            _dev(g)
+            if g.dtype != torch.float32 or g.numel() != tensors[0].shape[2]:
+                raise ValueError("gamma must be a float32 tensor of d elements")
+    sz = layout.sizes()
+    outs = [torch.empty((t.shape[0], sz["n_padded"], t.shape[2]), dtype=t.dtype, device=t.device)
+            for t in tensors]
+    means = [torch.empty((t.shape[0], sz["n_blocks"], t.shape[2]), dtype=torch.float64,
+                         device=t.device) for t in tensors[:npool]]
+    H, _, d = tensors[0].shape
+    n = len(tensors)
+    src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
+    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    mean_arr = (ctypes.c_void_p * max(npool, 1))(*[t.data_ptr() for t in means])
+    gam_arr = (ctypes.c_void_p * max(nrope, 1))(*[(g.data_ptr() if g is not None else None)
+                                                  for g in gammas[:nrope]])
+    L = layout.c()
+    _lib.check("bsa_permute_norm_rope", lib.bsa_permute_norm_rope(
+        ctypes.byref(L), _ptr(zone_shape), n, src_arr, dst_arr, H, d, _dtype(tensors[0]), nrope,
+        gam_arr, float(eps), float(rope_base), npool, mean_arr, _stream()))
+    return outs, means
+
+
 def select(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, tau: float,
            return_logits: bool = False):
     """bsa_select: counts [H, M] int32, idx [H, M, M] int32 from fp64 block
