@@ -75,7 +75,9 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
     N, Np, H, d = sizes["n_tokens"], sizes["n_padded"], wl.heads, wl.d
     e = 2  # bf16
     M = sizes["n_blocks"]
-    alg = {"unpermute": 2 * H * N * d * e}             # O: read real slots, write raster rows
+    alg = {}
+    if "unpermute" in stage_ms:
+        alg["unpermute"] = 2 * H * N * d * e           # O: read real slots, write raster rows
     if "permute" in stage_ms:
         alg["permute"] = 3 * H * (N + Np) * d * e      # Q, K, V: read real rows, write padded
         alg["pool_select"] = 2 * H * N * d * e         # pooling reads the real rows of Qp, Kp
@@ -183,6 +185,12 @@ def main():
         stages = ["zone_score", "permute_norm_rope", "select", "attn_fwd", "unpermute"]
     else:             # pooling fused into the gather; selection from its block means
         stages = ["zone_score", "permute_pool", "select", "attn_fwd", "unpermute"]
+    # forward-only sequences write O in raster order from the attention kernel
+    # (bsa_attn_fwd_raster); the backward needs the permuted O, so a backward
+    # workload keeps bsa_attn_fwd + bsa_unpermute
+    raster = not wl.backward and not args.unfused
+    if raster:
+        stages.remove("unpermute")
     if wl.backward:
         stages += ["permute_dO", "attn_bwd", "unpermute_grads"]
     ev = {s: [] for s in stages}
@@ -214,10 +222,14 @@ def main():
             mark()
             counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
         mark()
-        op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
-        mark()
-        (o,) = ops.unpermute(lay, zs, [op])
-        mark()
+        if raster:
+            o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
+            mark()
+        else:
+            op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
+            mark()
+            (o,) = ops.unpermute(lay, zs, [op])
+            mark()
         if wl.backward:
             (dop,) = ops.permute(lay, zs, [do])
             mark()
@@ -275,7 +287,8 @@ def main():
                    "blocks": sizes["n_blocks"], "sparsity": wl.sparsity_1e4 / 1e4, "tau": wl.tau,
                    "mode": wl.mode, "backward": wl.backward,
                    "sequence": ("unfused" if args.unfused else
-                                "norm_rope+pool" if args.norm_rope else "pool"),
+                                "norm_rope+pool" if args.norm_rope else "pool") +
+                               (", raster O" if raster else ""),
                    "mean_list": round(pairs / max(1, int((counts > 0).sum())), 2)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {

@@ -249,6 +249,18 @@ bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const vo
                         const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
                         float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* bsa_attn_fwd writing O and lse straight in raster token order (so that the
+ * forward path needs no bsa_unpermute of O):
+ *  o    [heads, N, d] out, the rows of the real tokens (every one is written)
+ *  lse  [heads, N] float out
+ *  Same arithmetic and other arguments as bsa_attn_fwd; supported for the
+ *  bf16, d = 128, 128-token-block configuration (BSA_UNSUPPORTED otherwise).
+ *  The backward takes the permuted O of bsa_attn_fwd. */
+bsa_status bsa_attn_fwd_raster(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                               const void* kp, const void* vp, const int32_t* counts,
+                               const int32_t* idx, int heads, int d, int dtype, float scale,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Block-sparse attention backward over the forward's lists and lse.
  * D_n = dO_n . O_n; dV_m = sum_n P_nm dO_n; dS_nm = P_nm (dO_n . V_m - D_n);
  * dQ_n = scale sum_m dS_nm K_m; dK_m = scale sum_n dS_nm Q_n; sums over the

@@ -136,6 +136,19 @@ def test_attn_fwd_validation(lib):
     assert _attn_fwd(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
 
 
+def test_attn_fwd_raster_validation(lib):
+    c = LAY.c()
+
+    def call(d=128, dt=1, q=FAKE):
+        return lib.bsa_attn_fwd_raster(ctypes.byref(c), FAKE, q, FAKE, FAKE, FAKE, FAKE, 2, d, dt,
+                                       0.0, FAKE, FAKE, FAKE, 1 << 40, None)
+
+    assert call(d=64) == _lib.BSA_UNSUPPORTED     # the raster output needs the MFMA kernel
+    assert call(dt=0) == _lib.BSA_UNSUPPORTED     # fp32
+    assert call(q=None) == _lib.BSA_INVALID_ARG
+    assert "raster" in (call(d=64) and lib.bsa_last_error().decode())
+
+
 def test_attn_bwd_validation(lib):
     c = LAY.c()
 

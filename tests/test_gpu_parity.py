@@ -285,6 +285,22 @@ def test_norm_rope_full_size():
     assert torch.equal(outs[2], vp)
 
 
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[3]], ids=lambda w: w.name)
+def test_attn_fwd_raster(wl):
+    """bsa_attn_fwd_raster writes exactly what bsa_attn_fwd + bsa_unpermute
+    give (same kernel arithmetic): O bitwise, lse bitwise at every real token."""
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(14)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    g = run_gpu(wl, inp, zone_shape=zs, fused=True)
+    o_r, lse_r = ops.attn_fwd_raster(g["lay"], g["zs"], g["qp"], g["kp"], g["vp"], g["counts"],
+                                     g["idx"])
+    assert torch.equal(o_r, g["o"])
+    perm = olay.permutation(L, zs)
+    assert np.array_equal(lse_r.cpu().numpy(), lse_raster(L, perm, g["lse"].cpu().numpy()))
+
+
 def test_cdf_branch_lists():
     """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
     top-k (s = 0.93), so most lists have n = m > k."""
@@ -394,6 +410,9 @@ def test_full_size_workload(name):
         assert not bad.any(), (np.nonzero(bad), zs_gpu[bad], shape[bad], gap[bad])
         print(f"[{name}] zone shapes {np.bincount(zs_gpu, minlength=3).tolist()}, "
               f"{int((zs_gpu != shape).sum())} tie-exempt differences", flush=True)
+    o_r, lse_r = ops.attn_fwd_raster(g["lay"], g["zs"], g["qp"], g["kp"], g["vp"], g["counts"],
+                                     g["idx"])
+    assert torch.equal(o_r, g["o"])          # the benchmark's raster-output forward
     print(f"[{name}] oracle selection", flush=True)
     q, k = (synth.bf16_bits_to_f64(inp[p]) for p in "qk")
     r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau,

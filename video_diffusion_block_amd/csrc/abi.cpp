@@ -341,15 +341,18 @@ bsa_status bsa_select(const bsa_layout* in, const int32_t* zone_shape, const dou
                     "select");
 }
 
-bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
-                        const void* kp, const void* vp, const int32_t* counts,
-                        const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
-                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shape,
+                                  const void* qp, const void* kp, const void* vp,
+                                  const int32_t* counts, const int32_t* idx, int heads, int d,
+                                  int dtype, float scale, void* op, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream, bool raster) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
   BSA_TRY(check_dtype_d(dtype, d));
   if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (raster && !bsa::attn_fwd_uses_mfma(L, d, dtype == BSA_BF16))
+    return fail(BSA_UNSUPPORTED, "raster output needs bf16, d = 128 and 128-token blocks");
   if (!qp || !kp || !vp || !counts || !idx || !op || !lse)
     return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
@@ -361,8 +364,24 @@ bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const v
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
   return hip_status(bsa::launch_attn_fwd(L, zone_shape, qp, kp, vp, counts, idx, heads, d,
                                          dtype == BSA_BF16, sc, op, lse, ws,
-                                         static_cast<hipStream_t>(stream)),
+                                         static_cast<hipStream_t>(stream), raster),
                     "attn_fwd");
+}
+
+bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const int32_t* counts,
+                        const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd_common(in, zone_shape, qp, kp, vp, counts, idx, heads, d, dtype, scale, op,
+                         lse, ws, ws_bytes, stream, false);
+}
+
+bsa_status bsa_attn_fwd_raster(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                               const void* kp, const void* vp, const int32_t* counts,
+                               const int32_t* idx, int heads, int d, int dtype, float scale,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd_common(in, zone_shape, qp, kp, vp, counts, idx, heads, d, dtype, scale, o,
+                         lse, ws, ws_bytes, stream, true);
 }
 
 bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,

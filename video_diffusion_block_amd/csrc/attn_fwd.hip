@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ idx, float scale_log2,
-    __bf16* __restrict__ op, float* __restrict__ lse) {
+    __bf16* __restrict__ op, float* __restrict__ lse, const int32_t* __restrict__ zone_shape,
+    int raster) {
   __shared__ __align__(16) __bf16 sK[2][kTile];  // 2 x 32 KB
   __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB
   __shared__ int32_t sL[kMaxList];               // the row's key-block list (16 KB)
@@ -261,12 +262,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const int32_t* lst = idx + row * L.M;
   const size_t head0 = (size_t)h * L.Np;
   const int q = 32 * qg + l32;  // this lane's query inside the block
+  // where this lane's output row goes: its slot of the permuted [H, Np, d]
+  // layout, or (raster) its token's row of [H, N, d] (pad slots: nowhere)
+  size_t orow_i = head0 + (size_t)i * kB + q;
+  bool o_real = true;
+  if (raster) {
+    const long long tok = slot_token(L, block_box(L, zone_shape, i), q);
+    o_real = tok >= 0;
+    orow_i = (size_t)h * L.N + (size_t)(o_real ? tok : 0);
+  }
 
-  if (n == 0) {  // empty query block (all pad): zeros, lse = -inf
-    if (kh == 0) {
-      __bf16* orow = op + (head0 + (size_t)i * kB + q) * kD;
+  if (n == 0) {  // empty list (an all-pad query block): zeros, lse = -inf
+    if (kh == 0 && o_real) {
+      __bf16* orow = op + orow_i * kD;
       for (int e = 8 * hi; e < kD; e += 16) *reinterpret_cast<uint4*>(orow + e) = make_uint4(0, 0, 0, 0);
-      if (hi == 0) lse[head0 + (size_t)i * kB + q] = -INFINITY;
+      if (hi == 0) lse[orow_i] = -INFINITY;
     }
     return;
   }
@@ -487,14 +497,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     xm[1] = l_run;
   }
   __syncthreads();
-  if (kh == 0) {
+  if (kh == 0 && o_real) {
     const float m2 = xm[0], l2 = xm[1];
     const float mt = fmaxf(m_run, m2);
     const float mu = mt == -INFINITY ? 0.f : mt;
     const float a1 = exp2_fast(m_run - mu), a2 = exp2_fast(m2 - mu);
     const float lt = l_run * a1 + l2 * a2;
     const float inv = 1.f / lt;
-    __bf16* orow = op + (head0 + (size_t)i * kB + q) * kD;
+    __bf16* orow = op + orow_i * kD;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
         }
         *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * hi) = v;
       }
-    if (hi == 0) lse[head0 + (size_t)i * kB + q] = (mt + log2f(lt)) * kLn2;
+    if (hi == 0) lse[orow_i] = (mt + log2f(lt)) * kLn2;
   }
 }
 
@@ -546,7 +556,7 @@ size_t attn_fwd_workspace(const Lay& L, int d, bool bf16) {
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, void* ws, hipStream_t st) {
+                           void* op, float* lse, void* ws, hipStream_t st, bool raster) {
   if (attn_fwd_uses_mfma(L, d, bf16)) {
     BlockMeta* meta = static_cast<BlockMeta*>(ws);
     hipError_t e = launch_block_meta(L, zone_shape, meta, st);
@@ -555,9 +565,10 @@ hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* 
     attn_fwd_mfma<<<grid, kThreads, 0, st>>>(
         L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
         static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e, static_cast<__bf16*>(op),
-        lse);
+        lse, zone_shape, raster ? 1 : 0);
     return hipGetLastError();
   }
+  if (raster) return hipErrorInvalidValue;  // (the raster output needs the MFMA kernel)
   if (bf16)
     return launch_scalar<__bf16>(L, zone_shape, qp, kp, vp, counts, idx, heads, d, scale, op,
                                  lse, st);

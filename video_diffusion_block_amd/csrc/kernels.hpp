@@ -53,13 +53,15 @@ hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logi
                          hipStream_t st);
 
 // Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel, which
-// needs attn_fwd_workspace() bytes (the block table).
+// needs attn_fwd_workspace() bytes (the block table). raster (MFMA kernel
+// only): O and lse are written in raster token order, [heads, N, d] and
+// [heads, N], instead of the permuted [heads, Np, d] and [heads, Np].
 bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16);
 size_t attn_fwd_workspace(const Lay& L, int d, bool bf16);
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, void* ws, hipStream_t st);
+                           void* op, float* lse, void* ws, hipStream_t st, bool raster = false);
 
 // Attention backward.
 size_t attn_bwd_workspace(const Lay& L, int heads, int d);

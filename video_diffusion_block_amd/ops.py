@@ -253,6 +253,24 @@ def attn_fwd(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: floa
     return op, lse
 
 
+def attn_fwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: float = 0.0):
+    """bsa_attn_fwd_raster: o [H, N, d] (raster token order, input dtype) and
+    lse [H, N] float32."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp, vp, counts, idx)
+    H, Np, d = qp.shape
+    N = layout.sizes()["n_tokens"]
+    o = torch.empty((H, N, d), dtype=qp.dtype, device=qp.device)
+    lse = torch.empty((H, N), dtype=torch.float32, device=qp.device)
+    ws = _workspace(_lib.BSA_CALL_ATTN_FWD, layout, H, d, qp.device)
+    L = layout.c()
+    _lib.check("bsa_attn_fwd_raster", lib.bsa_attn_fwd_raster(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(counts),
+        _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+        _stream()))
+    return o, lse
+
+
 def attn_bwd(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, idx,
              scale: float = 0.0):
     """bsa_attn_bwd: dqp, dkp, dvp [H, Np, d], float32 for any input dtype."""
