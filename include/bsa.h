@@ -128,7 +128,8 @@ size_t bsa_workspace_size(bsa_call call, const bsa_layout* L, int heads, int d);
  *   shape(z) = argmin_s sum_a r_a(z) (b_{s,a}^2 - 1)/(Z_a^2 - 1); costs within a
  *          relative 1e-6 of the minimum tie and the lowest shape id wins.
  *  video       [N, C] bf16, raster token order, N = T*H*W
- *  C           channels (1..8192, multiple of 64)
+ *  C           channels (64..8192, multiple of 64); zones up to 4x16x16 and
+ *              zt*H*W*C*2 < 2^31 (BSA_UNSUPPORTED otherwise)
  *  audio       [n_audio, C] bf16, or NULL (then the A2V term is dropped)
  *  n_audio     0..256 (0 iff audio == NULL)
  *  zone_shape  [n_zones] int32 out: shape id per zone

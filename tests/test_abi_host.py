@@ -249,3 +249,11 @@ def test_zone_score_validation(lib):
     big = BSALayout.dynamic((16, 64, 64), (8, 16, 16), ((2, 8, 8),)).c()
     assert lib.bsa_zone_score(ctypes.byref(big), FAKE, 1536, None, 0, FAKE, None, FAKE, 1 << 40,
                               None) == _lib.BSA_UNSUPPORTED
+
+
+def test_zone_score_rejects_zone_offsets_past_32_bits(lib):
+    # zt*H*W*C*2 = 4*256*512*2048*2 = 2^31: one zone's row offsets would not fit
+    wide = BSALayout.dynamic((4, 256, 512)).c()
+    assert lib.bsa_zone_score(ctypes.byref(wide), FAKE, 2048, None, 0, FAKE, None, FAKE, 1 << 40,
+                              None) == _lib.BSA_UNSUPPORTED
+    assert "2^31" in lib.bsa_last_error().decode()

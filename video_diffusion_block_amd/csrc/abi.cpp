@@ -189,6 +189,8 @@ bsa_status bsa_zone_score(const bsa_layout* in, const void* video, int C, const 
   if (n_audio < 0 || n_audio > 256) return fail(BSA_INVALID_ARG, "n_audio = %d out of [0, 256]", n_audio);
   if (L.zt > 4 || L.zh > 16 || L.zw > 16)
     return fail(BSA_UNSUPPORTED, "zone scoring supports zones up to 4x16x16");
+  if ((long long)L.zt * L.H * L.W * C * 2 >= (1LL << 31))
+    return fail(BSA_UNSUPPORTED, "zone scoring needs zt*H*W*C*2 < 2^31 (one zone's offsets in 32 bits)");
   const size_t need = bsa::zone_score_workspace(L, C, n_audio);
   if (!ws || ws_bytes < need)
     return fail(BSA_WORKSPACE_TOO_SMALL, "zone_score needs %zu workspace bytes, got %zu", need, ws_bytes);

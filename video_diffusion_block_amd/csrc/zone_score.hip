@@ -13,7 +13,8 @@
 // minimises the predicted within-block variance sum_a r_a (b_a^2-1)/(Z_a^2-1).
 //
 // Kernels:
-//  gram_kernel     G = A A^T on bf16 MFMA (exact products, fp32 sums), tiny.
+//  gram_kernel     G = A A^T on bf16 MFMA (exact products, fp32 sums), tiny;
+//                  the upper tile pairs, stored in fp32 MFMA operand order.
 //  a2v_kernel      per 256 tokens: logits^T = A X^T on bf16 MFMA (exact products,
 //                  fp32 sums), softmax in fp32 registers (lane-local rows), then
 //                  g^2 = p^T G p as Y = G P^T on fp32 MFMA (32x32x2) over the
@@ -28,6 +29,8 @@
 //                  means, r, the costs and the tie rule; writes the shape ids.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "kernels.hpp"
 
@@ -37,13 +40,23 @@ namespace {
 constexpr double kTieRel = 1e-6;
 
 // ------------------------------------------------------------- Gram matrix --
-// One wavefront per 32 x 32 tile of G = A A^T on bf16 MFMA: the products of
-// bf16 values are exact and accumulate in fp32. Rows past Na read as zero.
-__global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int na_pad, int C,
-                                                  float* gram) {
-  const int ti = blockIdx.x, tj = blockIdx.y, lane = threadIdx.x;
+// One wavefront per tile pair (mt, kt), kt >= mt, of G = A A^T on bf16 MFMA
+// (the products of bf16 values are exact and accumulate in fp32; rows past Na
+// read as zero). The tile is stored in the operand order the A2V kernel's
+// fp32 MFMA takes: lane l = 32 hi + l32 of pair p owns 16 consecutive floats,
+// float r = G[32 mt + l32][32 kt + 8 (r / 4) + 4 hi + r % 4]. The MFMA result
+// of rows kt x columns mt has exactly that lane layout (G is symmetric, and
+// G[i][j], G[j][i] are the same products summed in the same order).
+__host__ __device__ constexpr int gram_pairs(int mt_count) { return mt_count * (mt_count + 1) / 2; }
+
+__global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int mt_count, int C,
+                                                  float* gsw) {
+  const int p = blockIdx.x, lane = threadIdx.x;
+  int mt = 0, rem = p;
+  while (rem >= mt_count - mt) rem -= mt_count - mt++;
+  const int kt = mt + rem;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int ra = 32 * ti + l32, rb = 32 * tj + l32;
+  const int ra = 32 * kt + l32, rb = 32 * mt + l32;
   const __bf16* pa = A + (size_t)ra * C + 8 * hi;
   const __bf16* pb = A + (size_t)rb * C + 8 * hi;
   f32x16 acc = {};
@@ -58,10 +71,10 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int n
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma32x32x16(a[s], b[s], acc);
   }
-  // lane holds G[32 ti + 8(r/4) + 4hi + r%4][32 tj + l32]
+  float4* out = reinterpret_cast<float4*>(gsw + ((size_t)p * 64 + lane) * 16);
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    gram[(size_t)(32 * ti + 8 * (r >> 2) + 4 * hi + (r & 3)) * na_pad + 32 * tj + l32] = acc[r];
+  for (int v = 0; v < 4; ++v)
+    out[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
 }
 
 // --------------------------------------------------------------- A2V norm --
@@ -73,7 +86,8 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int n
 // ([8-channel piece][audio row]) so the fragment reads are conflict free.
 // Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p on fp32 MFMA over
 // the tile pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice),
-// G's row blocks staged in LDS over the (then free) A buffers.
+// each pair's G operands read from the operand-ordered copy the Gram kernel
+// writes, straight into registers, one pair ahead.
 constexpr int kA2vWaves = 8;
 constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
 constexpr int kCh = 64;               // channels per A chunk
@@ -82,16 +96,12 @@ constexpr int kMaxMT = 8;             // audio tiles of 32 (n_audio <= 256)
 template <int MT>
 __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, int C, long long N,
                                                              const __bf16* A, int Na,
-                                                             const float* gram, float inv_sqrt_c,
+                                                             const float* gsw, float inv_sqrt_c,
                                                              float* gout) {
   constexpr int NA_PAD = 32 * MT;
   constexpr int SLOTS = 8 * NA_PAD;               // 16-byte slots per A chunk
   constexpr int ABUF = SLOTS * 8;                  // bf16 elements per A buffer
-  constexpr int GS = 32 * (NA_PAD + 1);            // floats of one staged G row block
-  constexpr int LDS_BYTES = (2 * ABUF * 2 > GS * 4) ? 2 * ABUF * 2 : GS * 4;
-  __shared__ __align__(16) unsigned char smem[LDS_BYTES];
-  __bf16* abuf = reinterpret_cast<__bf16*>(smem);  // [2][piece][row][8]
-  float* gs = reinterpret_cast<float*>(smem);      // [32][NA_PAD + 1] (phase 2)
+  __shared__ __align__(16) __bf16 abuf[2 * ABUF];  // [2][piece][row][8]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -100,24 +110,34 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   const bool tok_ok = tok < N;
   const int nchunks = C / kCh;
 
-  const i32x4 ars = make_buffer_rsrc(A, (uint32_t)Na * C * 2);
-  // A chunk ch into buffer bf: slot s = piece * NA_PAD + row <- A[row][64 ch + 8 piece ..]
-  auto load_a = [&](int ch, int bf) {
-    for (int u = w; u * 64 < SLOTS; u += kA2vWaves) {
-      const int sl = u * 64 + lane;
+  // A chunk ch: LDS slot s = piece * NA_PAD + row <- A[row][64 ch + 8 piece ..]
+  // (zero for rows past Na); thread tid stages slots tid + 512 j.
+  constexpr int kAJ = (SLOTS + 64 * kA2vWaves - 1) / (64 * kA2vWaves);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto load_a = [&](int ch, u32x4 (&ar)[kAJ]) {
+#pragma unroll
+    for (int j = 0; j < kAJ; ++j) {
+      const int sl = tid + 64 * kA2vWaves * j;
       const int piece = sl / NA_PAD, r = sl - piece * NA_PAD;
-      const int voff = sl < SLOTS ? (r * C + kCh * ch + 8 * piece) * 2 : 0;
-      dma16_manual(ars, lds_addr_of(abuf + bf * ABUF + u * 64 * 8),
-                   sl < SLOTS ? voff : (int)(0x7fffffff & ~15), 0);
+      ar[j] = (sl < SLOTS && r < Na)
+                  ? *reinterpret_cast<const u32x4*>(A + (size_t)r * C + kCh * ch + 8 * piece)
+                  : zero4;
+    }
+  };
+  auto store_a = [&](const u32x4 (&ar)[kAJ], int bf) {
+#pragma unroll
+    for (int j = 0; j < kAJ; ++j) {
+      const int sl = tid + 64 * kA2vWaves * j;
+      if (sl < SLOTS) *reinterpret_cast<u32x4*>(abuf + bf * ABUF + sl * 8) = ar[j];
     }
   };
   // X fragments of chunk ch: lane holds X[tok][64 ch + 16 ks + 8 hi .. +8]
-  const bf16x8 zero8 = {};
+  // (tokens past N read the last token; their results are not written)
+  const long long tokc = tok_ok ? tok : N - 1;
   auto load_x = [&](int ch, bf16x8 (&xf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      xf[ks] = tok_ok ? *reinterpret_cast<const bf16x8*>(X + tok * C + kCh * ch + 16 * ks + 8 * hi)
-                      : zero8;
+      xf[ks] = *reinterpret_cast<const bf16x8*>(X + tokc * C + kCh * ch + 16 * ks + 8 * hi);
   };
 
   f32x16 acc[MT];
@@ -126,34 +146,42 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  bf16x8 xa[4];
-  load_a(0, 0);
-  load_x(0, xa);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Pipeline: X fragments three chunks ahead (a ring of four register sets),
+  // A one chunk ahead in registers and one more in LDS (double buffer). All
+  // loads are ordinary loads, so the compiler's waits cover exactly the data
+  // each step uses. Iteration ch: A(ch+1) registers -> LDS; load A(ch+2) and
+  // X(ch+3); multiply chunk ch; barrier.
+  bf16x8 xr[4][4];
+  u32x4 ar[kAJ];
+  load_a(0, ar);
+  load_x(0, xr[0]);
+  if (1 < nchunks) load_x(1, xr[1]);
+  if (2 < nchunks) load_x(2, xr[2]);
+  store_a(ar, 0);
+  if (1 < nchunks) load_a(1, ar);
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int bf = ch & 1;
-    // the next chunk's A (into the other buffer) and X fragments, in flight
-    // while this chunk is multiplied
-    bf16x8 xn[4];
-    if (ch + 1 < nchunks) {
-      load_a(ch + 1, bf ^ 1);
-      load_x(ch + 1, xn);
-    }
-    const __bf16* ab = abuf + bf * ABUF;
+  auto step = [&](int ch, auto ring) {
+    constexpr int R = decltype(ring)::value;  // ch % 4
+    if (ch + 1 < nchunks) store_a(ar, (R + 1) & 1);
+    if (ch + 2 < nchunks) load_a(ch + 2, ar);
+    if (ch + 3 < nchunks) load_x(ch + 3, xr[(R + 3) & 3]);
+    const __bf16* ab = abuf + (R & 1) * ABUF;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 af =
             *reinterpret_cast<const bf16x8*>(ab + ((2 * ks + hi) * NA_PAD + 32 * mt + l32) * 8);
-        acc[mt] = mfma32x32x16(af, xa[ks], acc[mt]);
+        acc[mt] = mfma32x32x16(af, xr[R][ks], acc[mt]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk has landed
-    asm volatile("s_barrier" ::: "memory");
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xa[ks] = xn[ks];
+    __syncthreads();
+  };
+  for (int ch = 0; ch < nchunks; ch += 4) {
+    step(ch, std::integral_constant<int, 0>{});
+    if (ch + 1 < nchunks) step(ch + 1, std::integral_constant<int, 1>{});
+    if (ch + 2 < nchunks) step(ch + 2, std::integral_constant<int, 2>{});
+    if (ch + 3 < nchunks) step(ch + 3, std::integral_constant<int, 3>{});
   }
 
   // softmax over the audio axis; lane holds audio 32mt + 8(r/4) + 4hi + r%4
@@ -179,26 +207,35 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   z += __shfl_xor(z, 32);
 
   // g^2 z^2 = sum over tile pairs of p_mt . (G[mt][kt] p_kt), kt >= mt, the
-  // off-diagonal pairs twice (G is symmetric)
+  // off-diagonal pairs twice (G is symmetric). Each pair's G operands (16
+  // floats per lane, stored in operand order) are loaded one pair ahead.
+  const float4* gl = reinterpret_cast<const float4*>(gsw) + 4 * lane;
+  float4 gn[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) gn[v] = gl[v];
   float gsq = 0.f;
+  int p = 0;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    __syncthreads();
-    for (int e = tid; e < 32 * NA_PAD; e += 64 * kA2vWaves) {
-      const int r = e / NA_PAD, c = e - r * NA_PAD;
-      gs[r * (NA_PAD + 1) + c] = gram[(size_t)(32 * mt + r) * NA_PAD + c];
-    }
-    __syncthreads();
     float part = 0.f;
 #pragma unroll
-    for (int kt = mt; kt < MT; ++kt) {
+    for (int kt = mt; kt < MT; ++kt, ++p) {
+      float gc[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        gc[4 * v] = gn[v].x;
+        gc[4 * v + 1] = gn[v].y;
+        gc[4 * v + 2] = gn[v].z;
+        gc[4 * v + 3] = gn[v].w;
+      }
+      if (p + 1 < gram_pairs(MT)) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gn[v] = gl[256 * (p + 1) + v];
+      }
       f32x16 y = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int a = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        y = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[l32 * (NA_PAD + 1) + a], acc[kt][r], y, 0,
-                                                 0, 0);
-      }
+      for (int r = 0; r < 16; ++r)
+        y = __builtin_amdgcn_mfma_f32_32x32x2f32(gc[r], acc[kt][r], y, 0, 0, 0);
       float d = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) d = fmaf(y[r], acc[mt][r], d);
@@ -214,10 +251,14 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
 // Partials per (zone, chunk of kLC channels): [0] sum x^2, [1..3] sum over the
 // lines along t, h, w of (line sum)^2 / line length, in fp64 (for bf16 inputs
 // the sums and squares are exact; the division by the length is a multiply by
-// its rounded reciprocal). The zone is streamed one t-slice (16 x 16 tokens x
-// kLC channels) at a time through LDS: w- and h-lines are complete inside a
-// slice, t-lines accumulate in registers across slices. Each thread owns fixed
-// lines and the workgroup reduction has a fixed order (deterministic).
+// its rounded reciprocal). The zone is held in LDS as t-slices of 16 x 16
+// tokens x kLC channels: w- and h-lines are complete inside a slice, t-lines
+// accumulate in registers across slices. bf16 features: the whole zone (up to
+// 4 slices, 64 KB) is requested at once with direct global->LDS loads (pad
+// tokens read as zero through the buffer bounds), so one memory latency is
+// paid per workgroup; the one-channel fp32 field is staged a slice at a time.
+// Each thread owns fixed lines and the workgroup reduction has a fixed order
+// (deterministic).
 constexpr int kLC = 32;   // channels per workgroup
 constexpr int kLT = 512;  // threads per workgroup
 constexpr int kTI = 256 * kLC / kLT;  // t-line items per thread
@@ -225,7 +266,9 @@ constexpr int kTI = 256 * kLC / kLT;  // t-line items per thread
 template <typename T>
 __global__ __launch_bounds__(kLT) void line_kernel(Lay L, const T* __restrict__ X, int C,
                                                    double* __restrict__ part) {
-  __shared__ T xs[16 * 16 * kLC];  // one t-slice: [h][w][c]
+  constexpr bool kDirect = sizeof(T) == 2;  // bf16: whole zone by direct loads
+  constexpr int kSlice = 16 * 16 * kLC;     // elements of one t-slice: [h][w][c]
+  __shared__ __align__(16) T xs[(kDirect ? 4 : 1) * kSlice];
   __shared__ double red[4][kLT / 64];
   const int z = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y, tid = threadIdx.x;
   const int zzt = z / (L.gzh * L.gzw), zzh = (z / L.gzw) % L.gzh, zzw = z % L.gzw;
@@ -243,33 +286,58 @@ __global__ __launch_bounds__(kLT) void line_kernel(Lay L, const T* __restrict__ 
   double tacc[kTI];  // t-line sums of items tid + kLT j: channel item % 32, token item / 32
 #pragma unroll
   for (int j = 0; j < kTI; ++j) tacc[j] = 0.0;
-  for (int tt = 0; tt < vt; ++tt) {
+  if constexpr (kDirect) {
+    // LDS slot s (16 bytes) = token s / NSEG of the zone ([t][h][w]), segment
+    // s % NSEG; wave u % 8 loads slots 64 u .. 64 u + 63. Offsets are relative
+    // to the zone's first token (the host requires zt H W C 2 < 2^31); pad and
+    // out-of-grid tokens take an offset past the buffer and read zero.
+    constexpr uint32_t kPadOff = 0x7ffffff0u;  // >= the buffer size below: reads zero
+    const size_t base = (((size_t)t0 * L.H + h0) * L.W + w0) * (size_t)C + c0;
+    const size_t left = ((size_t)L.N * C - base) * sizeof(T);  // bytes from base to X's end
+    const i32x4 rs = make_buffer_rsrc(X + base, (uint32_t)(left < kPadOff ? left : kPadOff));
+    const int w = tid >> 6, lane = tid & 63;
+    const int units = vt * 256 * NSEG / 64;  // 16 per slice
+    for (int u = w; u < units; u += kLT / 64) {
+      const int sl = 64 * u + lane, k = sl / NSEG, sg = sl % NSEG;
+      const int tt = k >> 8, th = (k >> 4) & 15, tw = k & 15;
+      const bool real = th < vh && tw < vw;
+      const int off = real ? (int)((((size_t)tt * L.H + th) * L.W + tw) * (size_t)C * 2 + 16 * sg)
+                           : (int)kPadOff;
+      dma16_manual(rs, lds_addr_of(xs + (size_t)64 * u * EPC), off, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    // stage the slice: token k = 16 th + tw, segment sg
-    for (int e = tid; e < 256 * NSEG; e += kLT) {
-      const int k = e / NSEG, sg = e % NSEG;
-      const int th = k >> 4, tw = k & 15;
-      T* dst = xs + k * kLC + sg * EPC;
-      const int cc = c0 + sg * EPC;
-      if (th < vh && tw < vw) {
-        const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
-        if (vec && cc + EPC <= C) {
-          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
+  }
+  for (int tt = 0; tt < vt; ++tt) {
+    const T* xsl = xs + (kDirect ? tt * kSlice : 0);
+    if constexpr (!kDirect) {
+      __syncthreads();
+      // stage the slice: token k = 16 th + tw, segment sg
+      for (int e = tid; e < 256 * NSEG; e += kLT) {
+        const int k = e / NSEG, sg = e % NSEG;
+        const int th = k >> 4, tw = k & 15;
+        T* dst = xs + k * kLC + sg * EPC;
+        const int cc = c0 + sg * EPC;
+        if (th < vh && tw < vw) {
+          const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
+          if (vec && cc + EPC <= C) {
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
+          } else {
+            for (int qq = 0; qq < EPC; ++qq) dst[qq] = cc + qq < C ? X[n * C + cc + qq] : (T)0.f;
+          }
         } else {
-          for (int qq = 0; qq < EPC; ++qq) dst[qq] = cc + qq < C ? X[n * C + cc + qq] : (T)0.f;
+          for (int qq = 0; qq < EPC; ++qq) dst[qq] = (T)0.f;
         }
-      } else {
-        for (int qq = 0; qq < EPC; ++qq) dst[qq] = (T)0.f;
       }
     }
-    __syncthreads();
+    if constexpr (!kDirect) __syncthreads();
     // w-lines (th, c) and h-lines (tw, c) of this slice, one of each per thread
     {
       const int item = tid, c = item & 31, l = item >> 5;
       double sw = 0.0, sh = 0.0;
       for (int u = 0; u < 16; ++u) {
-        const double xw = (double)(float)xs[(l * 16 + u) * kLC + c];  // (th = l, tw = u)
-        const double xh = (double)(float)xs[(u * 16 + l) * kLC + c];  // (th = u, tw = l)
+        const double xw = (double)(float)xsl[(l * 16 + u) * kLC + c];  // (th = l, tw = u)
+        const double xh = (double)(float)xsl[(u * 16 + l) * kLC + c];  // (th = u, tw = l)
         sw += xw;
         q += xw * xw;
         sh += xh;
@@ -280,7 +348,7 @@ __global__ __launch_bounds__(kLT) void line_kernel(Lay L, const T* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kTI; ++j) {
       const int item = tid + kLT * j;
-      tacc[j] += (double)(float)xs[(item >> 5) * kLC + (item & 31)];
+      tacc[j] += (double)(float)xsl[(item >> 5) * kLC + (item & 31)];
     }
   }
   double rt = 0.0;
@@ -398,7 +466,7 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Workspace: g [N] f32 | gram [pad^2] f32 | xpart [nZ][chunks][4] | gpart [nZ][4] | scratch [7 nZ]
+// Workspace: g [N] f32 | gram [pad^2] f32 (upper tile pairs use less) | xpart [nZ][chunks][4] | gpart [nZ][4] | scratch [7 nZ]
 size_t zone_score_workspace(const Lay& L, int C, int n_audio) {
   const int pad = 32 * ((n_audio + 31) / 32);
   const int chunks = (C + kLC - 1) / kLC;
@@ -431,7 +499,7 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
   const bool use_audio = audio != nullptr && n_audio > 0;
   if (use_audio) {
     const __bf16* A = static_cast<const __bf16*>(audio);
-    gram_kernel<<<dim3(pad / 32, pad / 32), 64, 0, st>>>(A, n_audio, pad, C, gram);
+    gram_kernel<<<gram_pairs(pad / 32), 64, 0, st>>>(A, n_audio, pad / 32, C, gram);
     const unsigned grid = (unsigned)((L.N + kTok - 1) / kTok);  // C % 64 == 0 (checked)
     const float isc = 1.0f / sqrtf((float)C);
     switch (pad / 32) {
