@@ -21,6 +21,8 @@ Modules, in the order the hot path runs them:
 - ``select``    block-mean pooling and hybrid (top-k U CDF-prefix) selection
 - ``attention`` dense softmax attention under an explicit block mask, forward
                 and backward, plus a gathered evaluator of the same sums
+- ``prenorm``   RMSNorm + 3-D RoPE of Q and K before the gather
+- ``causal``    the hybrid selection under a frame-chunk causal block mask
 
 All arithmetic is float64 on inputs upcast exactly from bf16/fp32.
 
