@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--norm-rope", action="store_true",
                     help="fuse RMSNorm + 3-D RoPE of Q and K into the gather (bsa_permute_norm_rope)")
+    ap.add_argument("--causal-frames", type=int, default=0, metavar="F",
+                    help="frame-chunk causal selection (bsa_select_causal) with chunks of F frames")
     ap.add_argument("--unfused", action="store_true",
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     return ap.parse_args()
@@ -156,6 +158,9 @@ def main():
         return
 
     wl = synth.WORKLOADS[args.workload]
+    if args.causal_frames and args.unfused:
+        sys.exit("--causal-frames selects from the gather's block means; it does not combine "
+                 "with --unfused")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
@@ -213,14 +218,17 @@ def main():
             qp, kp, vp = ops.permute(lay, zs, [q, k, v])
             mark()
             counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
-        elif args.norm_rope:
-            (qp, kp, vp), (qbar, kbar) = ops.permute_norm_rope(lay, zs, [q, k, v], gammas)
-            mark()
-            counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
         else:
-            (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
+            if args.norm_rope:
+                (qp, kp, vp), (qbar, kbar) = ops.permute_norm_rope(lay, zs, [q, k, v], gammas)
+            else:
+                (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
             mark()
-            counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
+            if args.causal_frames:
+                counts, idx = ops.select_causal(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau,
+                                                args.causal_frames)
+            else:
+                counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
         mark()
         if raster:
             o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
@@ -288,7 +296,9 @@ def main():
                    "mode": wl.mode, "backward": wl.backward,
                    "sequence": ("unfused" if args.unfused else
                                 "norm_rope+pool" if args.norm_rope else "pool") +
-                               (", raster O" if raster else ""),
+                               (", raster O" if raster else "") +
+                               (f", causal chunks of {args.causal_frames} frames"
+                                if args.causal_frames else ""),
                    "mean_list": round(pairs / max(1, int((counts > 0).sum())), 2)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {
@@ -298,7 +308,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(wl.name),
+            "traffic": None if args.causal_frames else measured_traffic(wl.name),
         },
         "hbm_stages": hbm_stages(wl, sizes, stage_ms, device_copy_gbps()),
         "input_gen_s": round(t_gen, 1),

@@ -229,6 +229,27 @@ bsa_status bsa_select(const bsa_layout* L, const int32_t* zone_shape, const doub
                       int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Frame-chunk causal selection [post-training page (gist.science, paper
+ * 2604.25427), section 2, stage 4: the bidirectional model is distilled into a
+ * causal student that generates frames from its own earlier output through a
+ * KV cache, under a causal attention mask]. Reading implemented (the page
+ * gives no formula): frames form chunks of frames_per_chunk consecutive
+ * frames; a block lies in the chunk of its first frame; query block i sees key
+ * block j iff chunk(j) <= chunk(i); bsa_select's rule then runs over each
+ * row's visible non-empty key blocks (k from their count V_i:
+ * max(1, ceil(V_i (10000 - sparsity_1e4) / 10000))). The lists only name
+ * visible blocks, so bsa_attn_fwd / bsa_attn_bwd on them are block-causal as
+ * they stand.
+ *  frames_per_chunk  >= 1, a multiple of the zone's time extent (the block's in
+ *                    fixed mode), so no block spans two chunks (BSA_INVALID_ARG
+ *                    otherwise)
+ *  pooled_logits     as in bsa_select (not masked)
+ *  Other arguments, outputs and workspace as bsa_select. */
+bsa_status bsa_select_causal(const bsa_layout* L, const int32_t* zone_shape, const double* qbar,
+                             const double* kbar, int heads, int d, int32_t sparsity_1e4,
+                             double tau, int frames_per_chunk, int32_t* counts, int32_t* idx,
+                             double* pooled_logits, void* ws, size_t ws_bytes, void* stream);
+
 /* Block-sparse attention forward [Prism §Blocks: Prism Block Sparse Attention].
  * For every real query slot n of block i: O[n] = sum over real key slots m of
  * the blocks idx[h][i][0..counts) of softmax_m(Q_n . K_m * scale) V_m, and

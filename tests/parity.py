@@ -60,12 +60,13 @@ def gpu_lists(counts: torch.Tensor, idx: torch.Tensor):
     return [[ix[h, i, :c[h, i]].astype(np.int64) for i in range(M)] for h in range(H)]
 
 
-def compare_lists(L, qbar, kbar, counts_np, sparsity_1e4, tau, gpu, oracle):
+def compare_lists(L, qbar, kbar, counts_np, sparsity_1e4, tau, gpu, oracle, visible=None):
     """Exact list equality per (head, query block), except near-ties.
+    ``visible`` (bool [M, M], optional): row i's candidate key blocks (the
+    causal selection); by default every non-empty block.
 
     Returns (exact rows, tie-exempt rows, list of failures)."""
-    cand = np.nonzero(counts_np > 0)[0]
-    k = osel.top_k_size(len(cand), sparsity_1e4)
+    cand_all = np.nonzero(counts_np > 0)[0]
     d = qbar.shape[-1]
     exact = exempt = 0
     failures = []
@@ -78,6 +79,8 @@ def compare_lists(L, qbar, kbar, counts_np, sparsity_1e4, tau, gpu, oracle):
             if counts_np[i] == 0:
                 failures.append((h, i, "empty query block got a list"))
                 continue
+            cand = cand_all if visible is None else np.nonzero(visible[i])[0]
+            k = osel.top_k_size(len(cand), sparsity_1e4)
             logits = (qbar[h, i] @ kbar[h, cand].T) / np.sqrt(d)
             order = np.lexsort((cand, -logits))
             srt = logits[order]
@@ -91,7 +94,8 @@ def compare_lists(L, qbar, kbar, counts_np, sparsity_1e4, tau, gpu, oracle):
             pos = {int(c): r for r, c in enumerate(cand[order])}
             near_cut = all(abs(logits[np.searchsorted(cand, j)] - cut) < LIST_TIE
                            for j in diff if j in pos)
-            ascending = np.all(np.diff(a) > 0) and np.all(counts_np[a] > 0)
+            ascending = np.all(np.diff(a) > 0) and np.all(counts_np[a] > 0) and \
+                np.all(np.isin(a, cand))
             if ascending and (cdf_tie or (near_cut and len(a) == len(b))):
                 exempt += 1
             else:

@@ -233,6 +233,24 @@ def test_select_validation(lib):
     assert 0 < need < lib.bsa_workspace_size(1, ctypes.byref(c), 2, 128)
 
 
+def test_select_causal_validation(lib):
+    c = LAY.c()   # fixed 2x8x8 blocks: chunks must be whole multiples of 2 frames
+    dyn = DYN.c()  # zones 4 frames deep
+
+    def call(F, L=c, S=8500, wsb=1 << 40, zs=FAKE):
+        return lib.bsa_select_causal(ctypes.byref(L), zs, FAKE, FAKE, 2, 128, S, 0.2, F, FAKE,
+                                     FAKE, None, FAKE, wsb, None)
+
+    for F in (0, -2, 3):
+        assert call(F) == _lib.BSA_INVALID_ARG, F
+    assert "frames_per_chunk" in lib.bsa_last_error().decode()
+    for F in (2, 6):
+        assert call(F, L=dyn) == _lib.BSA_INVALID_ARG, F
+    assert call(4, S=10000) == _lib.BSA_INVALID_ARG
+    assert call(4, wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert call(8, L=dyn, zs=None) == _lib.BSA_INVALID_ARG
+
+
 def test_zone_score_validation(lib):
     c = DYN.c()
 

@@ -15,6 +15,7 @@ from oracle import layout as olay
 from oracle import prenorm as opn
 from oracle import pipeline as opipe
 from oracle import select as osel
+from oracle import causal as ocau
 from oracle import zones as ozon
 from parity import (BF16_L1_REL, BF16_MAX_ABS, F32_TOL, ZONE_TIE, assert_bf16_close,
                     compare_lists, gpu_lists, host_f64, oracle_layout, to_dev, to_f64)
@@ -207,6 +208,71 @@ def test_permute_pool(wl):
     exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
                                          wl.tau, gpu_lists(counts, idx), r["lists"])
     assert not fails, fails[:3]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("mult", [1, 2])
+def test_select_causal(wl, mult):
+    """bsa_select_causal against the frame-chunk causal oracle (chunks of mult
+    zone time extents), every listed block visible to its row, and the
+    attention forward on those lists against the gathered fp64 oracle."""
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(11)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    F = mult * L.zone[0]
+    lay = layout_of(wl)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
+    counts, idx = ops.select_causal(lay, zs_dev, qbar, kbar, wl.sparsity_1e4, wl.tau, F)
+    qf, kf, vf = (host_f64(inp[p], wl.dtype) for p in "qkv")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, wl.sparsity_1e4, wl.tau,
+                            zone_shape=zs)
+    want, _, _, _ = ocau.select_causal(L, zs, r["qbar"], r["kbar"], r["counts"],
+                                       wl.sparsity_1e4, wl.tau, F)
+    vis = ocau.visible(L, zs, r["counts"], F)
+    got = gpu_lists(counts, idx)
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, got, want, visible=vis)
+    assert not fails, fails[:3]
+    for lh in got:
+        for i, lst in enumerate(lh):
+            assert np.all(vis[i, lst])
+    o, lse = ops.attn_fwd(lay, zs_dev, qp, kp, vp, counts, idx)
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, r["perm"], qf, kf, vf, got, 1 / np.sqrt(wl.d))
+    (o_r,) = ops.unpermute(lay, zs_dev, [o])
+    if wl.dtype == "bf16":
+        assert_bf16_close(to_f64(o_r), o_ref, "O")
+    else:
+        assert np.abs(to_f64(o_r) - o_ref).max() <= F32_TOL
+
+
+def test_select_causal_full_size():
+    """720p (fixed 2x8x8 blocks, 40 heads) with 4-frame chunks: lists in full
+    against the causal oracle."""
+    wl = synth.WORKLOADS["720p"]
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    lay = layout_of(wl)
+    L = oracle_layout(wl)
+    zs = np.zeros(L.n_zones, dtype=np.int32)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    print("\n[720p causal] gpu", flush=True)
+    _, (qbar, kbar) = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
+    counts, idx = ops.select_causal(lay, zs_dev, qbar, kbar, wl.sparsity_1e4, wl.tau, 4)
+    print("[720p causal] oracle", flush=True)
+    qf, kf = (host_f64(inp[p], wl.dtype) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, wl.sparsity_1e4, wl.tau,
+                            zone_shape=zs)
+    want, n, _, kk = ocau.select_causal(L, zs, r["qbar"], r["kbar"], r["counts"],
+                                        wl.sparsity_1e4, wl.tau, 4)
+    vis = ocau.visible(L, zs, r["counts"], 4)
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
+                                         wl.tau, gpu_lists(counts, idx), want, visible=vis)
+    assert not fails, fails[:3]
+    print(f"[720p causal] {exact} exact, {exempt} tie-exempt rows; mean list "
+          f"{n.mean():.1f} (non-causal k = 63)", flush=True)
 
 
 NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),

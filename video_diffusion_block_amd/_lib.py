@@ -56,6 +56,9 @@ SIGNATURES = {
                                              ctypes.POINTER(vp), vp]),
     "bsa_select": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                                   ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+    "bsa_select_causal": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int32, ctypes.c_double, ctypes.c_int, vp, vp,
+                                         vp, vp, ctypes.c_size_t, vp]),
     "bsa_unpermute": (ctypes.c_int, [LayoutP, vp, ctypes.c_int, ctypes.POINTER(vp),
                                      ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, vp]),

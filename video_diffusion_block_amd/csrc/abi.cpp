@@ -284,7 +284,8 @@ static bsa_status check_select_args(const bsa_layout* in, const bsa::Lay& L,
 static hipError_t select_tail(const bsa::Lay& L, const int32_t* zone_shape, const double* qbar,
                               const double* kbar, int heads, int d, int32_t sparsity_1e4,
                               double tau, int32_t* counts, int32_t* idx, double* pooled_logits,
-                              char* p, hipStream_t st, bool meta_ready) {
+                              char* p, hipStream_t st, bool meta_ready,
+                              int frames_per_chunk = 0) {
   double* logits = pooled_logits ? pooled_logits : reinterpret_cast<double*>(p);
   p += al256((size_t)heads * L.M * L.M * sizeof(double));
   bsa::BlockMeta* meta = reinterpret_cast<bsa::BlockMeta*>(p);
@@ -293,7 +294,8 @@ static hipError_t select_tail(const bsa::Lay& L, const int32_t* zone_shape, cons
     e = bsa::launch_pooled_logits(L, meta, qbar, kbar, heads, d, 1.0 / sqrt((double)d), logits,
                                   st);
   if (e == hipSuccess)
-    e = bsa::launch_select(L, meta, logits, heads, sparsity_1e4, tau, counts, idx, st);
+    e = bsa::launch_select(L, meta, logits, heads, sparsity_1e4, tau, counts, idx, st,
+                           frames_per_chunk);
   return e;
 }
 
@@ -326,21 +328,43 @@ bsa_status bsa_pool_select(const bsa_layout* in, const int32_t* zone_shape, cons
   return hip_status(e, "pool_select");
 }
 
-bsa_status bsa_select(const bsa_layout* in, const int32_t* zone_shape, const double* qbar,
-                      const double* kbar, int heads, int d, int32_t sparsity_1e4, double tau,
-                      int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
-                      size_t ws_bytes, void* stream) {
+static bsa_status select_common(const bsa_layout* in, const int32_t* zone_shape,
+                                const double* qbar, const double* kbar, int heads, int d,
+                                int32_t sparsity_1e4, double tau, int frames_per_chunk,
+                                int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
+                                size_t ws_bytes, void* stream) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_select_args(in, L, zone_shape, heads, d, sparsity_1e4, tau, counts, idx));
   if (!qbar || !kbar) return fail(BSA_INVALID_ARG, "qbar/kbar is NULL");
+  if (frames_per_chunk < 0 || (frames_per_chunk > 0 && frames_per_chunk % L.zt))
+    return fail(BSA_INVALID_ARG, "frames_per_chunk = %d must be a positive multiple of the zone's time extent %d",
+                frames_per_chunk, L.zt);
   const size_t need = select_ws(L, heads);
   if (!ws || ws_bytes < need)
     return fail(BSA_WORKSPACE_TOO_SMALL, "select needs %zu workspace bytes, got %zu", need, ws_bytes);
   return hip_status(select_tail(L, zone_shape, qbar, kbar, heads, d, sparsity_1e4, tau, counts,
                                 idx, pooled_logits, static_cast<char*>(ws),
-                                static_cast<hipStream_t>(stream), false),
+                                static_cast<hipStream_t>(stream), false, frames_per_chunk),
                     "select");
+}
+
+bsa_status bsa_select(const bsa_layout* in, const int32_t* zone_shape, const double* qbar,
+                      const double* kbar, int heads, int d, int32_t sparsity_1e4, double tau,
+                      int32_t* counts, int32_t* idx, double* pooled_logits, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return select_common(in, zone_shape, qbar, kbar, heads, d, sparsity_1e4, tau, 0, counts, idx,
+                       pooled_logits, ws, ws_bytes, stream);
+}
+
+bsa_status bsa_select_causal(const bsa_layout* in, const int32_t* zone_shape, const double* qbar,
+                             const double* kbar, int heads, int d, int32_t sparsity_1e4,
+                             double tau, int frames_per_chunk, int32_t* counts, int32_t* idx,
+                             double* pooled_logits, void* ws, size_t ws_bytes, void* stream) {
+  if (frames_per_chunk < 1)
+    return fail(BSA_INVALID_ARG, "frames_per_chunk = %d must be >= 1", frames_per_chunk);
+  return select_common(in, zone_shape, qbar, kbar, heads, d, sparsity_1e4, tau,
+                       frames_per_chunk, counts, idx, pooled_logits, ws, ws_bytes, stream);
 }
 
 static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shape,

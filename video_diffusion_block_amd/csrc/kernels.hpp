@@ -47,10 +47,12 @@ hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const doubl
                                 const double* kbar, int heads, int d, double scale,
                                 double* logits, hipStream_t st);
 
-// Hybrid selection per (head, query block) from the pooled logits.
+// Hybrid selection per (head, query block) from the pooled logits;
+// frames_per_chunk > 0 (a multiple of L.zt) restricts row i to the key blocks
+// of its own and earlier frame chunks.
 hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logits, int heads,
                          int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
-                         hipStream_t st);
+                         hipStream_t st, int frames_per_chunk = 0);
 
 // Attention forward. bf16 + d = 128 + B = 128 takes the MFMA kernel, which
 // needs attn_fwd_workspace() bytes (the block table). raster (MFMA kernel

@@ -217,6 +217,7 @@ template <int P2, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMeta* __restrict__ meta,
                                                              const double* __restrict__ logits,
                                                              int sparsity_1e4, double tau,
+                                                             int frames_per_chunk,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ idx) {
   constexpr int C = P2 / 64;  // entries per lane
@@ -234,14 +235,26 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
   uint32_t* bits = sbits[w];
   const double* lg = logits + row * L.M;
 
-  // candidates are the non-empty key blocks, whose pooled logits are finite
+  // candidates are the non-empty key blocks, whose pooled logits are finite.
+  // Frame-chunk causal rows (frames_per_chunk > 0, a multiple of the zone's
+  // time extent): chunk(b) = first frame of b's zone / F, and since zones run
+  // time-slowest the blocks of chunks <= chunk(i) are the prefix of ids below
+  // the first zone of chunk(i) + 1.
+  int jend = L.M;
+  if (frames_per_chunk > 0) {
+    const int zrow = (i / L.bpz) / (L.gzh * L.gzw);  // zone row (in time) of i
+    const long long next_row =
+        (long long)((zrow * L.zt) / frames_per_chunk + 1) * frames_per_chunk / L.zt;
+    const long long end = next_row * L.gzh * L.gzw * L.bpz;
+    jend = end < L.M ? (int)end : L.M;
+  }
   double key[C];
   int id[C];
   int valid = 0;
 #pragma unroll
   for (int e = 0; e < C; ++e) {
     const int j = lane * C + e;
-    key[e] = j < L.M ? lg[j] : -INFINITY;
+    key[e] = j < jend ? lg[j] : -INFINITY;
     id[e] = j;
     valid += key[e] != -INFINITY;
   }
@@ -487,10 +500,10 @@ hipError_t launch_pooled_logits(const Lay& L, const BlockMeta* meta, const doubl
 
 hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logits,
                          int heads, int sparsity_1e4, double tau, int32_t* counts, int32_t* idx,
-                         hipStream_t st) {
+                         hipStream_t st, int frames_per_chunk) {
 #define BSA_SELECT(P, W)                                                                   \
   select_kernel<P, W><<<dim3((L.M + (W) - 1) / (W), heads), 64 * (W), 0, st>>>(            \
-      L, meta, logits, sparsity_1e4, tau, counts, idx)
+      L, meta, logits, sparsity_1e4, tau, frames_per_chunk, counts, idx)
   // row widths: multiples of 64 (one register slot per lane each), chosen
   // to cover the common block counts with few empty slots
   if (L.M <= 256) BSA_SELECT(256, 4);

@@ -207,6 +207,24 @@ def select(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, tau: fl
     return (counts, idx, logits) if return_logits else (counts, idx)
 
 
+def select_causal(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, tau: float,
+                  frames_per_chunk: int):
+    """bsa_select_causal: bsa_select with each query block restricted to the
+    key blocks of its own and earlier chunks of frames_per_chunk frames."""
+    lib = _lib.load()
+    _dev(zone_shape, qbar, kbar)
+    H, M, d = qbar.shape
+    counts = torch.empty((H, M), dtype=torch.int32, device=qbar.device)
+    idx = torch.empty((H, M, M), dtype=torch.int32, device=qbar.device)
+    ws = _workspace(_lib.BSA_CALL_SELECT, layout, H, d, qbar.device)
+    L = layout.c()
+    _lib.check("bsa_select_causal", lib.bsa_select_causal(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qbar), _ptr(kbar), H, d, int(sparsity_1e4),
+        float(tau), int(frames_per_chunk), _ptr(counts), _ptr(idx), None, _ptr(ws), ws.numel(),
+        _stream()))
+    return counts, idx
+
+
 def unpermute(layout: BSALayout, zone_shape, tensors):
     """bsa_unpermute: list of [H, Np, d] -> list of [H, N, d] (one launch)."""
     _dev(zone_shape, *tensors)
