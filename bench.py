@@ -2,10 +2,11 @@
 
 One step = one BSA attention layer forward on the 720p workload (13x45x80 =
 46 800 latent tokens, 40 heads, d = 128, bf16, fixed 2x8x8 blocks, sparsity
-0.85, tau = 0.20): zone scoring (a no-op fill for a fixed layout), permutation
-of Q/K/V, block pooling + hybrid selection, block-sparse attention forward and
-unpermutation of O. Inputs are seeded synthetic latents (smooth field + noise),
-resident in HBM before timing starts.
+0.85, tau = 0.20): zone scoring (a no-op fill for a fixed layout), gather of
+Q/K/V with the block means of Q and K pooled on the way, hybrid selection, and
+the block-sparse attention forward writing O in raster order. Inputs are
+seeded synthetic latents (smooth field + noise), resident in HBM before timing
+starts.
 
 Prints one JSON line: value = executed attention TFLOP/s over the whole layer
 time (the layer's executed attention FLOPs / ms per layer), plus ms per layer,
@@ -15,7 +16,11 @@ rate on a bounded sample of the same workload.
 
 Options: --workload NAME runs another workload of the measurement plan
 (720p-dyn, 1080p, 2k; 2k adds the backward); --copy-calib runs only a plain
-1 GiB device copy (the calibration kernel for HBM byte counters).
+1 GiB device copy (the calibration kernel for HBM byte counters); --unfused
+(separate gather and pool+select calls), --norm-rope (RMSNorm + 3-D RoPE of Q
+and K in the gather), --causal-frames F (frame-chunk causal selection) and
+--reuse-every R (zone shapes and lists recomputed every R steps, reused in
+between) time the variants of the same layer.
 """
 from __future__ import annotations
 
@@ -44,6 +49,9 @@ def parse():
                     help="fuse RMSNorm + 3-D RoPE of Q and K into the gather (bsa_permute_norm_rope)")
     ap.add_argument("--causal-frames", type=int, default=0, metavar="F",
                     help="frame-chunk causal selection (bsa_select_causal) with chunks of F frames")
+    ap.add_argument("--reuse-every", type=int, default=1, metavar="R",
+                    help="recompute zone shapes and block lists every R steps and reuse them in "
+                         "between (forward-only; ms/layer is the average over the steps)")
     ap.add_argument("--unfused", action="store_true",
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     return ap.parse_args()
@@ -86,6 +94,8 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
     else:                                              # + the fp64 block means of Q and K
         name = "permute_norm_rope" if "permute_norm_rope" in stage_ms else "permute_pool"
         alg[name] = 3 * H * (N + Np) * d * e + 2 * H * M * d * 8
+    if "reuse_permute" in stage_ms:                    # reuse steps: gather without pooling
+        alg["reuse_permute"] = 3 * H * (N + Np) * d * e
     if wl.mode == "dynamic":
         alg["zone_score"] = N * wl.video_channels * e + wl.n_audio * wl.video_channels * e
     if wl.backward:
@@ -161,6 +171,10 @@ def main():
     if args.causal_frames and args.unfused:
         sys.exit("--causal-frames selects from the gather's block means; it does not combine "
                  "with --unfused")
+    if args.reuse_every < 1:
+        sys.exit("--reuse-every must be >= 1")
+    if args.reuse_every > 1 and (wl.backward or args.unfused or args.norm_rope):
+        sys.exit("--reuse-every applies to the default forward-only sequence")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
@@ -184,83 +198,91 @@ def main():
     gammas = [torch.from_numpy(grng.uniform(0.5, 1.5, wl.d).astype(np.float32)).to(dev)
               for _ in range(2)]
 
-    if args.unfused:  # separate permute and pool+select calls
-        stages = ["zone_score", "permute", "pool_select", "attn_fwd", "unpermute"]
-    elif args.norm_rope:  # Q, K normalized and rotated in the gather, then pooled
-        stages = ["zone_score", "permute_norm_rope", "select", "attn_fwd", "unpermute"]
-    else:             # pooling fused into the gather; selection from its block means
-        stages = ["zone_score", "permute_pool", "select", "attn_fwd", "unpermute"]
     # forward-only sequences write O in raster order from the attention kernel
     # (bsa_attn_fwd_raster); the backward needs the permuted O, so a backward
     # workload keeps bsa_attn_fwd + bsa_unpermute
     raster = not wl.backward and not args.unfused
-    if raster:
-        stages.remove("unpermute")
-    if wl.backward:
-        stages += ["permute_dO", "attn_bwd", "unpermute_grads"]
-    ev = {s: [] for s in stages}
-    state = {}
+    state = {"step": 0}
 
     def step(record):
         s = torch.cuda.current_stream()
         marks = []
 
-        def mark():
+        def mark(name):
             if record:
                 e = torch.cuda.Event(enable_timing=True)
                 e.record(s)
-                marks.append(e)
+                marks.append((name, e))
 
-        mark()
+        reuse = args.reuse_every > 1 and state["step"] % args.reuse_every != 0
+        state["step"] += 1
+        mark(None)
+        if reuse:   # zone shapes and lists of the last refresh; this step's Q, K, V
+            zs, counts, idx = state["zs"], state["counts"], state["idx"]
+            qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+            mark("permute")
+            o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
+            mark("attn_fwd")
+            if record:
+                ev_marks.append(marks)
+            return
         zs = ops.zone_score(lay, video, audio)
-        mark()
+        mark("zone_score")
         if args.unfused:
             qp, kp, vp = ops.permute(lay, zs, [q, k, v])
-            mark()
+            mark("permute")
             counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
+            mark("pool_select")
         else:
             if args.norm_rope:
                 (qp, kp, vp), (qbar, kbar) = ops.permute_norm_rope(lay, zs, [q, k, v], gammas)
+                mark("permute_norm_rope")
             else:
                 (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
-            mark()
+                mark("permute_pool")
             if args.causal_frames:
                 counts, idx = ops.select_causal(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau,
                                                 args.causal_frames)
             else:
                 counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
-        mark()
+            mark("select")
         if raster:
             o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
-            mark()
+            mark("attn_fwd")
         else:
             op, lse = ops.attn_fwd(lay, zs, qp, kp, vp, counts, idx)
-            mark()
+            mark("attn_fwd")
             (o,) = ops.unpermute(lay, zs, [op])
-            mark()
+            mark("unpermute")
         if wl.backward:
             (dop,) = ops.permute(lay, zs, [do])
-            mark()
+            mark("permute_dO")
             grads = ops.attn_bwd(lay, zs, qp, kp, vp, op, dop, lse, counts, idx)
-            mark()
+            mark("attn_bwd")
             ops.unpermute(lay, zs, list(grads))
-            mark()
-        state["counts"] = counts
+            mark("unpermute_grads")
+        state.update(zs=zs, counts=counts, idx=idx)
         if record:
             ev_marks.append(marks)
 
     ev_marks = []
     for _ in range(args.warmup):
         step(False)
+    state["step"] = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # stage times: refresh steps under their stage names, reuse steps (which
+    # gather without pooling and skip zone scoring and selection) under
+    # "reuse_<stage>"
+    ev = {}
     for marks in ev_marks:
-        for si, s in enumerate(stages):
-            ev[s].append(marks[si].elapsed_time(marks[si + 1]))
+        reuse_step = marks[1][0] == "permute" and args.reuse_every > 1
+        for (_, a), (name, b) in zip(marks, marks[1:]):
+            ev.setdefault(("reuse_" if reuse_step else "") + name, []).append(a.elapsed_time(b))
     stage_ms = {s: float(np.mean(v)) for s, v in ev.items()}
     ms_per_step = wall * 1e3 / args.steps
 
@@ -298,7 +320,9 @@ def main():
                                 "norm_rope+pool" if args.norm_rope else "pool") +
                                (", raster O" if raster else "") +
                                (f", causal chunks of {args.causal_frames} frames"
-                                if args.causal_frames else ""),
+                                if args.causal_frames else "") +
+                               (f", lists reused for {args.reuse_every} steps"
+                                if args.reuse_every > 1 else ""),
                    "mean_list": round(pairs / max(1, int((counts > 0).sum())), 2)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {

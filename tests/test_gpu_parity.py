@@ -275,6 +275,43 @@ def test_select_causal_full_size():
           f"{n.mean():.1f} (non-causal k = 63)", flush=True)
 
 
+def test_reused_selection_schedule():
+    """ReusedSelection over 4 steps, lists refreshed every 2 (whole run as the
+    middle segment): a refresh step equals the direct bsa_permute_pool +
+    bsa_select + bsa_attn_fwd_raster calls on that step's inputs; a reuse step
+    equals bsa_permute + bsa_attn_fwd_raster of the step's own Q, K, V under
+    the previous step's lists (bitwise)."""
+    from video_diffusion_block_amd.schedule import ReusedSelection
+    wl = SMALL[3]
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    lay = layout_of(wl)
+    base = [to_dev(inp[p], wl.dtype) for p in "qkv"]
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    layer = ReusedSelection(lay, wl.sparsity_1e4, wl.tau, total_steps=4, every=2, middle=(0.0, 1.0))
+    assert layer.plan == [True, False, True, False]
+    prev = None
+    for step in range(4):
+        q, k, v = ((t.float() + 0.05 * step * torch.randn(t.shape, device="cuda", generator=gen))
+                   .to(t.dtype) for t in base)
+        o, lse = layer(step, q, k, v)
+        zs = ops.zone_score(lay, None, None)
+        if step % 2 == 0:
+            assert layer.refreshed
+            (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
+            counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
+            assert torch.equal(counts, layer.counts)
+            for h in range(counts.shape[0]):
+                for i in range(counts.shape[1]):
+                    c = int(counts[h, i])
+                    assert torch.equal(idx[h, i, :c], layer.idx[h, i, :c])
+        else:
+            assert not layer.refreshed and layer.idx is prev
+            qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+        o2, lse2 = ops.attn_fwd_raster(lay, zs, qp, kp, vp, layer.counts, layer.idx)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+        prev = layer.idx
+
+
 NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),
                                    8500, 0.2)]
 
