@@ -23,6 +23,8 @@ Modules, in the order the hot path runs them:
                 and backward, plus a gathered evaluator of the same sums
 - ``prenorm``   RMSNorm + 3-D RoPE of Q and K before the gather
 - ``causal``    the hybrid selection under a frame-chunk causal block mask
+- ``crossattn`` the A2V cross-attention layer (projections, multi-head
+                attention over the audio tokens), forward and backward
 
 All arithmetic is float64 on inputs upcast exactly from bf16/fp32.
 
