@@ -298,6 +298,29 @@ bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const vo
                         int heads, int d, int dtype, float scale, void* dqp, void* dkp,
                         void* dvp, void* ws, size_t ws_bytes, void* stream);
 
+/* Audio-to-video cross-attention layer, forward [Prism §Blocks: the zone's
+ * block shape uses the feature norm of the audio-to-video cross-attention, in
+ * which video tokens attend to the audio tokens]. Reading implemented (the
+ * page gives no layer definition): H heads of d = 128, weights in [out, in]
+ * layout, no biases:
+ *   Q = X Wq^T, K = A Wk^T, V = A Wv^T (D = 128 H columns, head h = columns
+ *   128 h .. 128 h + 127), O_h = softmax(Q_h K_h^T / sqrt(128)) V_h over all
+ *   audio tokens, lse_h = ln of its denominator, Y = O Wo^T.
+ * Products accumulate in fp32; Q, K, V, O and Y are stored as bf16.
+ *  n_video   N >= 1 video tokens; n_audio 1..256 audio tokens
+ *  C         feature channels, 64..8192, a multiple of 64
+ *  heads     1..64; d must be 128 (BSA_UNSUPPORTED otherwise)
+ *  x [N, C], a [n_audio, C], wq, wk, wv [D, C], wo [C, D]   bf16, row-major,
+ *            16-byte aligned
+ *  q [N, D], k [n_audio, D], v [n_audio, D], o [N, D]       bf16 out (the
+ *            backward takes them)
+ *  lse [heads, N] float out; y [N, C] bf16 out
+ *  No workspace. */
+bsa_status bsa_xattn_fwd(int n_video, int n_audio, int C, int heads, int d, const void* x,
+                         const void* a, const void* wq, const void* wk, const void* wv,
+                         const void* wo, void* q, void* k, void* v, void* o, float* lse, void* y,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

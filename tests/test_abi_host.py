@@ -275,3 +275,18 @@ def test_zone_score_rejects_zone_offsets_past_32_bits(lib):
     assert lib.bsa_zone_score(ctypes.byref(wide), FAKE, 2048, None, 0, FAKE, None, FAKE, 1 << 40,
                               None) == _lib.BSA_UNSUPPORTED
     assert "2^31" in lib.bsa_last_error().decode()
+
+
+def test_xattn_fwd_validation(lib):
+    def call(N=100, Na=200, C=256, H=2, d=128, ptr=FAKE):
+        return lib.bsa_xattn_fwd(N, Na, C, H, d, ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(N=0) == _lib.BSA_INVALID_ARG
+    assert call(Na=0) == _lib.BSA_INVALID_ARG
+    assert call(Na=257) == _lib.BSA_INVALID_ARG
+    assert call(C=100) == _lib.BSA_INVALID_ARG
+    assert call(H=0) == _lib.BSA_INVALID_ARG
+    assert call(d=64) == _lib.BSA_UNSUPPORTED
+    assert call(ptr=None) == _lib.BSA_INVALID_ARG
+    assert call(ptr=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG   # misaligned

@@ -1,0 +1,83 @@
+"""GPU parity of the A2V cross-attention layer (bsa_xattn_fwd) against the
+fp64 oracle (oracle/crossattn.py), which stores Q, K, V, O and Y as bf16 at the
+same points. Bars: Q, K, V (single GEMMs) within one bf16 ulp of the oracle;
+O and Y under the bf16 rule of the other attention tests (max-abs <= 2e-2,
+sum|diff| / sum|ref| <= 5e-3; the GPU also rounds the softmax weights to bf16
+for the PV product); lse max-abs <= 2e-3 (ln(1 + 2^-9): the denominator sums
+the bf16-rounded weights, over as few as one audio token)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import crossattn as oca
+from parity import assert_bf16_close, to_dev, to_f64
+from video_diffusion_block_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(grid, C, Na, heads, seed=21):
+    """X: smooth field [N, C]; A: N(0, 1) audio tokens; weights N(0, 1/fan_in), all bf16."""
+    X = synth.smooth_field(1, grid, C, seed)[0]
+    A = synth.f32_to_bf16_bits(synth.gaussian_noise((Na, C), seed + 1))
+    D = 128 * heads
+    W = []
+    for i, (o, n) in enumerate(((D, C), (D, C), (D, C), (C, D))):
+        w = synth.gaussian_noise((o, n), seed + 2 + i) / np.sqrt(n)
+        W.append(synth.f32_to_bf16_bits(w.astype(np.float32)))
+    return X, A, W
+
+
+def _ulp_close(got, ref, what):
+    """Within one bf16 ulp (of the larger of the two values) of the oracle's
+    bf16 value, plus 2^-16 of the tensor's largest magnitude: fp32
+    accumulation moves results near zero, where an ulp is tiny, across a
+    rounding boundary."""
+    tol = np.maximum(np.abs(ref), np.abs(got)) * 2.0 ** -7 + 2.0 ** -16 * np.abs(ref).max()
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (what, int(bad.sum()), float(np.abs(got - ref).max()))
+
+
+def _run(grid, C, Na, heads, rows=None):
+    X, A, W = _inputs(grid, C, Na, heads)
+    y, saved = ops.xattn_fwd(to_dev(X, "bf16"), to_dev(A, "bf16"), *[to_dev(w, "bf16") for w in W],
+                             heads)
+    Xf, Af = synth.bf16_bits_to_f64(X), synth.bf16_bits_to_f64(A)
+    Wf = [synth.bf16_bits_to_f64(w) for w in W]
+    sel = np.arange(Xf.shape[0]) if rows is None else rows
+    ref = oca.forward(Xf[sel], Af, *Wf, heads)
+    _ulp_close(to_f64(saved["k"]), ref["k"], "K")
+    _ulp_close(to_f64(saved["v"]), ref["v"], "V")
+    _ulp_close(to_f64(saved["q"])[sel], ref["q"], "Q")
+    assert_bf16_close(to_f64(saved["o"])[sel], ref["o"], "O")
+    assert_bf16_close(to_f64(y)[sel], ref["y"], "Y")
+    lse = saved["lse"].cpu().numpy().astype(np.float64)[:, sel]
+    # the GPU's softmax denominator sums the bf16-rounded weights (each within
+    # 2^-9 relative), so lse is within ln(1 + 2^-9) < 2e-3 of the exact value
+    assert np.abs(lse - ref["lse"]).max() <= 2e-3
+    return y, saved
+
+
+@pytest.mark.parametrize("grid,C,Na,heads", [((2, 10, 15), 128, 37, 2), ((5, 8, 25), 256, 200, 3),
+                                             ((1, 3, 3), 64, 1, 1), ((3, 16, 16), 192, 256, 1)])
+def test_xattn_fwd_small(grid, C, Na, heads):
+    _run(grid, C, Na, heads)
+
+
+def test_xattn_fwd_full_size_sampled():
+    """720p video tokens (13 x 45 x 80), C = 1536, 200 audio tokens, 12 heads:
+    every K and V, and Q, O, Y, lse on 192 sampled query rows (first, middle,
+    last 64)."""
+    N = 13 * 45 * 80
+    rows = np.r_[0:64, N // 2:N // 2 + 64, N - 64:N]
+    print("\n[xattn 720p] running", flush=True)
+    _run((13, 45, 80), 1536, 200, 12, rows=rows)
+
+
+def test_xattn_fwd_is_deterministic():
+    X, A, W = _inputs((2, 10, 15), 128, 37, 2)
+    args = [to_dev(X, "bf16"), to_dev(A, "bf16")] + [to_dev(w, "bf16") for w in W]
+    y1, s1 = ops.xattn_fwd(*args, 2)
+    y2, s2 = ops.xattn_fwd(*args, 2)
+    assert torch.equal(y1, y2) and torch.equal(s1["lse"], s2["lse"])

@@ -56,6 +56,8 @@ SIGNATURES = {
                                              ctypes.POINTER(vp), vp]),
     "bsa_select": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int32,
                                   ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+    "bsa_xattn_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int] + [vp] * 6 + [vp] * 4 + [vp, vp, vp]),
     "bsa_select_causal": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int32, ctypes.c_double, ctypes.c_int, vp, vp,
                                          vp, vp, ctypes.c_size_t, vp]),

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libbsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "permute.hip", "pool_select.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "zone_score.hip"]
+           "zone_score.hip", "crossattn.hip"]
 
 # Packed fp32 instructions are disabled: hipcc would otherwise form them from
 # ordinary float code, and the kernels here do not rely on them.

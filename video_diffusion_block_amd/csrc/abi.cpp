@@ -436,3 +436,30 @@ bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const v
 }
 
 }  // extern "C"
+
+static bsa_status check_xattn(int n_video, int n_audio, int C, int heads, int d) {
+  if (n_video < 1) return fail(BSA_INVALID_ARG, "n_video = %d must be >= 1", n_video);
+  if (n_audio < 1 || n_audio > 256) return fail(BSA_INVALID_ARG, "n_audio = %d out of [1, 256]", n_audio);
+  if (C < 64 || C > 8192 || C % 64) return fail(BSA_INVALID_ARG, "C = %d must be a multiple of 64 in [64, 8192]", C);
+  if (heads < 1 || heads > 64) return fail(BSA_INVALID_ARG, "heads = %d out of [1, 64]", heads);
+  if (d != 128) return fail(BSA_UNSUPPORTED, "d = %d; the cross-attention supports d = 128", d);
+  return ok();
+}
+
+bsa_status bsa_xattn_fwd(int n_video, int n_audio, int C, int heads, int d, const void* x,
+                         const void* a, const void* wq, const void* wk, const void* wv,
+                         const void* wo, void* q, void* k, void* v, void* o, float* lse, void* y,
+                         void* stream) {
+  BSA_TRY(check_xattn(n_video, n_audio, C, heads, d));
+  const void* in[] = {x, a, wq, wk, wv, wo, q, k, v, o, lse, y};
+  for (const void* p : in)
+    if (!p) return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  for (const void* p : in)
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(BSA_INVALID_ARG, "tensors must be 16-byte aligned");
+  typedef const __bf16* cb;
+  return hip_status(bsa::launch_xattn_fwd(n_video, n_audio, heads, (cb)x, (cb)a, C, (cb)wq, (cb)wk,
+                                          (cb)wv, (cb)wo, (__bf16*)q, (__bf16*)k, (__bf16*)v,
+                                          (__bf16*)o, lse, (__bf16*)y,
+                                          static_cast<hipStream_t>(stream)),
+                    "xattn_fwd");
+}

@@ -73,6 +73,21 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
                            int heads, int d, bool bf16, float scale, void* dqp, void* dkp,
                            void* dvp, void* ws, hipStream_t st);
 
+// A2V cross-attention layer. C[M,N] = sum_k A[m][k] B[n][k] (bf16, K a
+// multiple of 8, rows 16-byte aligned), fp32 accumulation, bf16 or fp32 out
+// (fp32 optionally added to C).
+hipError_t launch_gemm_nt(const __bf16* A, int lda, const __bf16* B, int ldb, int M, int N, int K,
+                          void* C, int ldc, bool out_f32, bool accumulate, hipStream_t st);
+// bf16 [R, Cc] (row stride lds) -> [Cc, ldo], columns R..ldo-1 zero.
+hipError_t launch_transpose(const __bf16* src, int R, int Cc, int lds, __bf16* dst, int ldo,
+                            hipStream_t st);
+int xattn_na_pad(int n_audio);
+// Forward: q [N, H 128], k, v [Na, H 128], o [N, H 128], y [N, C] bf16; lse [H, N].
+hipError_t launch_xattn_fwd(int N, int Na, int heads, const __bf16* x, const __bf16* a, int C,
+                            const __bf16* wq, const __bf16* wk, const __bf16* wv,
+                            const __bf16* wo, __bf16* q, __bf16* k, __bf16* v, __bf16* o,
+                            float* lse, __bf16* y, hipStream_t st);
+
 // Zone scoring.
 size_t zone_score_workspace(const Lay& L, int C, int n_audio);
 hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void* audio,

@@ -307,3 +307,26 @@ def attn_bwd(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, id
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def xattn_fwd(x, a, wq, wk, wv, wo, heads: int):
+    """bsa_xattn_fwd: the A2V cross-attention layer forward. x [N, C], a [Na, C],
+    wq/wk/wv [128 heads, C], wo [C, 128 heads] (bf16). Returns y [N, C] and the
+    tensors the backward takes: dict(q, k, v, o, lse)."""
+    lib = _lib.load()
+    _dev(x, a, wq, wk, wv, wo)
+    N, C = x.shape
+    Na = a.shape[0]
+    D = wq.shape[0]
+    dev = x.device
+    bf = torch.bfloat16
+    q = torch.empty((N, D), dtype=bf, device=dev)
+    k = torch.empty((Na, D), dtype=bf, device=dev)
+    v = torch.empty((Na, D), dtype=bf, device=dev)
+    o = torch.empty((N, D), dtype=bf, device=dev)
+    lse = torch.empty((heads, N), dtype=torch.float32, device=dev)
+    y = torch.empty((N, C), dtype=bf, device=dev)
+    _lib.check("bsa_xattn_fwd", lib.bsa_xattn_fwd(
+        N, Na, C, heads, D // max(1, heads), _ptr(x), _ptr(a), _ptr(wq), _ptr(wk), _ptr(wv),
+        _ptr(wo), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(y), _stream()))
+    return y, {"q": q, "k": k, "v": v, "o": o, "lse": lse}
