@@ -321,6 +321,31 @@ bsa_status bsa_xattn_fwd(int n_video, int n_audio, int C, int heads, int d, cons
                          const void* wo, void* q, void* k, void* v, void* o, float* lse, void* y,
                          void* stream);
 
+/* [host only] Workspace bytes of bsa_xattn_bwd (0 with the last error set
+ * for invalid sizes). */
+size_t bsa_xattn_bwd_workspace_size(int n_video, int n_audio, int C, int heads);
+
+/* A2V cross-attention layer, backward of bsa_xattn_fwd (same reading): the
+ * gradients of sum(Y * dY),
+ *   dO = dY Wo, dWo = dY^T O; per head P = exp(S - lse), dP = dO_h V_h^T,
+ *   D = rowsum(dO_h * O_h), dS = P (dP - D), dQ_h = dS K_h / sqrt(128),
+ *   dK_h = dS^T Q_h / sqrt(128), dV_h = P^T dO_h;
+ *   dX = dQ Wq, dWq = dQ^T X, dA = dK Wk + dV Wv, dWk = dK^T A, dWv = dV^T A.
+ * dO, dQ, dK, dV are stored as bf16 in the workspace; products accumulate in
+ * fp32; dK, dV are summed over query splits in a fixed order (deterministic).
+ *  x, a, wq, wk, wv, wo      as given to bsa_xattn_fwd
+ *  q, k, v, o, lse           bsa_xattn_fwd's outputs
+ *  dy [N, C] bf16            output gradient
+ *  dx [N, C], da [n_audio, C], dwq, dwk, dwv [D, C], dwo [C, D]   float out
+ *  ws  workspace of bsa_xattn_bwd_workspace_size(...) bytes
+ *  Sizes and alignment as bsa_xattn_fwd. */
+bsa_status bsa_xattn_bwd(int n_video, int n_audio, int C, int heads, int d, const void* x,
+                         const void* a, const void* wq, const void* wk, const void* wv,
+                         const void* wo, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dy, float* dx, float* da,
+                         float* dwq, float* dwk, float* dwv, float* dwo, void* ws,
+                         size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

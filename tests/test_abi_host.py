@@ -290,3 +290,18 @@ def test_xattn_fwd_validation(lib):
     assert call(d=64) == _lib.BSA_UNSUPPORTED
     assert call(ptr=None) == _lib.BSA_INVALID_ARG
     assert call(ptr=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG   # misaligned
+
+
+def test_xattn_bwd_validation(lib):
+    need = lib.bsa_xattn_bwd_workspace_size(1000, 200, 256, 2)
+    assert need > 0
+    assert lib.bsa_xattn_bwd_workspace_size(1000, 300, 256, 2) == 0
+
+    def call(Na=200, d=128, wsb=need, ptr=FAKE):
+        return lib.bsa_xattn_bwd(1000, Na, 256, 2, d, ptr, *([FAKE] * 9), FAKE, FAKE,
+                                 *([FAKE] * 6), FAKE, wsb, None)
+
+    assert call(Na=0) == _lib.BSA_INVALID_ARG
+    assert call(d=96) == _lib.BSA_UNSUPPORTED
+    assert call(ptr=None) == _lib.BSA_INVALID_ARG
+    assert call(wsb=need - 1) == _lib.BSA_WORKSPACE_TOO_SMALL

@@ -58,6 +58,9 @@ SIGNATURES = {
                                   ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]),
     "bsa_xattn_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int] + [vp] * 6 + [vp] * 4 + [vp, vp, vp]),
+    "bsa_xattn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "bsa_xattn_bwd": (ctypes.c_int, [ctypes.c_int] * 5 + [vp] * 10 + [vp, vp] + [vp] * 6 +
+                      [vp, ctypes.c_size_t, vp]),
     "bsa_select_causal": (ctypes.c_int, [LayoutP, vp, vp, vp, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int32, ctypes.c_double, ctypes.c_int, vp, vp,
                                          vp, vp, ctypes.c_size_t, vp]),

@@ -463,3 +463,31 @@ bsa_status bsa_xattn_fwd(int n_video, int n_audio, int C, int heads, int d, cons
                                           static_cast<hipStream_t>(stream)),
                     "xattn_fwd");
 }
+
+size_t bsa_xattn_bwd_workspace_size(int n_video, int n_audio, int C, int heads) {
+  if (check_xattn(n_video, n_audio, C, heads, 128) != BSA_OK) return 0;
+  return bsa::xattn_bwd_workspace(n_video, n_audio, C, heads);
+}
+
+bsa_status bsa_xattn_bwd(int n_video, int n_audio, int C, int heads, int d, const void* x,
+                         const void* a, const void* wq, const void* wk, const void* wv,
+                         const void* wo, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dy, float* dx, float* da,
+                         float* dwq, float* dwk, float* dwv, float* dwo, void* ws,
+                         size_t ws_bytes, void* stream) {
+  BSA_TRY(check_xattn(n_video, n_audio, C, heads, d));
+  const void* in[] = {x, a, wq, wk, wv, wo, q, k, v, o, lse, dy, dx, da, dwq, dwk, dwv, dwo};
+  for (const void* p : in)
+    if (!p) return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  for (const void* p : in)
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(BSA_INVALID_ARG, "tensors must be 16-byte aligned");
+  const size_t need = bsa::xattn_bwd_workspace(n_video, n_audio, C, heads);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_WORKSPACE_TOO_SMALL, "xattn_bwd needs %zu workspace bytes, got %zu", need, ws_bytes);
+  typedef const __bf16* cb;
+  return hip_status(bsa::launch_xattn_bwd(n_video, n_audio, heads, (cb)x, (cb)a, C, (cb)wq,
+                                          (cb)wk, (cb)wv, (cb)wo, (cb)q, (cb)k, (cb)v, (cb)o, lse,
+                                          (cb)dy, dx, da, dwq, dwk, dwv, dwo, ws,
+                                          static_cast<hipStream_t>(stream)),
+                    "xattn_bwd");
+}

@@ -23,6 +23,18 @@
 //                    LDS; per wave 32 queries, S^T = K Q^T and O^T += V^T P^T on
 //                    MFMA over 64-key chunks with an online softmax; writes O
 //                    (bf16) and lse (natural log, fp32).
+//  xattn_delta_kernel  D[h][n] = dO_h[n] . O_h[n] (fp32).
+//  xattn_bwd_dq_kernel per (256 queries, head), K_h and V_h in LDS as in the
+//                    forward: S^T = K Q^T and dP^T = V dO^T on MFMA, P = exp(S
+//                    scale - lse), dS = P (dP - D), dQ^T = K^T dS^T (K^T through
+//                    transposed LDS reads); writes dQ (bf16, scaled).
+//  xattn_bwd_dkdv_kernel per (query split, 128 keys, head): each wave keeps its
+//                    32 keys of K and V in registers; Q, dO tiles of 128
+//                    queries with their lse and D stream through LDS; S = Q K^T,
+//                    dP = dO V^T, then dV += P^T dO and dK += dS^T Q (dO and Q
+//                    through transposed LDS reads); writes fp32 partial sums per
+//                    split, which xattn_reduce_kernel adds in a fixed order
+//                    (deterministic) into bf16 dK (scaled) and dV.
 #include <math.h>
 
 #include "attn_common.hpp"
@@ -270,6 +282,253 @@ __global__ __launch_bounds__(64 * kXWaves) void xattn_fwd_kernel(
   if (hi == 0) lse[(size_t)h * N + n] = (m_run + log2f(l_tot)) * kLn2;
 }
 
+// ------------------------------------------------ cross-attention backward --
+__global__ __launch_bounds__(256) void xattn_delta_kernel(const __bf16* __restrict__ dO,
+                                                          const __bf16* __restrict__ o, int N,
+                                                          int heads, float* __restrict__ delta) {
+  // one wave per (token, head) pair group: lane covers 2 channels of one head row
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (n, h) pair
+  const int lane = threadIdx.x & 63;
+  if (item >= (long long)N * heads) return;
+  const long long n = item / heads;
+  const int h = (int)(item - n * heads);
+  const size_t base = (size_t)n * heads * kXD + h * kXD + 2 * lane;
+  float acc = (float)dO[base] * (float)o[base] + (float)dO[base + 1] * (float)o[base + 1];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) delta[(size_t)h * N + n] = acc;
+}
+
+__global__ __launch_bounds__(64 * kXWaves) void xattn_bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ delta, int N, int Na, int na_pad, int D, float scale,
+    __bf16* __restrict__ dq) {
+  __shared__ __align__(16) __bf16 sK[kXMaxNa * kXLd];
+  __shared__ __align__(16) __bf16 sV[kXMaxNa * kXLd];
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  for (int e = tid; e < na_pad * 16; e += 64 * kXWaves) {
+    const int r = e >> 4, ch = e & 15;
+    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (r < Na) {
+      kv = *reinterpret_cast<const u32x4*>(k + (size_t)r * D + h * kXD + 8 * ch);
+      vv = *reinterpret_cast<const u32x4*>(v + (size_t)r * D + h * kXD + 8 * ch);
+    }
+    *reinterpret_cast<u32x4*>(sK + r * kXLd + 8 * ch) = kv;
+    *reinterpret_cast<u32x4*>(sV + r * kXLd + 8 * ch) = vv;
+  }
+  const long long n = (long long)blockIdx.x * kXQ + 32 * w + l32;
+  const bool n_ok = n < N;
+  const long long nr = n_ok ? n : N - 1;
+  const __bf16* qrow = q + (size_t)nr * D + h * kXD + 8 * hi;
+  const __bf16* drow = dO + (size_t)nr * D + h * kXD + 8 * hi;
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    df[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s);
+  }
+  const float l2 = lse[(size_t)h * N + nr] * kLog2e;  // lse in log2 units
+  const float dn = delta[(size_t)h * N + nr];
+  const float sl2 = scale * kLog2e;
+  __syncthreads();
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  const int G = lane >> 4, u = lane & 15;
+  const int vrow = u >> 2, vcol = 16 * (G & 1) + 4 * (u & 3);
+  for (int c0 = 0; c0 < na_pad; c0 += 64) {
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = dp[t][r] = 0.f;
+      const __bf16* kr = sK + (c0 + 32 * t + l32) * kXLd + 8 * hi;
+      const __bf16* vr = sV + (c0 + 32 * t + l32) * kXLd + 8 * hi;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        s[t] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * st), qf[st], s[t]);
+        dp[t] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + 16 * st), df[st], dp[t]);
+      }
+    }
+    // dS (bf16) in the key order the dQ product takes: k-step j, slot jj =
+    // key c0 + 32 (j/2) + 16 (j%2) + 8 (jj/4) + 4 hi + jj%4
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int t = j >> 1, r = 4 * (2 * (j & 1) + (jj >> 2)) + (jj & 3);
+        const int key = c0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float p = key < Na ? exp2f(s[t][r] * sl2 - l2) : 0.f;
+        dsf[j][jj] = (__bf16)(p * (dp[t][r] - dn));
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int R = c0 + 32 * (j >> 1) + 16 * (j & 1) + 4 * hi;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const __bf16* p0 = sK + (R + vrow) * kXLd + 32 * t + vcol;
+        const bf16x4 lo = tr_read4(p0);
+        const bf16x4 up = tr_read4(p0 + 8 * kXLd);
+        acc[t] = mfma32x32x16(__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7), dsf[j],
+                              acc[t]);
+      }
+    }
+  }
+  if (!n_ok) return;
+  __bf16* orow = dq + (size_t)n * D + h * kXD + 4 * hi;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(acc[t][4 * g + i] * scale);
+      *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g) = v4;
+    }
+}
+
+constexpr int kKW = 4;             // waves of the dK/dV kernel, 32 keys each
+constexpr int kKQ = 128;           // queries per streamed tile
+
+__global__ __launch_bounds__(64 * kKW) void xattn_bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ delta, int N, int Na, int D, float scale, int splits,
+    float* __restrict__ part_k, float* __restrict__ part_v) {
+  __shared__ __align__(16) __bf16 sQ[kKQ * kXLd];
+  __shared__ __align__(16) __bf16 sD[kKQ * kXLd];
+  __shared__ float sL[kKQ], sDel[kKQ];
+  const int split = blockIdx.x, kb = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int key = 128 * kb + 32 * w + l32;  // this lane's key (B operand column)
+  const bool key_ok = key < Na;
+  // K and V fragments of the wave's 32 keys: lane holds X[key][16 s + 8 hi .. +8]
+  bf16x8 kf[8], vf[8];
+  {
+    const bf16x8 z = {};
+    const __bf16* kr = k + (size_t)(key_ok ? key : 0) * D + h * kXD + 8 * hi;
+    const __bf16* vr = v + (size_t)(key_ok ? key : 0) * D + h * kXD + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = key_ok ? *reinterpret_cast<const bf16x8*>(kr + 16 * s) : z;
+      vf[s] = key_ok ? *reinterpret_cast<const bf16x8*>(vr + 16 * s) : z;
+    }
+  }
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+  const float sl2 = scale * kLog2e;
+  const int G = lane >> 4, u = lane & 15;
+  const int trow = u >> 2, tcol = 16 * (G & 1) + 4 * (u & 3);
+  const int ntiles = (N + kKQ - 1) / kKQ;
+  for (int qt = split; qt < ntiles; qt += splits) {
+    const long long q0 = (long long)qt * kKQ;
+    __syncthreads();
+    for (int e = tid; e < kKQ * 16; e += 64 * kKW) {
+      const int r = e >> 4, ch = e & 15;
+      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
+      if (q0 + r < N) {
+        qv = *reinterpret_cast<const u32x4*>(q + (size_t)(q0 + r) * D + h * kXD + 8 * ch);
+        dv4 = *reinterpret_cast<const u32x4*>(dO + (size_t)(q0 + r) * D + h * kXD + 8 * ch);
+      }
+      *reinterpret_cast<u32x4*>(sQ + r * kXLd + 8 * ch) = qv;
+      *reinterpret_cast<u32x4*>(sD + r * kXLd + 8 * ch) = dv4;
+    }
+    for (int e = tid; e < kKQ; e += 64 * kKW) {
+      const bool ok = q0 + e < N;
+      sL[e] = ok ? lse[(size_t)h * N + q0 + e] * kLog2e : INFINITY;  // pad rows: P = 0
+      sDel[e] = ok ? delta[(size_t)h * N + q0 + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qs = 0; qs < kKQ / 32; ++qs) {
+      // S = Q K^T and dP = dO V^T for queries q0 + 32 qs .. +32 (rows) and the
+      // wave's keys (columns): lane holds query 32 qs + 8 (r/4) + 4 hi + r%4
+      f32x16 s = {}, dp = {};
+      const __bf16* qr = sQ + (32 * qs + l32) * kXLd + 8 * hi;
+      const __bf16* dr = sD + (32 * qs + l32) * kXLd + 8 * hi;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(qr + 16 * st), kf[st], s);
+        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(dr + 16 * st), vf[st], dp);
+      }
+      // P and dS (bf16) in the query order of the dV / dK products: k-step j
+      // (16 queries), slot jj = query 32 qs + 16 j + 8 (jj/4) + 4 hi + jj%4
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int r = 4 * (2 * j + (jj >> 2)) + (jj & 3);
+          const int ql = 32 * qs + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const float p = key_ok ? exp2f(s[r] * sl2 - sL[ql]) : 0.f;
+          const __bf16 pb = (__bf16)p;
+          pf[j][jj] = pb;
+          dsf[j][jj] = (__bf16)(p * (dp[r] - sDel[ql]));
+        }
+      // dV[key][d] += sum_q P[q][key] dO[q][d]; dK likewise with dS and Q:
+      // A = P^T / dS^T (lane = key), B = dO / Q columns through transposed reads
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 32 * qs + 16 * j + 4 * hi;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const __bf16* pd = sD + (R + trow) * kXLd + 32 * t + tcol;
+          const __bf16* pq = sQ + (R + trow) * kXLd + 32 * t + tcol;
+          const bf16x8 bd = __builtin_shufflevector(tr_read4(pd), tr_read4(pd + 8 * kXLd),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 bq = __builtin_shufflevector(tr_read4(pq), tr_read4(pq + 8 * kXLd),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          dv[t] = mfma32x32x16(pf[j], bd, dv[t]);
+          dk[t] = mfma32x32x16(dsf[j], bq, dk[t]);
+        }
+      }
+    }
+  }
+  // lane holds X[key 128 kb + 32 w + 8 (r/4) + 4 hi + r%4][d = 32 t + l32]:
+  // partial [split][h][key][d]
+  const size_t hbase = ((size_t)split * gridDim.z + h) * gridDim.y * 128;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 128 * kb + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const size_t off = (hbase + kr) * kXD + 32 * t + l32;
+      part_k[off] = dk[t][r];
+      part_v[off] = dv[t][r];
+    }
+}
+
+// dK, dV [Na, D] bf16 = sum over splits (fixed order) of the partials; dK scaled
+__global__ __launch_bounds__(256) void xattn_reduce_kernel(const float* __restrict__ part_k,
+                                                           const float* __restrict__ part_v,
+                                                           int splits, int heads, int kpad, int Na,
+                                                           float scale, __bf16* __restrict__ dk,
+                                                           __bf16* __restrict__ dv) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // (key, h, d)
+  const long long total = (long long)Na * heads * kXD;
+  if (i >= total) return;
+  const int d = (int)(i % kXD);
+  const int h = (int)((i / kXD) % heads);
+  const int key = (int)(i / ((long long)kXD * heads));
+  float sk = 0.f, sv = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t off = ((((size_t)sp * heads + h) * kpad) + key) * kXD + d;
+    sk += part_k[off];
+    sv += part_v[off];
+  }
+  dk[(size_t)key * heads * kXD + h * kXD + d] = (__bf16)(sk * scale);
+  dv[(size_t)key * heads * kXD + h * kXD + d] = (__bf16)sv;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(const __bf16* A, int lda, const __bf16* B, int ldb, int M, int N, int K,
@@ -310,6 +569,118 @@ hipError_t launch_xattn_fwd(int N, int Na, int heads, const __bf16* x, const __b
   e = hipGetLastError();
   if (e == hipSuccess) e = launch_gemm_nt(o, D, wo, D, N, C, D, y, C, false, false, st);
   return e;
+}
+
+namespace {
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+int up64(int x) { return 64 * ((x + 63) / 64); }
+
+// Backward workspace, in order: dO, dQ [N, D] bf16 | dK, dV [Na, D] bf16 |
+// delta [H, N] f32 | dK, dV partials [splits, H, kpad, 128] f32 | Wo^T [D, C],
+// Wq^T, Wk^T, Wv^T [C, D] bf16 | dY^T, X^T [C, Npad], O^T, dQ^T [D, Npad] bf16 |
+// A^T [C, Nap], dK^T, dV^T [D, Nap] bf16.
+struct XBwdWs {
+  int splits, kpad, npad, nap;
+  size_t off[20];
+  size_t total;
+};
+
+XBwdWs xattn_bwd_layout(int N, int Na, int C, int heads) {
+  XBwdWs w{};
+  const int D = heads * kXD;
+  w.kpad = 128 * ((Na + 127) / 128);
+  const int kblocks = w.kpad / 128;
+  const int ntiles = (N + kKQ - 1) / kKQ;
+  w.splits = (512 + heads * kblocks - 1) / (heads * kblocks);
+  if (w.splits > ntiles) w.splits = ntiles;
+  if (w.splits < 1) w.splits = 1;
+  w.npad = up64(N);
+  w.nap = up64(Na);
+  const size_t b2 = sizeof(__bf16);
+  const size_t sizes[] = {
+      (size_t)N * D * b2, (size_t)N * D * b2, (size_t)Na * D * b2, (size_t)Na * D * b2,
+      (size_t)heads * N * 4,
+      (size_t)w.splits * heads * w.kpad * kXD * 4, (size_t)w.splits * heads * w.kpad * kXD * 4,
+      (size_t)D * C * b2, (size_t)C * D * b2, (size_t)C * D * b2, (size_t)C * D * b2,
+      (size_t)C * w.npad * b2, (size_t)C * w.npad * b2, (size_t)D * w.npad * b2,
+      (size_t)D * w.npad * b2,
+      (size_t)C * w.nap * b2, (size_t)D * w.nap * b2, (size_t)D * w.nap * b2};
+  size_t o = 0;
+  for (int i = 0; i < (int)(sizeof(sizes) / sizeof(sizes[0])); ++i) {
+    w.off[i] = o;
+    o += al256(sizes[i]);
+  }
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t xattn_bwd_workspace(int N, int Na, int C, int heads) {
+  return xattn_bwd_layout(N, Na, C, heads).total;
+}
+
+hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __bf16* a, int C,
+                            const __bf16* wq, const __bf16* wk, const __bf16* wv,
+                            const __bf16* wo, const __bf16* q, const __bf16* k, const __bf16* v,
+                            const __bf16* o, const float* lse, const __bf16* dy, float* dx,
+                            float* da, float* dwq, float* dwk, float* dwv, float* dwo, void* ws,
+                            hipStream_t st) {
+  const int D = heads * kXD;
+  const XBwdWs w = xattn_bwd_layout(N, Na, C, heads);
+  char* base = static_cast<char*>(ws);
+  auto bf = [&](int i) { return reinterpret_cast<__bf16*>(base + w.off[i]); };
+  auto f32 = [&](int i) { return reinterpret_cast<float*>(base + w.off[i]); };
+  __bf16 *dO = bf(0), *dQ = bf(1), *dK = bf(2), *dV = bf(3);
+  float *delta = f32(4), *pk = f32(5), *pv = f32(6);
+  __bf16 *woT = bf(7), *wqT = bf(8), *wkT = bf(9), *wvT = bf(10);
+  __bf16 *dyT = bf(11), *xT = bf(12), *oT = bf(13), *dqT = bf(14);
+  __bf16 *aT = bf(15), *dkT = bf(16), *dvT = bf(17);
+  const float scale = 1.f / sqrtf((float)kXD);
+  hipError_t e = hipSuccess;
+#define BSA_X(call)                 \
+  do {                              \
+    e = (call);                     \
+    if (e != hipSuccess) return e;  \
+  } while (0)
+  // dO = dY Wo
+  BSA_X(launch_transpose(wo, C, D, D, woT, C, st));
+  BSA_X(launch_gemm_nt(dy, C, woT, C, N, D, C, dO, D, false, false, st));
+  // D = rowsum(dO * O); dQ; dK, dV
+  xattn_delta_kernel<<<(unsigned)(((long long)N * heads + 3) / 4), 256, 0, st>>>(dO, o, N, heads,
+                                                                                  delta);
+  BSA_X(hipGetLastError());
+  const int na_pad = xattn_na_pad(Na);
+  xattn_bwd_dq_kernel<<<dim3((N + kXQ - 1) / kXQ, heads), 64 * kXWaves, 0, st>>>(
+      q, k, v, dO, lse, delta, N, Na, na_pad, D, scale, dQ);
+  BSA_X(hipGetLastError());
+  xattn_bwd_dkdv_kernel<<<dim3(w.splits, w.kpad / 128, heads), 64 * kKW, 0, st>>>(
+      q, k, v, dO, lse, delta, N, Na, D, scale, w.splits, pk, pv);
+  BSA_X(hipGetLastError());
+  xattn_reduce_kernel<<<(unsigned)(((long long)Na * D + 255) / 256), 256, 0, st>>>(
+      pk, pv, w.splits, heads, w.kpad, Na, scale, dK, dV);
+  BSA_X(hipGetLastError());
+  // dWo = dY^T O
+  BSA_X(launch_transpose(dy, N, C, C, dyT, w.npad, st));
+  BSA_X(launch_transpose(o, N, D, D, oT, w.npad, st));
+  BSA_X(launch_gemm_nt(dyT, w.npad, oT, w.npad, C, D, w.npad, dwo, D, true, false, st));
+  // dX = dQ Wq, dWq = dQ^T X
+  BSA_X(launch_transpose(wq, D, C, C, wqT, D, st));
+  BSA_X(launch_gemm_nt(dQ, D, wqT, D, N, C, D, dx, C, true, false, st));
+  BSA_X(launch_transpose(dQ, N, D, D, dqT, w.npad, st));
+  BSA_X(launch_transpose(x, N, C, C, xT, w.npad, st));
+  BSA_X(launch_gemm_nt(dqT, w.npad, xT, w.npad, D, C, w.npad, dwq, C, true, false, st));
+  // dA = dK Wk + dV Wv, dWk = dK^T A, dWv = dV^T A
+  BSA_X(launch_transpose(wk, D, C, C, wkT, D, st));
+  BSA_X(launch_transpose(wv, D, C, C, wvT, D, st));
+  BSA_X(launch_gemm_nt(dK, D, wkT, D, Na, C, D, da, C, true, false, st));
+  BSA_X(launch_gemm_nt(dV, D, wvT, D, Na, C, D, da, C, true, true, st));
+  BSA_X(launch_transpose(a, Na, C, C, aT, w.nap, st));
+  BSA_X(launch_transpose(dK, Na, D, D, dkT, w.nap, st));
+  BSA_X(launch_transpose(dV, Na, D, D, dvT, w.nap, st));
+  BSA_X(launch_gemm_nt(dkT, w.nap, aT, w.nap, D, C, w.nap, dwk, C, true, false, st));
+  BSA_X(launch_gemm_nt(dvT, w.nap, aT, w.nap, D, C, w.nap, dwv, C, true, false, st));
+#undef BSA_X
+  return hipSuccess;
 }
 
 }  // namespace bsa

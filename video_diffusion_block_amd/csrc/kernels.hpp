@@ -88,6 +88,16 @@ hipError_t launch_xattn_fwd(int N, int Na, int heads, const __bf16* x, const __b
                             const __bf16* wo, __bf16* q, __bf16* k, __bf16* v, __bf16* o,
                             float* lse, __bf16* y, hipStream_t st);
 
+// Backward: gradients of sum(Y * dY) as fp32 (dx [N, C], da [Na, C], dwq,
+// dwk, dwv [D, C], dwo [C, D]) from the forward's q, k, v, o, lse.
+size_t xattn_bwd_workspace(int N, int Na, int C, int heads);
+hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __bf16* a, int C,
+                            const __bf16* wq, const __bf16* wk, const __bf16* wv,
+                            const __bf16* wo, const __bf16* q, const __bf16* k, const __bf16* v,
+                            const __bf16* o, const float* lse, const __bf16* dy, float* dx,
+                            float* da, float* dwq, float* dwk, float* dwv, float* dwo, void* ws,
+                            hipStream_t st);
+
 // Zone scoring.
 size_t zone_score_workspace(const Lay& L, int C, int n_audio);
 hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void* audio,

@@ -330,3 +330,31 @@ def xattn_fwd(x, a, wq, wk, wv, wo, heads: int):
         N, Na, C, heads, D // max(1, heads), _ptr(x), _ptr(a), _ptr(wq), _ptr(wk), _ptr(wv),
         _ptr(wo), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(y), _stream()))
     return y, {"q": q, "k": k, "v": v, "o": o, "lse": lse}
+
+
+def xattn_bwd(x, a, wq, wk, wv, wo, heads: int, saved: dict, dy):
+    """bsa_xattn_bwd: fp32 gradients dict(dx, da, dwq, dwk, dwv, dwo) of
+    sum(Y * dy), from the forward's saved tensors."""
+    lib = _lib.load()
+    _dev(x, a, wq, wk, wv, wo, dy)
+    N, C = x.shape
+    Na = a.shape[0]
+    D = wq.shape[0]
+    dev = x.device
+    f = torch.float32
+    out = {"dx": torch.empty((N, C), dtype=f, device=dev),
+           "da": torch.empty((Na, C), dtype=f, device=dev),
+           "dwq": torch.empty((D, C), dtype=f, device=dev),
+           "dwk": torch.empty((D, C), dtype=f, device=dev),
+           "dwv": torch.empty((D, C), dtype=f, device=dev),
+           "dwo": torch.empty((C, D), dtype=f, device=dev)}
+    nbytes = lib.bsa_xattn_bwd_workspace_size(N, Na, C, heads)
+    if nbytes == 0:
+        raise _lib.BSAError("bsa_xattn_bwd_workspace_size", _lib.BSA_INVALID_ARG)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _lib.check("bsa_xattn_bwd", lib.bsa_xattn_bwd(
+        N, Na, C, heads, D // max(1, heads), _ptr(x), _ptr(a), _ptr(wq), _ptr(wk), _ptr(wv),
+        _ptr(wo), _ptr(saved["q"]), _ptr(saved["k"]), _ptr(saved["v"]), _ptr(saved["o"]),
+        _ptr(saved["lse"]), _ptr(dy), _ptr(out["dx"]), _ptr(out["da"]), _ptr(out["dwq"]),
+        _ptr(out["dwk"]), _ptr(out["dwv"]), _ptr(out["dwo"]), _ptr(ws), nbytes, _stream()))
+    return out
