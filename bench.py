@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--reuse-every", type=int, default=1, metavar="R",
                     help="recompute zone shapes and block lists every R steps and reuse them in "
                          "between (forward-only; ms/layer is the average over the steps)")
+    ap.add_argument("--xattn", action="store_true",
+                    help="time the A2V cross-attention layer (forward + backward) at the "
+                         "workload's token count instead of the BSA layer")
     ap.add_argument("--unfused", action="store_true",
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     return ap.parse_args()
@@ -151,6 +154,67 @@ def copy_calib():
     print(json.dumps({"copy_bytes": n, "copy_GBps": 2 * n / dt / 1e9}))
 
 
+def xattn_bench(args, wl):
+    """The A2V cross-attention layer at the workload's video token count:
+    C = 1536 channels, 200 audio tokens, 12 heads of 128; seeded synthetic
+    features, weights N(0, 1/fan_in) and output gradient (no trained weights)."""
+    import numpy as np
+    import torch
+    import synth
+    from video_diffusion_block_amd import ops
+    dev = torch.device("cuda:0")
+    grid = wl.grid
+    N, C, Na, H = int(np.prod(grid)), 1536, 200, 12
+    D = 128 * H
+    rng = np.random.default_rng(11)
+
+    def bf(x):
+        return torch.from_numpy(synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+                                .view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf(synth.bf16_bits_to_f32(synth.smooth_field(1, grid, C, 4)[0]))
+    a = bf(synth.gaussian_noise((Na, C), 5))
+    w = [bf(rng.normal(size=(D, C)) / np.sqrt(C)) for _ in range(3)] + \
+        [bf(rng.normal(size=(C, D)) / np.sqrt(D))]
+    g = torch.Generator(device=dev).manual_seed(6)
+    dy = torch.randn((N, C), generator=g, device=dev).to(torch.bfloat16)
+    evs = []
+    for it in range(args.warmup + args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        y, saved = ops.xattn_fwd(x, a, *w, H)
+        e[1].record()
+        ops.xattn_bwd(x, a, *w, H, saved, dy)
+        e[2].record()
+        if it >= args.warmup:
+            evs.append(e)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    proj = 2.0 * N * C * D                       # one video-side projection GEMM
+    audio = 2.0 * Na * C * D                     # one audio-side projection GEMM
+    core = 2.0 * N * Na * D                      # one attention product (S, PV, ...)
+    fwd_fl = 2 * proj + 2 * audio + 2 * core     # Q, Y; K, V; S, PV
+    bwd_fl = 4 * proj + 4 * audio + 7 * core     # dO, dWo, dX, dWq; dA x2, dWk, dWv;
+    #                                              dQ pass: S, dP, dQ; dK/dV pass: S, dP, dV, dK
+    res = {
+        "metric": "A2V cross-attention layer ms (forward + backward) and executed TFLOP/s",
+        "value": round((fwd_fl + bwd_fl) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (executed FLOPs per layer time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(fwd_ms + bwd_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded features, weights, dY)",
+        "config": {"workload": f"xattn-{wl.name}", "video_tokens": N, "audio_tokens": Na,
+                   "channels": C, "heads": H, "d": 128},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_TFLOPs": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_TFLOPs": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * (fwd_fl + bwd_fl) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+                               / PEAK_BF16_TFLOPS, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,6 +232,9 @@ def main():
         return
 
     wl = synth.WORKLOADS[args.workload]
+    if args.xattn:
+        xattn_bench(args, wl)
+        return
     if args.causal_frames and args.unfused:
         sys.exit("--causal-frames selects from the gather's block means; it does not combine "
                  "with --unfused")

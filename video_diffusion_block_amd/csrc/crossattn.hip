@@ -37,6 +37,8 @@
 //                    (deterministic) into bf16 dK (scaled) and dV.
 #include <math.h>
 
+#include <algorithm>
+
 #include "attn_common.hpp"
 #include "kernels.hpp"
 
@@ -57,10 +59,13 @@ constexpr int kGThreads = 256;                 // 4 waves, 2 x 2, 64 x 64 each
 
 __device__ inline int gswz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// Split-K (kchunk > 0): workgroup z covers k in [z kchunk, (z + 1) kchunk) and
+// writes its fp32 partial tile to C + z M ldc (kOutF32, no kAccum).
 template <bool kOutF32, bool kAccum>
 __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const __bf16* __restrict__ A, int lda,
                                                           const __bf16* __restrict__ B, int ldb,
-                                                          int M, int N, int K, void* C, int ldc) {
+                                                          int M, int N, int K, void* C, int ldc,
+                                                          int kchunk) {
   __shared__ __align__(16) __bf16 sA[2][kGM * kGK];
   __shared__ __align__(16) __bf16 sB[2][kGN * kGK];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -70,14 +75,15 @@ __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const __bf16* __rest
   // loader: chunk e = tid + 256 u (u = 0..3) of a tile: row e / 8, chunk e % 8
   u32x4 ra[4], rb[4];
   const u32x4 z4 = {0u, 0u, 0u, 0u};
+  int klim = K;  // loads past klim read zero (the end of this workgroup's k range)
   auto gload = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = tid + kGThreads * u, r = e >> 3, ch = e & 7;
       const int k = k0 + 8 * ch;
-      ra[u] = (m0 + r < M && k < K)
+      ra[u] = (m0 + r < M && k < klim)
                   ? *reinterpret_cast<const u32x4*>(A + (size_t)(m0 + r) * lda + k) : z4;
-      rb[u] = (n0 + r < N && k < K)
+      rb[u] = (n0 + r < N && k < klim)
                   ? *reinterpret_cast<const u32x4*>(B + (size_t)(n0 + r) * ldb + k) : z4;
     }
   };
@@ -96,13 +102,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const __bf16* __rest
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  const int nk = (K + kGK - 1) / kGK;
-  gload(0);
+  const int kbeg = kchunk > 0 ? blockIdx.z * kchunk : 0;
+  const int kend = kchunk > 0 ? min(K, kbeg + kchunk) : K;
+  const int nk = kend > kbeg ? (kend - kbeg + kGK - 1) / kGK : 0;
+  klim = kend;
+  if (kchunk > 0) C = static_cast<float*>(C) + (size_t)blockIdx.z * M * ldc;
+  gload(kbeg);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kGK);
+    if (kt + 1 < nk) gload(kbeg + (kt + 1) * kGK);
 #pragma unroll
     for (int s = 0; s < kGK / 16; ++s) {
       bf16x8 af[2], bf[2];
@@ -286,17 +296,24 @@ __global__ __launch_bounds__(64 * kXWaves) void xattn_fwd_kernel(
 __global__ __launch_bounds__(256) void xattn_delta_kernel(const __bf16* __restrict__ dO,
                                                           const __bf16* __restrict__ o, int N,
                                                           int heads, float* __restrict__ delta) {
-  // one wave per (token, head) pair group: lane covers 2 channels of one head row
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (n, h) pair
-  const int lane = threadIdx.x & 63;
-  if (item >= (long long)N * heads) return;
-  const long long n = item / heads;
-  const int h = (int)(item - n * heads);
-  const size_t base = (size_t)n * heads * kXD + h * kXD + 2 * lane;
-  float acc = (float)dO[base] * (float)o[base] + (float)dO[base + 1] * (float)o[base + 1];
+  // 16 lanes per (token, head) row of 128 channels, 8 channels (16 bytes) each
+  const long long item = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;  // (n, h) row
+  const int c = threadIdx.x & 15;
+  const bool ok = item < (long long)N * heads;
+  const long long it = ok ? item : 0;
+  const size_t base = (size_t)it * kXD + 8 * c;  // rows of D = heads * 128 are contiguous
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(dO + base);
+  const bf16x8 b = *reinterpret_cast<const bf16x8*>(o + base);
+  float acc = 0.f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) delta[(size_t)h * N + n] = acc;
+  for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (ok && c == 0) {
+    const long long n = it / heads;
+    const int h = (int)(it - n * heads);
+    delta[(size_t)h * N + n] = acc;
+  }
 }
 
 __global__ __launch_bounds__(64 * kXWaves) void xattn_bwd_dq_kernel(
@@ -535,11 +552,49 @@ hipError_t launch_gemm_nt(const __bf16* A, int lda, const __bf16* B, int ldb, in
                           void* C, int ldc, bool out_f32, bool accumulate, hipStream_t st) {
   dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM);
   if (!out_f32)
-    gemm_nt_kernel<false, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc);
+    gemm_nt_kernel<false, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc, 0);
   else if (accumulate)
-    gemm_nt_kernel<true, true><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc);
+    gemm_nt_kernel<true, true><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc, 0);
   else
-    gemm_nt_kernel<true, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc);
+    gemm_nt_kernel<true, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc, 0);
+  return hipGetLastError();
+}
+
+namespace {
+// out[m][n] = sum over z (in order) of part[z][m][n]
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int M, int N,
+                                                            float* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)M * N;
+  if (i >= total) return;
+  float sum = 0.f;
+  for (int z = 0; z < splits; ++z) sum += part[(size_t)z * total + i];
+  out[i] = sum;
+}
+}  // namespace
+
+int gemm_splitk_splits(int M, int N, int K) {
+  const int tiles = ((M + kGM - 1) / kGM) * ((N + kGN - 1) / kGN);
+  int s = (512 + tiles - 1) / tiles;
+  const int kmax = (K + kGK - 1) / kGK;  // at least one k step per split
+  if (s > kmax) s = kmax;
+  return s < 1 ? 1 : s;
+}
+
+// fp32 C[M, N] (row stride N) = A B^T with the k range split over
+// gemm_splitk_splits(M, N, K) workgroup layers; part holds splits x M x N floats.
+hipError_t launch_gemm_nt_splitk(const __bf16* A, int lda, const __bf16* B, int ldb, int M, int N,
+                                 int K, float* C, float* part, hipStream_t st) {
+  const int splits = gemm_splitk_splits(M, N, K);
+  const int kchunk = kGK * (((K + kGK - 1) / kGK + splits - 1) / splits);
+  dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, splits);
+  gemm_nt_kernel<true, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, part, N,
+                                                          kchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  splitk_reduce_kernel<<<(unsigned)(((long long)M * N + 255) / 256), 256, 0, st>>>(part, splits, M,
+                                                                                N, C);
   return hipGetLastError();
 }
 
@@ -578,9 +633,10 @@ int up64(int x) { return 64 * ((x + 63) / 64); }
 // Backward workspace, in order: dO, dQ [N, D] bf16 | dK, dV [Na, D] bf16 |
 // delta [H, N] f32 | dK, dV partials [splits, H, kpad, 128] f32 | Wo^T [D, C],
 // Wq^T, Wk^T, Wv^T [C, D] bf16 | dY^T, X^T [C, Npad], O^T, dQ^T [D, Npad] bf16 |
-// A^T [C, Nap], dK^T, dV^T [D, Nap] bf16.
+// A^T [C, Nap], dK^T, dV^T [D, Nap] bf16 | split-K partials of the weight
+// gradients over the tokens [ksplits, C D] f32.
 struct XBwdWs {
-  int splits, kpad, npad, nap;
+  int splits, kpad, npad, nap, ksplits;
   size_t off[20];
   size_t total;
 };
@@ -596,6 +652,7 @@ XBwdWs xattn_bwd_layout(int N, int Na, int C, int heads) {
   if (w.splits < 1) w.splits = 1;
   w.npad = up64(N);
   w.nap = up64(Na);
+  w.ksplits = std::max(gemm_splitk_splits(C, D, w.npad), gemm_splitk_splits(D, C, w.npad));
   const size_t b2 = sizeof(__bf16);
   const size_t sizes[] = {
       (size_t)N * D * b2, (size_t)N * D * b2, (size_t)Na * D * b2, (size_t)Na * D * b2,
@@ -604,7 +661,8 @@ XBwdWs xattn_bwd_layout(int N, int Na, int C, int heads) {
       (size_t)D * C * b2, (size_t)C * D * b2, (size_t)C * D * b2, (size_t)C * D * b2,
       (size_t)C * w.npad * b2, (size_t)C * w.npad * b2, (size_t)D * w.npad * b2,
       (size_t)D * w.npad * b2,
-      (size_t)C * w.nap * b2, (size_t)D * w.nap * b2, (size_t)D * w.nap * b2};
+      (size_t)C * w.nap * b2, (size_t)D * w.nap * b2, (size_t)D * w.nap * b2,
+      (size_t)w.ksplits * C * D * 4};
   size_t o = 0;
   for (int i = 0; i < (int)(sizeof(sizes) / sizeof(sizes[0])); ++i) {
     w.off[i] = o;
@@ -635,6 +693,7 @@ hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __b
   __bf16 *woT = bf(7), *wqT = bf(8), *wkT = bf(9), *wvT = bf(10);
   __bf16 *dyT = bf(11), *xT = bf(12), *oT = bf(13), *dqT = bf(14);
   __bf16 *aT = bf(15), *dkT = bf(16), *dvT = bf(17);
+  float* kpart = f32(18);
   const float scale = 1.f / sqrtf((float)kXD);
   hipError_t e = hipSuccess;
 #define BSA_X(call)                 \
@@ -646,8 +705,8 @@ hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __b
   BSA_X(launch_transpose(wo, C, D, D, woT, C, st));
   BSA_X(launch_gemm_nt(dy, C, woT, C, N, D, C, dO, D, false, false, st));
   // D = rowsum(dO * O); dQ; dK, dV
-  xattn_delta_kernel<<<(unsigned)(((long long)N * heads + 3) / 4), 256, 0, st>>>(dO, o, N, heads,
-                                                                                  delta);
+  xattn_delta_kernel<<<(unsigned)(((long long)N * heads * 16 + 255) / 256), 256, 0, st>>>(
+      dO, o, N, heads, delta);
   BSA_X(hipGetLastError());
   const int na_pad = xattn_na_pad(Na);
   xattn_bwd_dq_kernel<<<dim3((N + kXQ - 1) / kXQ, heads), 64 * kXWaves, 0, st>>>(
@@ -662,13 +721,13 @@ hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __b
   // dWo = dY^T O
   BSA_X(launch_transpose(dy, N, C, C, dyT, w.npad, st));
   BSA_X(launch_transpose(o, N, D, D, oT, w.npad, st));
-  BSA_X(launch_gemm_nt(dyT, w.npad, oT, w.npad, C, D, w.npad, dwo, D, true, false, st));
+  BSA_X(launch_gemm_nt_splitk(dyT, w.npad, oT, w.npad, C, D, w.npad, dwo, kpart, st));
   // dX = dQ Wq, dWq = dQ^T X
   BSA_X(launch_transpose(wq, D, C, C, wqT, D, st));
   BSA_X(launch_gemm_nt(dQ, D, wqT, D, N, C, D, dx, C, true, false, st));
   BSA_X(launch_transpose(dQ, N, D, D, dqT, w.npad, st));
   BSA_X(launch_transpose(x, N, C, C, xT, w.npad, st));
-  BSA_X(launch_gemm_nt(dqT, w.npad, xT, w.npad, D, C, w.npad, dwq, C, true, false, st));
+  BSA_X(launch_gemm_nt_splitk(dqT, w.npad, xT, w.npad, D, C, w.npad, dwq, kpart, st));
   // dA = dK Wk + dV Wv, dWk = dK^T A, dWv = dV^T A
   BSA_X(launch_transpose(wk, D, C, C, wkT, D, st));
   BSA_X(launch_transpose(wv, D, C, C, wvT, D, st));
