@@ -155,6 +155,105 @@ __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const __bf16* __rest
     }
 }
 
+// Large-shape variant: 256 x 256 block tile, 8 waves of 64 x 128 (2 x 4 MFMA
+// tiles, 8 products per 6 fragment reads), operands copied global -> LDS by
+// direct buffer loads (the XOR swizzle applied on the fetch side: LDS slot s of
+// a tile holds row s / 8, logical chunk (s % 8) ^ (row % 8)); rows past M or N
+// read zero through the buffer bounds. Needs K % 64 == 0 and each operand's
+// rows below 2^31 bytes from the tile's first row.
+constexpr int kBM = 256, kBN = 256;
+constexpr int kBThreads = 512;
+
+template <bool kOutF32, bool kAccum>
+__global__ __launch_bounds__(kBThreads) void gemm_nt_big_kernel(
+    const __bf16* __restrict__ A, int lda, const __bf16* __restrict__ B, int ldb, int M, int N,
+    int K, void* C, int ldc, int kchunk) {
+  __shared__ __align__(16) __bf16 sA[2][kBM * kGK];
+  __shared__ __align__(16) __bf16 sB[2][kBN * kGK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int wm = w >> 1, wn = w & 1;  // rows 64 wm .., columns 128 wn ..
+  const uint32_t abytes = (uint32_t)std::min<long long>((long long)(M - m0) * lda * 2, 0x7fffffffLL);
+  const uint32_t bbytes = (uint32_t)std::min<long long>((long long)(N - n0) * ldb * 2, 0x7fffffffLL);
+  const i32x4 ars = make_buffer_rsrc(A + (size_t)m0 * lda, abytes);
+  const i32x4 brs = make_buffer_rsrc(B + (size_t)n0 * ldb, bbytes);
+  // this lane's slots: unit u = w + 8 j (j = 0..3) of each tile, slot 64 u + lane
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = 64 * (w + 8 * j) + lane, r = sl >> 3, ch = (sl & 7) ^ (r & 7);
+    aoff[j] = (r * lda + 8 * ch) * 2;
+    boff[j] = (r * ldb + 8 * ch) * 2;
+  }
+  const int kbeg = kchunk > 0 ? blockIdx.z * kchunk : 0;
+  const int kend = kchunk > 0 ? min(K, kbeg + kchunk) : K;
+  const int nk = kend > kbeg ? (kend - kbeg) / kGK : 0;
+  if (kchunk > 0) C = static_cast<float*>(C) + (size_t)blockIdx.z * M * ldc;
+  auto issue = [&](int kt, int buf) {
+    const int kb = (kbeg + kt * kGK) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = w + 8 * j;
+      dma16_manual(ars, lds_addr_of(&sA[buf][u * 64 * 8]), aoff[j], kb);
+      dma16_manual(brs, lds_addr_of(&sB[buf][u * 64 * 8]), boff[j], kb);
+    }
+  };
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  if (nk > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+#pragma unroll
+    for (int s = 0; s < kGK / 16; ++s) {
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int r = 64 * wm + 32 * a + l32;
+        af[a] = *reinterpret_cast<const bf16x8*>(&sA[buf][r * kGK + 8 * gswz(r, 2 * s + hi)]);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = 128 * wn + 32 * b + l32;
+        bf[b] = *reinterpret_cast<const bf16x8*>(&sB[buf][r * kGK + 8 * gswz(r, 2 * s + hi)]);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(af[a], bf[b], acc[a][b]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next stage has landed
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = n0 + 128 * wn + 32 * b + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (m >= M) continue;
+        if constexpr (kOutF32) {
+          float* c = static_cast<float*>(C) + (size_t)m * ldc + n;
+          *c = kAccum ? *c + acc[a][b][r] : acc[a][b][r];
+        } else {
+          static_cast<__bf16*>(C)[(size_t)m * ldc + n] = (__bf16)acc[a][b][r];
+        }
+      }
+    }
+}
+
 // -------------------------------------------------------------- transpose --
 __global__ __launch_bounds__(256) void transpose_kernel(const __bf16* __restrict__ src, int R,
                                                         int Cc, int lds, __bf16* __restrict__ dst,
@@ -548,8 +647,31 @@ __global__ __launch_bounds__(256) void xattn_reduce_kernel(const float* __restri
 
 }  // namespace
 
+namespace {
+// the 256 x 256 kernel: operands within its 32-bit buffer offsets and K whole
+// 64-deep steps
+bool big_ok(int M, int N, int K, int lda, int ldb) {
+  return M >= kBM && N >= kBN && K % kGK == 0 && (long long)M * lda * 2 < (1LL << 31) &&
+         (long long)N * ldb * 2 < (1LL << 31);
+}
+int big_tiles(int M, int N) { return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+}  // namespace
+
 hipError_t launch_gemm_nt(const __bf16* A, int lda, const __bf16* B, int ldb, int M, int N, int K,
                           void* C, int ldc, bool out_f32, bool accumulate, hipStream_t st) {
+  if (big_ok(M, N, K, lda, ldb) && big_tiles(M, N) >= 128) {
+    dim3 bgrid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM);
+    if (!out_f32)
+      gemm_nt_big_kernel<false, false><<<bgrid, kBThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C,
+                                                                    ldc, 0);
+    else if (accumulate)
+      gemm_nt_big_kernel<true, true><<<bgrid, kBThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc,
+                                                                  0);
+    else
+      gemm_nt_big_kernel<true, false><<<bgrid, kBThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C,
+                                                                   ldc, 0);
+    return hipGetLastError();
+  }
   dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM);
   if (!out_f32)
     gemm_nt_kernel<false, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, C, ldc, 0);
@@ -575,7 +697,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }  // namespace
 
 int gemm_splitk_splits(int M, int N, int K) {
-  const int tiles = ((M + kGM - 1) / kGM) * ((N + kGN - 1) / kGN);
+  // (operand strides equal K here: the transposed token-major operands)
+  const int tiles = big_ok(M, N, K, K, K) ? big_tiles(M, N)
+                                          : ((M + kGM - 1) / kGM) * ((N + kGN - 1) / kGN);
   int s = (512 + tiles - 1) / tiles;
   const int kmax = (K + kGK - 1) / kGK;  // at least one k step per split
   if (s > kmax) s = kmax;
@@ -588,9 +712,15 @@ hipError_t launch_gemm_nt_splitk(const __bf16* A, int lda, const __bf16* B, int 
                                  int K, float* C, float* part, hipStream_t st) {
   const int splits = gemm_splitk_splits(M, N, K);
   const int kchunk = kGK * (((K + kGK - 1) / kGK + splits - 1) / splits);
-  dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, splits);
-  gemm_nt_kernel<true, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, part, N,
-                                                          kchunk);
+  if (big_ok(M, N, K, lda, ldb)) {
+    dim3 bgrid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM, splits);
+    gemm_nt_big_kernel<true, false><<<bgrid, kBThreads, 0, st>>>(A, lda, B, ldb, M, N, K, part,
+                                                                 N, kchunk);
+  } else {
+    dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, splits);
+    gemm_nt_kernel<true, false><<<grid, kGThreads, 0, st>>>(A, lda, B, ldb, M, N, K, part, N,
+                                                            kchunk);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   splitk_reduce_kernel<<<(unsigned)(((long long)M * N + 255) / 256), 256, 0, st>>>(part, splits, M,
