@@ -38,6 +38,21 @@ __device__ inline f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Work item of a workgroup of a 2-D grid (x fastest), in an L2-aware order:
+// workgroups are handed to the 8 XCDs round-robin (dispatch b runs on XCD
+// b % 8, each XCD with its own L2), so inside every window of 256 dispatches
+// XCD x takes 32 consecutive items. Neighbouring blocks of one head, whose
+// block lists overlap, then share an L2, and the window keeps all XCDs on
+// nearby items. A bijection on [0, T); the last partial window is in order.
+__device__ inline void xcd_item(int& x, int& y) {
+  const int T = gridDim.x * gridDim.y;
+  const int b = blockIdx.x + gridDim.x * blockIdx.y;
+  int item = b;
+  if (b < (T / 256) * 256) item = (b & ~255) + (b & 7) * 32 + ((b >> 3) & 31);
+  x = item % gridDim.x;
+  y = item / gridDim.x;
+}
+
 // ---- direct global -> LDS loads through a buffer resource -------------------
 // The buffer form (buffer_load_dwordx4 ... lds) is counted by vmcnt only; the
 // flat/global form is also treated by the compiler as a possible LDS access of

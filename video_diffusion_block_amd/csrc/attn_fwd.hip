@@ -252,7 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB
   __shared__ int32_t sL[kMaxList];               // the row's key-block list (16 KB)
   __shared__ __align__(16) uint32_t sM[2][64];   // block facts of blocks j, j+1 (8 copies each)
-  const int i = blockIdx.x, h = blockIdx.y;
+  int i, h;  // (query block, head)
+  xcd_item(i, h);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = w & 3, kh = w >> 2;
