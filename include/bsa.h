@@ -291,6 +291,7 @@ bsa_status bsa_attn_fwd_raster(const bsa_layout* L, const int32_t* zone_shape, c
  *              (pad query slots must be zero, as bsa_permute writes them)
  *  dqp, dkp, dvp [heads, Np, d] float32 out, whatever `dtype` is (gradients
  *              are accumulated and returned in fp32); pad slots get zeros.
+ *  qp, kp, vp, op, dop must be 16-byte aligned (BSA_INVALID_ARG otherwise).
  *  The key-major (transposed) lists are built in the workspace. */
 bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
                         const void* kp, const void* vp, const void* op, const void* dop,

@@ -152,11 +152,12 @@ def test_attn_fwd_raster_validation(lib):
 def test_attn_bwd_validation(lib):
     c = LAY.c()
 
-    def call(dq=FAKE, wsb=1 << 40, d=128):
-        return lib.bsa_attn_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    def call(dq=FAKE, wsb=1 << 40, d=128, op=FAKE):
+        return lib.bsa_attn_bwd(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, op, FAKE, FAKE, FAKE,
                                 FAKE, 2, d, 1, 0.0, dq, FAKE, FAKE, FAKE, wsb, None)
 
     assert call(dq=None) == _lib.BSA_INVALID_ARG
+    assert call(op=ctypes.c_void_p(0x1004)) == _lib.BSA_INVALID_ARG   # misaligned
     assert call(wsb=1) == _lib.BSA_WORKSPACE_TOO_SMALL
     assert call(d=48) == _lib.BSA_UNSUPPORTED
 

@@ -422,6 +422,9 @@ bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const v
   if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
   if (!qp || !kp || !vp || !op || !dop || !lse || !counts || !idx || !dqp || !dkp || !dvp)
     return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  for (const void* p : {qp, kp, vp, op, dop})
+    if (reinterpret_cast<uintptr_t>(p) % 16)
+      return fail(BSA_INVALID_ARG, "qp, kp, vp, op, dop must be 16-byte aligned");
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
   if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");

@@ -20,16 +20,31 @@ namespace bsa {
 namespace {
 
 // ------------------------------------------------------ D = rowsum(dO * O) --
+// G = d / (elements per 16 bytes) lanes per row (8, 16 or 32), one 16-byte
+// chunk of O and dO each; the row sum is a shuffle reduction inside the group.
 template <typename T>
 __global__ __launch_bounds__(256) void delta_kernel(const T* op, const T* dop, int d,
                                                     long long rows, float* delta) {
-  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= rows) return;
+  constexpr int EPC = 16 / sizeof(T);
+  const int G = d / EPC;
+  const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / G;
+  const int c = threadIdx.x % G;
+  const bool ok = r < rows;
+  const size_t base = (size_t)(ok ? r : 0) * d + (size_t)c * EPC;
   float acc = 0.f;
-  for (int e = lane; e < d; e += 64) acc += to_f32(op[r * d + e]) * to_f32(dop[r * d + e]);
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) delta[r] = acc;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(op + base);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dop + base);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(op + base);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(dop + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += a[i] * b[i];
+  }
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (ok && c == 0) delta[r] = acc;
 }
 
 // ------------------------------------------------ list transpose (CSR->CSC) --
@@ -714,7 +729,8 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   BlockMeta* meta = reinterpret_cast<BlockMeta*>(p);
 
   const long long rows = (long long)heads * L.Np;
-  const unsigned dgrid = (unsigned)((rows + 3) / 4);
+  const int lanes_per_row = d * (bf16 ? 2 : 4) / 16;
+  const unsigned dgrid = (unsigned)((rows * lanes_per_row + 255) / 256);
   if (bf16)
     delta_kernel<__bf16><<<dgrid, 256, 0, st>>>(static_cast<const __bf16*>(op),
                                                   static_cast<const __bf16*>(dop), d, rows, delta);
