@@ -27,7 +27,8 @@
 //  xattn_bwd_dq_kernel per (256 queries, head), K_h and V_h in LDS as in the
 //                    forward: S^T = K Q^T and dP^T = V dO^T on MFMA, P = exp(S
 //                    scale - lse), dS = P (dP - D), dQ^T = K^T dS^T (K^T through
-//                    transposed LDS reads); writes dQ (bf16, scaled).
+//                    transposed LDS reads); writes dQ (bf16, scaled) and its
+//                    transpose (the dWq product's operand).
 //  xattn_bwd_dkdv_kernel per (query split, 128 keys, head): each wave keeps its
 //                    32 keys of K and V in registers; Q, dO tiles of 128
 //                    queries with their lse and D stream through LDS; S = Q K^T,
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(64 * kXWaves) void xattn_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ delta, int N, int Na, int na_pad, int D, float scale,
-    __bf16* __restrict__ dq) {
+    __bf16* __restrict__ dq, __bf16* __restrict__ dqT, int npad) {
   __shared__ __align__(16) __bf16 sK[kXMaxNa * kXLd];
   __shared__ __align__(16) __bf16 sV[kXMaxNa * kXLd];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -494,6 +495,17 @@ __global__ __launch_bounds__(64 * kXWaves) void xattn_bwd_dq_kernel(
                               acc[t]);
       }
     }
+  }
+  // dQ^T [D, npad] too (the dWq product's operand): lane holds column n,
+  // rows h d + 32 t + 8 g + 4 hi + i; columns N .. npad - 1 get zeros
+  if (n < npad) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dd = h * kXD + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+        dqT[(size_t)dd * npad + n] = n_ok ? (__bf16)(acc[t][r] * scale) : (__bf16)0.f;
+      }
   }
   if (!n_ok) return;
   __bf16* orow = dq + (size_t)n * D + h * kXD + 4 * hi;
@@ -840,7 +852,7 @@ hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __b
   BSA_X(hipGetLastError());
   const int na_pad = xattn_na_pad(Na);
   xattn_bwd_dq_kernel<<<dim3((N + kXQ - 1) / kXQ, heads), 64 * kXWaves, 0, st>>>(
-      q, k, v, dO, lse, delta, N, Na, na_pad, D, scale, dQ);
+      q, k, v, dO, lse, delta, N, Na, na_pad, D, scale, dQ, dqT, w.npad);
   BSA_X(hipGetLastError());
   xattn_bwd_dkdv_kernel<<<dim3(w.splits, w.kpad / 128, heads), 64 * kKW, 0, st>>>(
       q, k, v, dO, lse, delta, N, Na, D, scale, w.splits, pk, pv);
@@ -855,7 +867,6 @@ hipError_t launch_xattn_bwd(int N, int Na, int heads, const __bf16* x, const __b
   // dX = dQ Wq, dWq = dQ^T X
   BSA_X(launch_transpose(wq, D, C, C, wqT, D, st));
   BSA_X(launch_gemm_nt(dQ, D, wqT, D, N, C, D, dx, C, true, false, st));
-  BSA_X(launch_transpose(dQ, N, D, D, dqT, w.npad, st));
   BSA_X(launch_transpose(x, N, C, C, xT, w.npad, st));
   BSA_X(launch_gemm_nt_splitk(dqT, w.npad, xT, w.npad, D, C, w.npad, dwq, kpart, st));
   // dA = dK Wk + dV Wv, dWk = dK^T A, dWv = dV^T A
