@@ -9,8 +9,16 @@ from .ops import (  # noqa: F401
     BSALayout,
     attn_bwd,
     attn_fwd,
+    attn_fwd_raster,
     permute,
+    permute_norm_rope,
+    permute_pool,
     pool_select,
+    select,
+    select_causal,
     unpermute,
+    xattn_bwd,
+    xattn_fwd,
     zone_score,
 )
+from .schedule import ReusedSelection, refresh_steps  # noqa: F401
