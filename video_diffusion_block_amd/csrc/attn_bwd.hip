@@ -413,12 +413,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     asm volatile("s_barrier" ::: "memory");
   }
   // sum the two key halves (waves w and w+4 share their 32 queries)
-  float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;
+  // element e of lane (qg, lane) at xo[256 e]: conflict-free accesses
+  float* xo = reinterpret_cast<float*>(&sK[0][0]) + qg * 64 + lane;
   if (kh == 1) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[16 * t + r] = acc[t][r];
+      for (int r = 0; r < 16; ++r) xo[256 * (16 * t + r)] = acc[t][r];
   }
   __syncthreads();
   if (kh == 0) {
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
         f32x4 v;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          v[rr] = q_real ? (acc[t][4 * g + rr] + xo[16 * t + 4 * g + rr]) * scale : 0.f;
+          v[rr] = q_real ? (acc[t][4 * g + rr] + xo[256 * (16 * t + 4 * g + rr)]) * scale : 0.f;
         *reinterpret_cast<f32x4*>(out + 32 * t + 8 * g + 4 * hi) = v;
       }
   }

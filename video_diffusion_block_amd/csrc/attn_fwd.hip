@@ -487,19 +487,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 
   // merge the two key halves (waves w and w+4 share their 32 queries)
   l_run = pair_sum(l_run);
-  float* xo = reinterpret_cast<float*>(&sK[0][0]) + (qg * 64 + lane) * 64;  // 64 KB
-  float* xm = reinterpret_cast<float*>(&sV[0][0]) + (qg * 64 + lane) * 2;
+  // element e of lane (qg, lane) at xo[256 e] (64 KB), so that the 64 lanes of
+  // each access hit 64 consecutive words (no bank conflicts)
+  float* xo = reinterpret_cast<float*>(&sK[0][0]) + qg * 64 + lane;
+  float* xm = reinterpret_cast<float*>(&sV[0][0]) + qg * 64 + lane;
   if (kh == 1) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[16 * t + r] = o[t][r];
+      for (int r = 0; r < 16; ++r) xo[256 * (16 * t + r)] = o[t][r];
     xm[0] = m_run;
-    xm[1] = l_run;
+    xm[256] = l_run;
   }
   __syncthreads();
   if (kh == 0 && o_real) {
-    const float m2 = xm[0], l2 = xm[1];
+    const float m2 = xm[0], l2 = xm[256];
     const float mt = fmaxf(m_run, m2);
     const float mu = mt == -INFINITY ? 0.f : mt;
     const float a1 = exp2_fast(m_run - mu), a2 = exp2_fast(m2 - mu);
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int r = 4 * g + rr;
-          v[rr] = (__bf16)((o[t][r] * a1 + xo[16 * t + r] * a2) * inv);
+          v[rr] = (__bf16)((o[t][r] * a1 + xo[256 * (16 * t + r)] * a2) * inv);
         }
         *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * hi) = v;
       }
