@@ -248,20 +248,27 @@ def test_select_causal(wl, mult):
         assert np.abs(to_f64(o_r) - o_ref).max() <= F32_TOL
 
 
-def test_select_causal_full_size():
-    """720p (fixed 2x8x8 blocks, 40 heads) with 4-frame chunks: lists in full
-    against the causal oracle."""
-    wl = synth.WORKLOADS["720p"]
-    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+@pytest.mark.parametrize("name", ["720p", "1080p"])
+def test_select_causal_full_size(name):
+    """720p (fixed 2x8x8 blocks, 40 heads) and 1080p (dynamic zones from the
+    GPU's zone scoring, 10 heads) with 4-frame chunks: lists in full against
+    the causal oracle."""
+    wl = synth.WORKLOADS[name]
+    parts = ("q", "k", "v") + (("video", "audio") if wl.mode == "dynamic" else ())
+    inp = synth.make_inputs(wl, parts=parts)
     lay = layout_of(wl)
     L = oracle_layout(wl)
-    zs = np.zeros(L.n_zones, dtype=np.int32)
-    zs_dev = torch.as_tensor(zs).cuda()
+    if wl.mode == "dynamic":
+        zs_dev = ops.zone_score(lay, to_dev(inp["video"], "bf16"), to_dev(inp["audio"], "bf16"))
+        zs = zs_dev.cpu().numpy()
+    else:
+        zs = np.zeros(L.n_zones, dtype=np.int32)
+        zs_dev = torch.as_tensor(zs).cuda()
     q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
-    print("\n[720p causal] gpu", flush=True)
+    print(f"\n[{name} causal] gpu", flush=True)
     _, (qbar, kbar) = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
     counts, idx = ops.select_causal(lay, zs_dev, qbar, kbar, wl.sparsity_1e4, wl.tau, 4)
-    print("[720p causal] oracle", flush=True)
+    print(f"[{name} causal] oracle", flush=True)
     qf, kf = (host_f64(inp[p], wl.dtype) for p in "qk")
     r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, wl.sparsity_1e4, wl.tau,
                             zone_shape=zs)
@@ -271,8 +278,8 @@ def test_select_causal_full_size():
     exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], wl.sparsity_1e4,
                                          wl.tau, gpu_lists(counts, idx), want, visible=vis)
     assert not fails, fails[:3]
-    print(f"[720p causal] {exact} exact, {exempt} tie-exempt rows; mean list "
-          f"{n.mean():.1f} (non-causal k = 63)", flush=True)
+    print(f"[{name} causal] {exact} exact, {exempt} tie-exempt rows; mean list "
+          f"{n[:, r['counts'] > 0].mean():.1f}", flush=True)
 
 
 def test_reused_selection_schedule():
