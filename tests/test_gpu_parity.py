@@ -319,6 +319,45 @@ def test_reused_selection_schedule():
         prev = layer.idx
 
 
+@pytest.mark.parametrize("S,tau", [(0, 0.2), (8500, 1.0), (9999, 0.2), (9999, 1e-9)])
+def test_select_degenerate_settings(S, tau):
+    """The selection at its edges on a ragged dynamic grid with empty blocks:
+    sparsity 0 lists every non-empty block; tau = 1 asks for the whole mass
+    (where the rounded prefix sum first reaches 1 depends on the summation
+    order once the tail probabilities fall below fp64 resolution, so the lists
+    are held to the near-tie rule like any CDF crossing); S = 9999 gives k = 1
+    (the list is the CDF prefix); a tiny tau makes m = 1. Lists against the
+    oracle's, every list ascending over non-empty blocks only."""
+    wl = SMALL[0]
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(13)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    lay = layout_of(wl)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], wl.dtype) for p in "qkv")
+    _, (qbar, kbar) = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
+    counts, idx = ops.select(lay, zs_dev, qbar, kbar, S, tau)
+    qf, kf = (host_f64(inp[p], wl.dtype) for p in "qk")
+    r = opipe.run_selection(wl.grid, wl.mode, wl.block, qf, kf, S, tau, zone_shape=zs)
+    got = gpu_lists(counts, idx)
+    exact, exempt, fails = compare_lists(L, r["qbar"], r["kbar"], r["counts"], S, tau, got,
+                                         r["lists"])
+    assert not fails, fails[:3]
+    nonempty = np.nonzero(r["counts"] > 0)[0]
+    assert 0 < len(nonempty) < L.n_blocks              # the grid has empty blocks
+    for h in range(len(got)):
+        for i, lst in enumerate(got[h]):
+            if r["counts"][i] == 0:
+                assert lst.size == 0
+                continue
+            assert np.all(np.diff(lst) > 0) and np.all(r["counts"][lst] > 0)
+            if S == 0:
+                assert np.array_equal(lst, nonempty)
+            if tau == 1e-9:
+                assert lst.size == max(1, r["k"])
+
+
 NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),
                                    8500, 0.2)]
 
