@@ -356,6 +356,23 @@ def test_select_degenerate_settings(S, tau):
                 assert np.array_equal(lst, nonempty)
             if tau == 1e-9:
                 assert lst.size == max(1, r["k"])
+    if tau == 1e-9:  # one-block lists: the attention kernels' single-entry path
+        (qp, kp, vp) = ops.permute(lay, zs_dev, [q, k, v])
+        o, lse = ops.attn_fwd(lay, zs_dev, qp, kp, vp, counts, idx)
+        vf = host_f64(inp["v"], wl.dtype)
+        o_ref, _ = oatt.attn_fwd_gathered(L, r["perm"], qf, kf, vf, got, 1 / np.sqrt(wl.d))
+        (o_r,) = ops.unpermute(lay, zs_dev, [o])
+        assert_bf16_close(to_f64(o_r), o_ref, "O")
+        o_ras, _ = ops.attn_fwd_raster(lay, zs_dev, qp, kp, vp, counts, idx)
+        assert torch.equal(o_ras, o_r)
+        do = synth.make_inputs(wl, parts=("do",))["do"]
+        (dop,) = ops.permute(lay, zs_dev, [to_dev(do, wl.dtype)])
+        grads = ops.attn_bwd(lay, zs_dev, qp, kp, vp, o, dop, lse, counts, idx)
+        gr = [to_f64(t) for t in ops.unpermute(lay, zs_dev, list(grads))]
+        ref = oatt.attn_bwd_gathered(L, r["perm"], qf, kf, vf, host_f64(do, wl.dtype), got,
+                                     1 / np.sqrt(wl.d), o=to_f64(o_r))
+        for name, a, b in zip(("dQ", "dK", "dV"), gr, ref):
+            assert_bf16_close(a, b, name)
 
 
 NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),
