@@ -235,8 +235,6 @@ __device__ inline bf16x4 tr_read(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Direct global->LDS copy of one 128 x 128 bf16 tile by kWaves wavefronts:
 // load m of wave w fills LDS slots (kWaves m + w) * 64 + lane (row r = slot/16,
 // physical chunk lane % 16), fetching the logical chunk the swizzle puts there.
@@ -685,13 +683,15 @@ hipError_t launch_bwd_scalar(const Lay& L, const int32_t* zs, const T* q, const 
   dim3 grid(L.M, heads);
   const size_t sh_kv = (2 * (size_t)L.B * D + 2 * (size_t)L.B) * sizeof(float);
   auto k1 = dkdv_scalar<T, D>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_kv);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_kv);
+  if (e != hipSuccess) return e;
   k1<<<grid, L.B, sh_kv, st>>>(L, zs, q, k, v, dO, lse, delta, tcounts, tidx, scale, dk, dv);
   const size_t sh_q = 2 * (size_t)L.B * D * sizeof(float);
   auto k2 = dq_scalar<T, D>;
-  hipFuncSetAttribute(reinterpret_cast<const void*>(k2),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_q);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh_q);
+  if (e != hipSuccess) return e;
   k2<<<grid, L.B, sh_q, st>>>(L, zs, q, k, v, dO, lse, delta, counts, idx, scale, dq);
   return hipGetLastError();
 }

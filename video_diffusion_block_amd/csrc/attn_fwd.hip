@@ -136,16 +136,6 @@ __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
 // that a phase's LDS reads are all issued before its matrix instructions.
 __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// A zero that the compiler cannot prove uniform: a load indexed with it stays
-// on the vector memory path (counted by vmcnt, drained with the tile loads at
-// the end of an iteration) instead of becoming a scalar load, whose completion
-// shares lgkmcnt with the LDS reads and would force full waits on them.
-__device__ inline int vzero() {
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return z;
-}
-
 // max / sum of a value over the lane pair (l, l ^ 32)
 __device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -536,13 +526,17 @@ hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp
   T* o = static_cast<T*>(op);
   if (d == 64) {
     auto kern = attn_fwd_scalar<T, 64>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)shmem);
+    if (e != hipSuccess) return e;
     kern<<<grid, L.B, shmem, st>>>(L, zone_shape, q, k, v, counts, idx, scale, o, lse);
   } else {
     auto kern = attn_fwd_scalar<T, 128>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)shmem);
+    if (e != hipSuccess) return e;
     kern<<<grid, L.B, shmem, st>>>(L, zone_shape, q, k, v, counts, idx, scale, o, lse);
   }
   return hipGetLastError();

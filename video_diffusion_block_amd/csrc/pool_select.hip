@@ -159,10 +159,6 @@ __global__ __launch_bounds__(kThreads) void pooled_logits_kernel(Lay L,
 }
 
 // -------------------------------------------------------------- selection --
-__device__ inline bool before(double ka, int ia, double kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
 // Wave-level sum / exclusive prefix sum / min over the 64 lanes, in a fixed
 // order (the result does not depend on timing).
 __device__ inline double wave_sum(double v) {

@@ -91,7 +91,6 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int m
 constexpr int kA2vWaves = 8;
 constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
 constexpr int kCh = 64;               // channels per A chunk
-constexpr int kMaxMT = 8;             // audio tiles of 32 (n_audio <= 256)
 
 template <int MT>
 __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, int C, long long N,
