@@ -171,3 +171,35 @@ def attn_bwd_gathered_blocks(L: Layout, perm, q, k, v, do, lists, scale, h, q_bl
                 dk += (ds[:, off:off + n].T @ qh[rows]) * scale
             off += n
     return out_q, acc_k
+
+
+def attn_bwd_key_blocks_from_lse(L: Layout, perm, q, k, v, do, o, lse, lists, scale, h, k_blocks):
+    """dK and dV rows of the key blocks ``k_blocks`` of head h, with the
+    softmax weights formed from the forward's log-sum-exp, P = exp(S - lse),
+    and D = rowsum(dO * O) from the forward's output: the quantities a flash
+    backward receives from its forward. Same sums as ``attn_bwd_gathered``
+    restricted to those key blocks, at the cost of one pass over the queries
+    that list them (no per-row softmax over whole lists).
+
+    o [H, N, d] and lse [H, N] in raster order. Returns block -> (raster rows,
+    dK, dV)."""
+    toks = _block_tokens(L, perm)
+    out = {}
+    for j in k_blocks:
+        j = int(j)
+        keys = toks[j]
+        qb = [i for i in range(L.n_blocks) if toks[i].size and np.any(np.asarray(lists[h][i]) == j)]
+        if not qb or keys.size == 0:
+            out[j] = (keys, np.zeros((keys.size, q.shape[2])), np.zeros((keys.size, q.shape[2])))
+            continue
+        rows = np.concatenate([toks[i] for i in qb])
+        qr = q[h, rows].astype(np.float64)
+        dor = do[h, rows].astype(np.float64)
+        kj = k[h, keys].astype(np.float64)
+        vj = v[h, keys].astype(np.float64)
+        p = np.exp((qr @ kj.T) * scale - lse[h, rows].astype(np.float64)[:, None])
+        D = (dor * o[h, rows].astype(np.float64)).sum(axis=1, keepdims=True)
+        ds = p * (dor @ vj.T - D)
+        out[j] = (keys, (ds.T @ qr) * scale, p.T @ dor)
+    return out
+

@@ -511,6 +511,55 @@ def test_max_blocks_lists(grid, M):
     assert 0.3 < (r["n"] > r["k"]).mean() < 0.7
 
 
+def test_max_blocks_full_lists_attention():
+    """Every list holds all 4096 blocks (S = 0 on the largest layout the
+    library takes), so the forward's LDS list buffer and the backward's row
+    and column lists are full. Checked against the oracle over all 524288
+    keys: O and lse on three query blocks (first, middle, last), dQ on two;
+    dK and dV on two key blocks from the lse form, given the GPU forward's O
+    and lse, which is what the backward receives."""
+    wl = synth.Workload("full-lists", (32, 128, 128), 1, 128, "bf16", "fixed", (2, 8, 8), 0, 0.2)
+    print("\n[full lists] generating inputs", flush=True)
+    inp = synth.make_inputs(wl, parts=("q", "k", "v", "do"))
+    g = run_gpu(wl, inp, fused=True)
+    M = g["lay"].sizes()["n_blocks"]
+    assert M == 4096
+    assert np.all(g["counts"].cpu().numpy() == M)
+    assert np.array_equal(g["idx"].cpu().numpy()[0], np.broadcast_to(np.arange(M), (M, M)))
+    lay = g["lay"]
+    (dop,) = ops.permute(lay, g["zs"], [to_dev(inp["do"], "bf16")])
+    grads = ops.attn_bwd(lay, g["zs"], g["qp"], g["kp"], g["vp"], g["op"], dop, g["lse"],
+                         g["counts"], g["idx"])
+    dq, dk, dv = (to_f64(x) for x in ops.unpermute(lay, g["zs"], list(grads)))
+    print("[full lists] gpu done; oracle", flush=True)
+    L = oracle_layout(wl)
+    perm = olay.permutation(L, np.zeros(L.n_zones, np.int32))
+    q, k, v, do = (synth.bf16_bits_to_f64(inp[p]) for p in ("q", "k", "v", "do"))
+    full = np.arange(M)
+    lists = [[full] * M]
+    scale = 1 / np.sqrt(wl.d)
+    B = L.block_tokens
+    qblocks = [0, M // 2, M - 1]
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, perm, q, k, v, lists, scale,
+                                            pairs=[(0, i) for i in qblocks])
+    o_host = to_f64(g["o"])
+    lse_gpu = to_f64(g["lse"])
+    for i in qblocks:
+        rows = perm[i * B:(i + 1) * B]
+        assert_bf16_close(o_host[0, rows], o_ref[0, rows], f"O block {i}")
+        assert np.abs(lse_gpu[0, i * B:(i + 1) * B] - lse_ref[0, rows]).max() <= 1e-3
+    oq, _ = oatt.attn_bwd_gathered_blocks(L, perm, q, k, v, do, lists, scale, 0,
+                                          q_blocks=qblocks[:2], o=o_host)
+    for i, (rows, ref) in oq.items():
+        assert_bf16_close(dq[0, rows], ref, f"dQ block {i}")
+    lse_r = lse_raster(L, perm, lse_gpu)
+    ok = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, o_host, lse_r, lists, scale, 0,
+                                           [0, M - 1])
+    for j, (rows, rdk, rdv) in ok.items():
+        assert_bf16_close(dk[0, rows], rdk, f"dK block {j}")
+        assert_bf16_close(dv[0, rows], rdv, f"dV block {j}")
+
+
 # ------------------------------------------------------------- zone scoring --
 def _zone_case(grid, C, na, seed=4):
     X = synth.smooth_field(1, grid, C, seed)[0]

@@ -167,3 +167,31 @@ def test_backward_invariants_and_gathered(kw):
     withO = att.attn_bwd_gathered(L, r["perm"], q, k, v, do, r["lists"], scale, o=O)
     for a, b in zip(withO, (dQ, dK, dV)):
         np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("kw", CASES)
+def test_key_blocks_from_lse_equal_the_gathered_backward(kw):
+    """The lse form of the key-side gradients equals the per-row softmax form
+    (itself pinned to autograd and finite differences above) when it is given
+    the exact forward output and log-sum-exp, on every non-empty key block;
+    a key block no query lists gets zero gradients."""
+    r, q, k, v = _case(**kw)
+    L = r["layout"]
+    scale = 1 / np.sqrt(q.shape[2])
+    do = np.random.default_rng(5).standard_normal(q.shape)
+    dQ, dK, dV = att.attn_bwd_gathered(L, r["perm"], q, k, v, do, r["lists"], scale)
+    O, lse = att.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], scale)
+    O, lse = np.nan_to_num(O), np.nan_to_num(lse)
+    for h in range(q.shape[0]):
+        blocks = [j for j in range(L.n_blocks) if r["counts"][j] > 0]
+        got = att.attn_bwd_key_blocks_from_lse(L, r["perm"], q, k, v, do, O, lse, r["lists"],
+                                               scale, h, blocks)
+        for j, (rows, dk, dv) in got.items():
+            np.testing.assert_allclose(dk, dK[h, rows], rtol=1e-10, atol=1e-11)
+            np.testing.assert_allclose(dv, dV[h, rows], rtol=1e-10, atol=1e-11)
+    lists = [[np.array([0]) for _ in range(L.n_blocks)] for _ in range(q.shape[0])]
+    nz = [j for j in range(1, L.n_blocks) if r["counts"][j] > 0][:1]
+    (rows, dk, dv), = att.attn_bwd_key_blocks_from_lse(L, r["perm"], q, k, v, do, O, lse, lists,
+                                                       scale, 0, nz).values()
+    assert rows.size > 0 and np.all(dk == 0) and np.all(dv == 0)
+
