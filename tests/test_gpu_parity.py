@@ -5,6 +5,8 @@ dynamic, 1080p, 2K) are compared at full size in the launch configuration the
 benchmark times: zone shapes and block lists in full, outputs on seeded
 samples of (head, block) pairs evaluated by the oracle one by one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -702,3 +704,37 @@ def test_forward_is_deterministic():
     assert torch.equal(a["op"].view(torch.int16), b["op"].view(torch.int16))
     assert torch.equal(a["lse"], b["lse"])
     assert not torch.isnan(a["o"].float()).any()
+
+
+def test_backward_is_deterministic():
+    """The backward reduces its partial sums in a fixed order: a rerun on the
+    same inputs gives bitwise-equal dQ, dK and dV (720p grid, 4 heads)."""
+    wl = synth.Workload("det-bwd", (13, 45, 80), 4, 128, "bf16", "fixed", (2, 8, 8), 8500, 0.2)
+    inp = synth.make_inputs(wl, parts=("q", "k", "v", "do"))
+    g = run_gpu(wl, inp)
+    lay = g["lay"]
+    (dop,) = ops.permute(lay, g["zs"], [to_dev(inp["do"], "bf16")])
+    args = (lay, g["zs"], g["qp"], g["kp"], g["vp"], g["op"], dop, g["lse"], g["counts"], g["idx"])
+    a = ops.attn_bwd(*args)
+    b = ops.attn_bwd(*args)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert not torch.isnan(x).any()
+
+
+def test_dynamic_pipeline_is_deterministic():
+    """Zone scoring, the gather, the selection and the forward on a dynamic
+    layout (720p-dyn grid and video/audio features, 2 heads): reruns give the
+    same zone shapes, lists and bitwise-equal O and lse."""
+    wl = dataclasses.replace(synth.WORKLOADS["720p-dyn"], heads=2)
+    inp = synth.make_inputs(wl, parts=("q", "k", "v", "video", "audio"))
+    video, audio = to_dev(inp["video"], "bf16"), to_dev(inp["audio"], "bf16")
+    a = run_gpu(wl, inp, video=video, audio=audio, fused=True)
+    b = run_gpu(wl, inp, video=video, audio=audio, fused=True)
+    assert torch.equal(a["zs"], b["zs"])
+    assert torch.equal(a["counts"], b["counts"])
+    la, lb = gpu_lists(a["counts"], a["idx"]), gpu_lists(b["counts"], b["idx"])
+    assert all(np.array_equal(x, y) for ra, rb in zip(la, lb) for x, y in zip(ra, rb))
+    assert torch.equal(a["op"].view(torch.int16), b["op"].view(torch.int16))
+    assert torch.equal(a["lse"], b["lse"])
+
