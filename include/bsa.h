@@ -149,7 +149,8 @@ bsa_status bsa_zone_score(const bsa_layout* L, const void* video, int C, const v
  *  src         [host] array of ntensors device pointers, each [heads, N, d]
  *  dst         [host] array of ntensors device pointers, each [heads, Np, d];
  *              pad slots are written with zeros
- *  d           head dim (multiple of 8, <= 256); dtype BSA_F32 or BSA_BF16 */
+ *  d           head dim (multiple of 8, <= 256); dtype BSA_F32 or BSA_BF16
+ *  Every src and dst pointer must be 16-byte aligned (BSA_INVALID_ARG otherwise). */
 bsa_status bsa_permute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
                        const void* const* src, void* const* dst, int heads, int d, int dtype,
                        void* stream);
@@ -190,8 +191,12 @@ bsa_status bsa_permute_norm_rope(const bsa_layout* L, const int32_t* zone_shape,
                                  int dtype, int nrope, const float* const* gamma, float eps,
                                  float rope_base, int npool, double* const* means, void* stream);
 
-/* Inverse of bsa_permute: src [heads, Np, d] -> dst [heads, N, d], reading
- * real slots only. Same arguments as bsa_permute. */
+/* Inverse of bsa_permute [Prism §Blocks: attention runs on the tokens
+ * regrouped into the zones' blocks, so its outputs (and, in training, its
+ * gradients) are in block order and go back to the latent token order the rest
+ * of the model uses]: src [heads, Np, d] -> dst [heads, N, d], reading real
+ * slots only (pad slots are dropped). Same arguments as bsa_permute; src and
+ * dst 16-byte aligned. */
 bsa_status bsa_unpermute(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
                          const void* const* src, void* const* dst, int heads, int d,
                          int dtype, void* stream);
@@ -264,6 +269,7 @@ bsa_status bsa_select_causal(const bsa_layout* L, const int32_t* zone_shape, con
  *              query blocks
  *  ws          workspace of bsa_workspace_size(BSA_CALL_ATTN_FWD, ...) bytes (a
  *              per-block table; 0 bytes, ws may be NULL, when that size is 0)
+ *  qp, kp, vp and op must be 16-byte aligned (BSA_INVALID_ARG otherwise).
  *  Supported: dtype BSA_BF16 or BSA_F32, d in {64, 128}, B in {64, 128}; the
  *  bf16 MFMA kernel runs for d = 128, B = 128, the others take a scalar kernel. */
 bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
@@ -283,7 +289,14 @@ bsa_status bsa_attn_fwd_raster(const bsa_layout* L, const int32_t* zone_shape, c
                                const int32_t* idx, int heads, int d, int dtype, float scale,
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Block-sparse attention backward over the forward's lists and lse.
+/* Block-sparse attention backward over the forward's lists and lse [Prism
+ * §Blocks: Prism Block Sparse Attention is switched on in the training
+ * configuration and reported to train 2.5x faster than full attention; Prism
+ * §Data ("데이터 준비와 학습 절차", data preparation and training procedure):
+ * the whole model is trained with that configuration, so the attention over
+ * the selected blocks needs its gradients]. The gradients are those of the
+ * forward's function with the lists held fixed (selection is a discrete
+ * choice and passes no gradient):
  * D_n = dO_n . O_n; dV_m = sum_n P_nm dO_n; dS_nm = P_nm (dO_n . V_m - D_n);
  * dQ_n = scale sum_m dS_nm K_m; dK_m = scale sum_n dS_nm Q_n; sums over the
  * selected (query, real key) pairs only.

@@ -136,6 +136,11 @@ def test_attn_fwd_validation(lib):
     assert _attn_fwd(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
 
 
+def test_attn_fwd_rejects_misaligned_tensors(lib):
+    assert _attn_fwd(lib, q=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG
+    assert "aligned" in lib.bsa_last_error().decode()
+
+
 def test_attn_fwd_raster_validation(lib):
     c = LAY.c()
 

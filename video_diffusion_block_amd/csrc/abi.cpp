@@ -213,6 +213,9 @@ static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape
   if (!src || !dst) return fail(BSA_INVALID_ARG, "src/dst pointer arrays are NULL");
   for (int i = 0; i < ntensors; ++i)
     if (!src[i] || !dst[i]) return fail(BSA_INVALID_ARG, "tensor %d pointer is NULL", i);
+  for (int i = 0; i < ntensors; ++i)
+    if (reinterpret_cast<uintptr_t>(src[i]) % 16 || reinterpret_cast<uintptr_t>(dst[i]) % 16)
+      return fail(BSA_INVALID_ARG, "tensor %d: src and dst must be 16-byte aligned", i);
   const size_t row = (size_t)d * esize(dtype);
   if (row % 16 || d > 256) return fail(BSA_UNSUPPORTED, "row of %zu bytes (d = %d); need a multiple of 16 bytes and d <= 256", row, d);
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
@@ -381,6 +384,9 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
     return fail(BSA_UNSUPPORTED, "raster output needs bf16, d = 128 and 128-token blocks");
   if (!qp || !kp || !vp || !counts || !idx || !op || !lse)
     return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
+  for (const void* p : {qp, kp, vp, static_cast<const void*>(op)})
+    if (reinterpret_cast<uintptr_t>(p) % 16)
+      return fail(BSA_INVALID_ARG, "qp, kp, vp and the output must be 16-byte aligned");
   if (in->mode == BSA_MODE_DYNAMIC && !zone_shape)
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
   if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");

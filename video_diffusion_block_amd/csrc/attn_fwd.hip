@@ -417,10 +417,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // path drains about 64 bytes per clock per CU, a wave that issues into a
   // full queue stalls, and the exponentiating wave has slack where the matrix
   // wave has none.
+  // Buffer ownership: iteration 0 refills sK[0] (with K_2) and sM[0] (with the
+  // facts of block 2), which every wave reads before the loop (S_0 and block 0's
+  // facts); the barrier after S_0 keeps those refills behind the last of
+  // these reads. From then on, a buffer is refilled only in the iteration after
+  // the one that read it, past that iteration's closing barrier.
   auto walk = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
     qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi, no_hook);
     mask_pad_keys(s_cur, meta_j, hi);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();
     bf16x8 pf8[4];
     if (KH == 1) softmax(pf8, no_hook);
     // ids of blocks j+1 and j+2 (carried in scalar registers; the next one is

@@ -64,10 +64,16 @@ constexpr int kPermThreads = 256;
 // (256 is a multiple of the chunk count), so the chunks of a row sit in
 // adjacent lanes (the row's sum of squares is a shuffle reduction) and a
 // lane's partial block sums need one LDS reduction over its column.
-template <bool kInverse, int kEpc, bool kNR>
+// kChunks: the row's 16-byte chunk count when it is known at compile time (16
+// for bf16 and 32 for fp32 rows of d = 128), else 0 and `chunks_rt` gives it.
+// The instantiations of the four uses (the Q/K/V gather with pooling, the
+// plain gather, the bf16 scatter of O and the fp32 scatter of gradients) are
+// distinct kernels, so per-kernel counters and traces tell them apart.
+template <bool kInverse, int kEpc, bool kNR, int kChunks>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int32_t* zone_shape,
-                                                               PtrPack P, int chunks,
+                                                               PtrPack P, int chunks_rt,
                                                                PoolPack pool, NormRope nr) {
+  const int chunks = kChunks > 0 ? kChunks : chunks_rt;
   const int b = blockIdx.x;
   const int h = blockIdx.y;
   const int t = blockIdx.z;
@@ -236,22 +242,32 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
   for (int i = 0; i < nrope; ++i) R.gamma[i] = gamma ? gamma[i] : nullptr;
   const int chunks = row_bytes / 16;
   dim3 grid(L.M, heads, ntensors);
-#define BSA_PERMUTE(INV, EPC, NR) \
-  permute_kernel<INV, EPC, NR><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q, R)
+#define BSA_PERMUTE(INV, EPC, NR, CH) \
+  permute_kernel<INV, EPC, NR, CH><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q, R)
+#define BSA_PERMUTE_ROWS(INV, EPC, NR) \
+  do {                                 \
+    if (chunks == 16)                  \
+      BSA_PERMUTE(INV, EPC, NR, 16);   \
+    else if (chunks == 32)             \
+      BSA_PERMUTE(INV, EPC, NR, 32);   \
+    else                               \
+      BSA_PERMUTE(INV, EPC, NR, 0);    \
+  } while (0)
   if (inverse)
-    BSA_PERMUTE(true, 0, false);
+    BSA_PERMUTE_ROWS(true, 0, false);
   else if (npool == 0 && nrope == 0)
-    BSA_PERMUTE(false, 0, false);
+    BSA_PERMUTE_ROWS(false, 0, false);
   else if (nrope == 0 && epc == 8)
-    BSA_PERMUTE(false, 8, false);
+    BSA_PERMUTE(false, 8, false, 0);
   else if (nrope == 0 && epc == 4)
-    BSA_PERMUTE(false, 4, false);
+    BSA_PERMUTE(false, 4, false, 0);
   else if (epc == 8)
-    BSA_PERMUTE(false, 8, true);
+    BSA_PERMUTE(false, 8, true, 0);
   else if (epc == 4)
-    BSA_PERMUTE(false, 4, true);
+    BSA_PERMUTE(false, 4, true, 0);
   else
     return hipErrorInvalidValue;
+#undef BSA_PERMUTE_ROWS
 #undef BSA_PERMUTE
   return hipGetLastError();
 }

@@ -342,7 +342,9 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
     }
     const double Z = wave_sum(zl);
     const double mass = wave_sum(ml) / Z;
-    int n_sel = k_top;
+    // the top-k cut, kept in case the CDF crossing falls inside the top-k set
+    const uint64_t prefix_k = prefix;
+    const int id_cut_k = id_cut;
     if (mass < tau) {
       // The CDF prefix is longer than k: a second radix select, now of the
       // first element at which the mass in (logit desc, id asc) order reaches
@@ -438,8 +440,18 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
         cut = cur;
       }
       const int m_cdf = cbefore + taken;
-      n_sel = min(max(k_top, m_cdf), mv);
-      id_cut = cut;  // the list: every element ranked up to the crossing
+      if (m_cdf > k_top) {
+        id_cut = cut;  // the list: every element ranked up to the crossing
+      } else {
+        // Both sets are prefixes of one order, so the union is the longer
+        // one. Pass 1 found the top-k mass below tau, so the crossing should
+        // lie past rank k; the mass sums of the two passes group the same
+        // terms differently, and when the top-k mass is within rounding of tau
+        // the second pass can place the crossing inside the top-k set. The
+        // list is then the top-k set.
+        prefix = prefix_k;
+        id_cut = id_cut_k;
+      }
     }
     {
 #pragma unroll
@@ -457,6 +469,9 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
         cnt += (bits[b >> 5] >> (b & 31)) & 1u;
       }
       int pos = wave_exclusive_scan(cnt, lane);
+      // the count is the number of ids written (the length of the prefix
+      // the cut marks), so the list and its count cannot disagree
+      const int n_sel = wave_sum(cnt);
       int32_t* out = idx + row * L.M;
 #pragma unroll
       for (int e = 0; e < C; ++e) {
