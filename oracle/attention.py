@@ -64,6 +64,29 @@ def _block_tokens(L: Layout, perm: np.ndarray):
     return [row[row >= 0] for row in pb]
 
 
+def attn_fwd_gathered_pair(toks, q, k, v, lst, scale, i):
+    """One (head, query block): q, k, v [N, d] of that head (raster), ``lst``
+    the block's key-block list, ``toks`` the raster ids of every block's real
+    tokens. Returns (raster rows, O rows [n, d], lse rows [n]) in fp64."""
+    rows = toks[i]
+    if rows.size == 0:
+        return rows, np.zeros((0, q.shape[1])), np.zeros(0)
+    keys = np.concatenate([toks[j] for j in lst])
+    qi = q[rows].astype(np.float64)
+    kj = k[keys].astype(np.float64)
+    vj = v[keys].astype(np.float64)
+    s = (qi @ kj.T) * scale
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    z = e.sum(axis=1, keepdims=True)
+    return rows, (e / z) @ vj, (mx + np.log(z))[:, 0]
+
+
+def block_tokens(L: Layout, perm):
+    """Raster ids of the real tokens of every block (list of int arrays)."""
+    return _block_tokens(L, perm)
+
+
 def attn_fwd_gathered(L: Layout, perm, q, k, v, lists, scale, pairs=None):
     """All heads, raster layout. q,k,v [H, N, d] (any float dtype, upcast to fp64).
 
@@ -76,19 +99,10 @@ def attn_fwd_gathered(L: Layout, perm, q, k, v, lists, scale, pairs=None):
     if pairs is None:
         pairs = [(h, i) for h in range(H) for i in range(L.n_blocks)]
     for h, i in pairs:
-        rows = toks[i]
-        if rows.size == 0:
-            continue
-        keys = np.concatenate([toks[j] for j in lists[h][i]])
-        qi = q[h, rows].astype(np.float64)
-        kj = k[h, keys].astype(np.float64)
-        vj = v[h, keys].astype(np.float64)
-        s = (qi @ kj.T) * scale
-        mx = s.max(axis=1, keepdims=True)
-        e = np.exp(s - mx)
-        z = e.sum(axis=1, keepdims=True)
-        O[h, rows] = (e / z) @ vj
-        lse[h, rows] = (mx + np.log(z))[:, 0]
+        rows, o_rows, l_rows = attn_fwd_gathered_pair(toks, q[h], k[h], v[h], lists[h][i],
+                                                      scale, i)
+        O[h, rows] = o_rows
+        lse[h, rows] = l_rows
     return O, lse
 
 

@@ -16,12 +16,15 @@ definition; the readings taken here (the plainest multi-head form):
   dP = dO_h V_h^T, D = rowsum(dO_h * O_h), dS = P (dP - D),
   dQ_h = dS K_h / sqrt(d), dK_h = dS^T Q_h / sqrt(d), dV_h = P^T dO_h;
   dX = dQ Wq, dWq = dQ^T X, dA = dK Wk + dV Wv, dWk = dK^T A, dWv = dV^T A.
-- Storage precision: the layer keeps its activations and activation
-  gradients as bf16 tensors (Q, K, V, O, Y; dO, dQ, dK, dV), so with
-  ``rounding=True`` each of those is rounded to bf16 (nearest, ties to even)
-  where it is stored; every product and sum is fp64 and the weight gradients,
-  dX and dA are returned unrounded. ``rounding=False`` gives the exact fp64
-  function (used by the finite-difference pins).
+- Storage precision: the layer hands back its activations as bf16 tensors
+  (Q, K, V, O and Y, the forward's outputs, which its backward takes as
+  inputs), so with ``rounding=True`` the forward rounds each of those to bf16
+  (nearest, ties to even) where it is stored. Nothing else is rounded: every
+  product and sum is fp64, and the backward is the exact fp64 gradient of the
+  layer given the forward's stored tensors (whatever a kernel keeps inside its
+  backward, such as dO, dQ, dK and dV, is its own affair and not part of the
+  layer's interface). ``rounding=False`` gives the exact fp64 function (used by
+  the finite-difference pins).
 """
 from __future__ import annotations
 
@@ -63,12 +66,13 @@ def forward(X, A, Wq, Wk, Wv, Wo, heads: int, rounding: bool = True) -> dict:
     return {"q": q, "k": k, "v": v, "o": o, "lse": lse, "y": y}
 
 
-def backward(X, A, Wq, Wk, Wv, Wo, heads: int, fwd: dict, dY, rounding: bool = True) -> dict:
-    """Gradients of sum(Y * dY) given the forward's stored tensors ``fwd``."""
+def backward(X, A, Wq, Wk, Wv, Wo, heads: int, fwd: dict, dY) -> dict:
+    """Exact gradients of sum(Y * dY) given the forward's stored tensors ``fwd``
+    (fp64 throughout)."""
     D = Wq.shape[0]
     d = D // heads
     q, k, v, o, lse = fwd["q"], fwd["k"], fwd["v"], fwd["o"], fwd["lse"]
-    dO = _r(dY @ Wo, rounding)
+    dO = dY @ Wo
     dWo = dY.T @ o
     dQ = np.empty_like(q)
     dK = np.empty_like(k)
@@ -84,6 +88,5 @@ def backward(X, A, Wq, Wk, Wv, Wo, heads: int, fwd: dict, dY, rounding: bool = T
         dQ[:, c] = (ds @ k[:, c]) * scale
         dK[:, c] = (ds.T @ q[:, c]) * scale
         dV[:, c] = p.T @ dO[:, c]
-    dQ, dK, dV = _r(dQ, rounding), _r(dK, rounding), _r(dV, rounding)
     return {"dx": dQ @ Wq, "da": dK @ Wk + dV @ Wv, "dwq": dQ.T @ X, "dwk": dK.T @ A,
             "dwv": dV.T @ A, "dwo": dWo, "do": dO, "dq": dQ, "dk": dK, "dv": dV}

@@ -104,3 +104,18 @@ def block_mask(L: Layout, lists, h: int, perm: np.ndarray) -> np.ndarray:
     for i, lst in enumerate(lists[h]):
         sel[i, lst] = True
     return sel[blk[:, None], blk[None, :]]
+
+
+def block_mask_rows(L: Layout, lst, perm: np.ndarray) -> np.ndarray:
+    """One row of ``block_mask`` for the queries of a block whose list is
+    ``lst``: [N] bool in raster order, key m allowed iff block(m) is listed
+    (pad slots are not tokens, so every raster key is real). Every query of
+    the block shares this row."""
+    N = L.n_tokens
+    B = L.block_tokens
+    blk = np.full(N, -1, dtype=np.int64)
+    slots = np.nonzero(perm >= 0)[0]
+    blk[perm[slots]] = slots // B
+    sel = np.zeros(L.n_blocks, dtype=bool)
+    sel[np.asarray(lst, dtype=np.int64)] = True
+    return sel[blk]

@@ -154,3 +154,23 @@ def test_flat_rows_take_more_than_k_blocks():
     logits = np.linspace(0.0, 0.01, 100)
     lst, n, m, _ = sel.select_row(logits, np.arange(100), sel.top_k_size(100, 9300), 0.2)
     assert n == m and 19 <= n <= 21
+
+
+def test_block_mask_rows_by_brute_force():
+    """The one-block mask row against a per-token walk over the permutation
+    (slot p of block b holds raster token perm[p]): on a ragged dynamic grid
+    with forced shapes, key token m is allowed for block i exactly when the
+    slot holding m lies in a block of i's list."""
+    L = lay.make_layout((5, 20, 36), "dynamic", (4, 16, 16))
+    rng = np.random.default_rng(3)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    perm = lay.permutation(L, zs)
+    B = L.block_tokens
+    for _ in range(5):
+        lst = np.sort(rng.choice(L.n_blocks, 7, replace=False))
+        row = sel.block_mask_rows(L, lst, perm)
+        want = np.zeros(L.n_tokens, dtype=bool)
+        for p in range(L.n_padded):
+            if perm[p] >= 0 and (p // B) in set(lst.tolist()):
+                want[perm[p]] = True
+        assert np.array_equal(row, want)

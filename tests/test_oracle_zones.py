@@ -171,3 +171,45 @@ def test_a2v_term_acts_per_axis():
     r = zon.zone_signal(V, G, nz, use_audio=True)
     shape, _ = zon.choose_shapes(zon.shape_costs(L, r))
     assert shape[0] == 1
+
+
+def test_two_signals_pulling_apart_hand_values():
+    """Both terms non-zero and pulling toward different shapes. Worked by hand:
+
+    zone 0: V = (8, 0, 1), G = (0, 8, 1); zone 1: V = (5, 5, 5), G = (1, 1, 1);
+    zone 2 is empty (n_z = 0, V = G = 0) and must not enter the means.
+    Means over the six non-empty (zone, axis) pairs: Vbar = 24/6 = 4,
+    Gbar = 12/6 = 2. So r = V/4 + G/2:
+      zone 0: (2 + 0, 0 + 4, 1/4 + 1/2) = (2, 4, 3/4);  zone 1: (7/4, 7/4, 7/4).
+    Shape factors (b^2-1)/(Z^2-1), Z = (4, 16, 16):
+      2x8x8: (3/15, 63/255, 63/255); 4x4x8: (1, 15/255, 63/255);
+      1x8x16: (0, 63/255, 1).
+    Zone 0 costs: 2x8x8: 2/5 + 4.75*63/255 = 401.25/255;
+                  4x4x8: 2 + (60 + 47.25)/255 = 617.25/255;
+                  1x8x16: 252/255 + 3/4 = 443.25/255  -> 2x8x8.
+    The video term alone (r = (2, 0, 1/4)) picks 1x8x16 (costs 0.4 + 15.75/255,
+    2 + 15.75/255, 1/4), the audio term alone (r = (0, 4, 1/2)) picks 4x4x8
+    (costs 283.5/255, 91.5/255, 379.5/255), and the sum without the
+    normalisation (r = (8, 8, 2)) picks 1x8x16 (costs 1.6 + 630/255,
+    8 + 246/255, 504/255 + 2): only the normalised sum of both gives 2x8x8.
+    Zone 1: 7/4 (177/255, 333/255, 318/255) -> 2x8x8."""
+    L = lay.make_layout((12, 16, 16), "dynamic", ZONE)   # three zones along t
+    V = np.array([[8.0, 0.0, 1.0], [5.0, 5.0, 5.0], [0.0, 0.0, 0.0]])
+    G = np.array([[0.0, 8.0, 1.0], [1.0, 1.0, 1.0], [0.0, 0.0, 0.0]])
+    nz = np.array([1024, 1024, 0])
+    r = zon.zone_signal(V, G, nz, use_audio=True)
+    np.testing.assert_allclose(r, [[2.0, 4.0, 0.75], [1.75, 1.75, 1.75], [0.0, 0.0, 0.0]],
+                               rtol=1e-15)
+    cost = zon.shape_costs(L, r)
+    np.testing.assert_allclose(cost[0], np.array([401.25, 617.25, 443.25]) / 255, rtol=1e-14)
+    np.testing.assert_allclose(cost[1], 1.75 * np.array([177.0, 333.0, 318.0]) / 255, rtol=1e-14)
+    shape, _ = zon.choose_shapes(cost)
+    assert shape.tolist() == [0, 0, 0]
+    # each signal alone, and the unnormalised sum, choose differently
+    rv = zon.zone_signal(V, G, nz, use_audio=False)
+    np.testing.assert_allclose(rv[0], [2.0, 0.0, 0.25], rtol=1e-15)
+    assert zon.choose_shapes(zon.shape_costs(L, rv))[0][0] == 2
+    ra = zon.zone_signal(np.zeros_like(V), G, nz, use_audio=True)
+    np.testing.assert_allclose(ra[0], [0.0, 4.0, 0.5], rtol=1e-15)
+    assert zon.choose_shapes(zon.shape_costs(L, ra))[0][0] == 1
+    assert zon.choose_shapes(zon.shape_costs(L, V + G))[0][0] == 2
