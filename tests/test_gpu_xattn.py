@@ -65,14 +65,12 @@ def test_xattn_fwd_small(grid, C, Na, heads):
     _run(grid, C, Na, heads)
 
 
-def test_xattn_fwd_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_xattn_fwd_full_size():
     """720p video tokens (13 x 45 x 80), C = 1536, 200 audio tokens, 12 heads:
-    every K and V, and Q, O, Y, lse on 192 sampled query rows (first, middle,
-    last 64)."""
-    N = 13 * 45 * 80
-    rows = np.r_[0:64, N // 2:N // 2 + 64, N - 64:N]
+    Q, K, V, O, Y and lse of every row."""
     print("\n[xattn 720p] running", flush=True)
-    _run((13, 45, 80), 1536, 200, 12, rows=rows)
+    _run((13, 45, 80), 1536, 200, 12)
 
 
 def test_xattn_fwd_is_deterministic():
@@ -113,6 +111,37 @@ def test_xattn_bwd(grid, C, Na, heads):
     ref = oca.backward(Xf, Af, *Wf, heads, fwd, synth.bf16_bits_to_f64(dY))
     for name in ("dx", "da", "dwq", "dwk", "dwv", "dwo"):
         _grad_close(g[name].cpu().numpy().astype(np.float64), ref[name], name)
+
+
+@pytest.mark.timeout(900)
+def test_xattn_bwd_full_size():
+    """The size the benchmark times: 720p video tokens (13 x 45 x 80 = 46 800),
+    C = 1536, 200 audio tokens, 12 heads. Every gradient (dX, dA, dWq, dWk,
+    dWv, dWo) in full, outputs starting as NaN, against the oracle's exact
+    backward on the tensors the GPU forward saved."""
+    grid, C, Na, heads = (13, 45, 80), 1536, 200, 12
+    print("\n[xattn bwd 720p] running", flush=True)
+    X, A, W = _inputs(grid, C, Na, heads)
+    N = int(np.prod(grid))
+    dY = synth.f32_to_bf16_bits(synth.gaussian_noise((N, C), 99))
+    dev = [to_dev(X, "bf16"), to_dev(A, "bf16")] + [to_dev(w, "bf16") for w in W]
+    y, saved = ops.xattn_fwd(*dev, heads)
+    g = ops.xattn_bwd(*dev, heads, saved, to_dev(dY, "bf16"))
+    torch.cuda.synchronize()
+    print("[xattn bwd 720p] oracle", flush=True)
+    fwd = {n: to_f64(saved[n]) for n in ("q", "k", "v", "o")}
+    fwd["lse"] = saved["lse"].cpu().numpy().astype(np.float64)
+    Xf, Af = synth.bf16_bits_to_f64(X), synth.bf16_bits_to_f64(A)
+    Wf = [synth.bf16_bits_to_f64(w) for w in W]
+    ref = oca.backward(Xf, Af, *Wf, heads, fwd, synth.bf16_bits_to_f64(dY))
+    for name in ("dx", "da", "dwq", "dwk", "dwv", "dwo"):
+        got = g[name].cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), name
+        _grad_close(got, ref[name], name)
+        diff = np.abs(got - ref[name])
+        print(f"[xattn bwd 720p] {name}: max-abs {diff.max():.3g} (max |ref| "
+              f"{np.abs(ref[name]).max():.3g}), L1 {diff.sum() / np.abs(ref[name]).sum():.3g}",
+              flush=True)
 
 
 def test_xattn_bwd_is_deterministic():

@@ -61,6 +61,25 @@ class BSALayout:
                     block_tokens=b.value)
 
 
+_POISON = False
+
+
+def poison_outputs(enable: bool = True) -> None:
+    """Fill every output and workspace this module allocates with 0xFF bytes
+    before the call (NaN in floating point, -1 in int32), so that a kernel that
+    leaves part of its output unwritten, or reads workspace it did not write,
+    is seen by the caller. A testing aid; off by default."""
+    global _POISON
+    _POISON = bool(enable)
+
+
+def _empty(shape, dtype, device) -> torch.Tensor:
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if _POISON:
+        t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -89,7 +108,7 @@ def _dev(*ts):
 def _workspace(call: int, layout: BSALayout, heads: int, d: int, device) -> torch.Tensor:
     L = layout.c()
     n = _lib.load().bsa_workspace_size(call, ctypes.byref(L), heads, d)
-    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+    return _empty(max(int(n), 256), torch.uint8, device)
 
 
 def zone_score(layout: BSALayout, video: torch.Tensor | None, audio: torch.Tensor | None,
@@ -100,8 +119,8 @@ def zone_score(layout: BSALayout, video: torch.Tensor | None, audio: torch.Tenso
     sz = layout.sizes()
     dev = video.device if video is not None else torch.device("cuda")
     _dev(video, audio)
-    zs = torch.empty(sz["n_zones"], dtype=torch.int32, device=dev)
-    stats = torch.empty((sz["n_zones"], 3, 2), dtype=torch.float64, device=dev) if with_stats else None
+    zs = _empty(sz["n_zones"], torch.int32, dev)
+    stats = _empty((sz["n_zones"], 3, 2), torch.float64, dev) if with_stats else None
     C = 0 if video is None else video.shape[1]
     na = 0 if audio is None else audio.shape[0]
     ws = _workspace(_lib.BSA_CALL_ZONE_SCORE, layout, 1, max(C, 1), dev)
@@ -128,7 +147,7 @@ def permute(layout: BSALayout, zone_shape, tensors):
     """bsa_permute: list of [H, N, d] -> list of [H, Np, d] (one launch)."""
     _dev(zone_shape, *tensors)
     npad = layout.sizes()["n_padded"]
-    outs = [torch.empty((t.shape[0], npad, t.shape[2]), dtype=t.dtype, device=t.device)
+    outs = [_empty((t.shape[0], npad, t.shape[2]), t.dtype, t.device)
             for t in tensors]
     _permute_call("bsa_permute", layout, zone_shape, list(tensors), outs)
     return outs
@@ -140,10 +159,10 @@ def permute_pool(layout: BSALayout, zone_shape, tensors, npool: int = 2):
     lib = _lib.load()
     _dev(zone_shape, *tensors)
     sz = layout.sizes()
-    outs = [torch.empty((t.shape[0], sz["n_padded"], t.shape[2]), dtype=t.dtype, device=t.device)
+    outs = [_empty((t.shape[0], sz["n_padded"], t.shape[2]), t.dtype, t.device)
             for t in tensors]
-    means = [torch.empty((t.shape[0], sz["n_blocks"], t.shape[2]), dtype=torch.float64,
-                         device=t.device) for t in tensors[:npool]]
+    means = [_empty((t.shape[0], sz["n_blocks"], t.shape[2]), torch.float64, t.device)
+             for t in tensors[:npool]]
     H, _, d = tensors[0].shape
     n = len(tensors)
     src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
@@ -171,10 +190,10 @@ def permute_norm_rope(layout: BSALayout, zone_shape, tensors, gammas=None, eps: 
             if g.dtype != torch.float32 or g.numel() != tensors[0].shape[2]:
                 raise ValueError("gamma must be a float32 tensor of d elements")
     sz = layout.sizes()
-    outs = [torch.empty((t.shape[0], sz["n_padded"], t.shape[2]), dtype=t.dtype, device=t.device)
+    outs = [_empty((t.shape[0], sz["n_padded"], t.shape[2]), t.dtype, t.device)
             for t in tensors]
-    means = [torch.empty((t.shape[0], sz["n_blocks"], t.shape[2]), dtype=torch.float64,
-                         device=t.device) for t in tensors[:npool]]
+    means = [_empty((t.shape[0], sz["n_blocks"], t.shape[2]), torch.float64, t.device)
+             for t in tensors[:npool]]
     H, _, d = tensors[0].shape
     n = len(tensors)
     src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
@@ -196,9 +215,9 @@ def select(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, tau: fl
     lib = _lib.load()
     _dev(zone_shape, qbar, kbar)
     H, M, d = qbar.shape
-    counts = torch.empty((H, M), dtype=torch.int32, device=qbar.device)
-    idx = torch.empty((H, M, M), dtype=torch.int32, device=qbar.device)
-    logits = torch.empty((H, M, M), dtype=torch.float64, device=qbar.device) if return_logits else None
+    counts = _empty((H, M), torch.int32, qbar.device)
+    idx = _empty((H, M, M), torch.int32, qbar.device)
+    logits = _empty((H, M, M), torch.float64, qbar.device) if return_logits else None
     ws = _workspace(_lib.BSA_CALL_SELECT, layout, H, d, qbar.device)
     L = layout.c()
     _lib.check("bsa_select", lib.bsa_select(
@@ -214,8 +233,8 @@ def select_causal(layout: BSALayout, zone_shape, qbar, kbar, sparsity_1e4: int, 
     lib = _lib.load()
     _dev(zone_shape, qbar, kbar)
     H, M, d = qbar.shape
-    counts = torch.empty((H, M), dtype=torch.int32, device=qbar.device)
-    idx = torch.empty((H, M, M), dtype=torch.int32, device=qbar.device)
+    counts = _empty((H, M), torch.int32, qbar.device)
+    idx = _empty((H, M, M), torch.int32, qbar.device)
     ws = _workspace(_lib.BSA_CALL_SELECT, layout, H, d, qbar.device)
     L = layout.c()
     _lib.check("bsa_select_causal", lib.bsa_select_causal(
@@ -229,7 +248,7 @@ def unpermute(layout: BSALayout, zone_shape, tensors):
     """bsa_unpermute: list of [H, Np, d] -> list of [H, N, d] (one launch)."""
     _dev(zone_shape, *tensors)
     n = layout.sizes()["n_tokens"]
-    outs = [torch.empty((t.shape[0], n, t.shape[2]), dtype=t.dtype, device=t.device)
+    outs = [_empty((t.shape[0], n, t.shape[2]), t.dtype, t.device)
             for t in tensors]
     _permute_call("bsa_unpermute", layout, zone_shape, list(tensors), outs)
     return outs
@@ -243,9 +262,9 @@ def pool_select(layout: BSALayout, zone_shape, qp, kp, sparsity_1e4: int, tau: f
     _dev(zone_shape, qp, kp)
     H, _, d = qp.shape
     M = layout.sizes()["n_blocks"]
-    counts = torch.empty((H, M), dtype=torch.int32, device=qp.device)
-    idx = torch.empty((H, M, M), dtype=torch.int32, device=qp.device)
-    logits = torch.empty((H, M, M), dtype=torch.float64, device=qp.device) if return_logits else None
+    counts = _empty((H, M), torch.int32, qp.device)
+    idx = _empty((H, M, M), torch.int32, qp.device)
+    logits = _empty((H, M, M), torch.float64, qp.device) if return_logits else None
     ws = _workspace(_lib.BSA_CALL_POOL_SELECT, layout, H, d, qp.device)
     L = layout.c()
     _lib.check("bsa_pool_select", lib.bsa_pool_select(
@@ -260,8 +279,8 @@ def attn_fwd(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: floa
     lib = _lib.load()
     _dev(zone_shape, qp, kp, vp, counts, idx)
     H, Np, d = qp.shape
-    op = torch.empty_like(qp)
-    lse = torch.empty((H, Np), dtype=torch.float32, device=qp.device)
+    op = _empty(qp.shape, qp.dtype, qp.device)
+    lse = _empty((H, Np), torch.float32, qp.device)
     ws = _workspace(_lib.BSA_CALL_ATTN_FWD, layout, H, d, qp.device)
     L = layout.c()
     _lib.check("bsa_attn_fwd", lib.bsa_attn_fwd(
@@ -278,8 +297,8 @@ def attn_fwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scal
     _dev(zone_shape, qp, kp, vp, counts, idx)
     H, Np, d = qp.shape
     N = layout.sizes()["n_tokens"]
-    o = torch.empty((H, N, d), dtype=qp.dtype, device=qp.device)
-    lse = torch.empty((H, N), dtype=torch.float32, device=qp.device)
+    o = _empty((H, N, d), qp.dtype, qp.device)
+    lse = _empty((H, N), torch.float32, qp.device)
     ws = _workspace(_lib.BSA_CALL_ATTN_FWD, layout, H, d, qp.device)
     L = layout.c()
     _lib.check("bsa_attn_fwd_raster", lib.bsa_attn_fwd_raster(
@@ -295,7 +314,7 @@ def attn_bwd(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, id
     lib = _lib.load()
     _dev(zone_shape, qp, kp, vp, op, dop, lse, counts, idx)
     H, Np, d = qp.shape
-    dq, dk, dv = (torch.empty(qp.shape, dtype=torch.float32, device=qp.device) for _ in range(3))
+    dq, dk, dv = (_empty(qp.shape, torch.float32, qp.device) for _ in range(3))
     ws = _workspace(_lib.BSA_CALL_ATTN_BWD, layout, H, d, qp.device)
     L = layout.c()
     _lib.check("bsa_attn_bwd", lib.bsa_attn_bwd(
@@ -320,12 +339,12 @@ def xattn_fwd(x, a, wq, wk, wv, wo, heads: int):
     D = wq.shape[0]
     dev = x.device
     bf = torch.bfloat16
-    q = torch.empty((N, D), dtype=bf, device=dev)
-    k = torch.empty((Na, D), dtype=bf, device=dev)
-    v = torch.empty((Na, D), dtype=bf, device=dev)
-    o = torch.empty((N, D), dtype=bf, device=dev)
-    lse = torch.empty((heads, N), dtype=torch.float32, device=dev)
-    y = torch.empty((N, C), dtype=bf, device=dev)
+    q = _empty((N, D), bf, dev)
+    k = _empty((Na, D), bf, dev)
+    v = _empty((Na, D), bf, dev)
+    o = _empty((N, D), bf, dev)
+    lse = _empty((heads, N), torch.float32, dev)
+    y = _empty((N, C), bf, dev)
     _lib.check("bsa_xattn_fwd", lib.bsa_xattn_fwd(
         N, Na, C, heads, D // max(1, heads), _ptr(x), _ptr(a), _ptr(wq), _ptr(wk), _ptr(wv),
         _ptr(wo), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(y), _stream()))
@@ -342,16 +361,16 @@ def xattn_bwd(x, a, wq, wk, wv, wo, heads: int, saved: dict, dy):
     D = wq.shape[0]
     dev = x.device
     f = torch.float32
-    out = {"dx": torch.empty((N, C), dtype=f, device=dev),
-           "da": torch.empty((Na, C), dtype=f, device=dev),
-           "dwq": torch.empty((D, C), dtype=f, device=dev),
-           "dwk": torch.empty((D, C), dtype=f, device=dev),
-           "dwv": torch.empty((D, C), dtype=f, device=dev),
-           "dwo": torch.empty((C, D), dtype=f, device=dev)}
+    out = {"dx": _empty((N, C), f, dev),
+           "da": _empty((Na, C), f, dev),
+           "dwq": _empty((D, C), f, dev),
+           "dwk": _empty((D, C), f, dev),
+           "dwv": _empty((D, C), f, dev),
+           "dwo": _empty((C, D), f, dev)}
     nbytes = lib.bsa_xattn_bwd_workspace_size(N, Na, C, heads)
     if nbytes == 0:
         raise _lib.BSAError("bsa_xattn_bwd_workspace_size", _lib.BSA_INVALID_ARG)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws = _empty(nbytes, torch.uint8, dev)
     _lib.check("bsa_xattn_bwd", lib.bsa_xattn_bwd(
         N, Na, C, heads, D // max(1, heads), _ptr(x), _ptr(a), _ptr(wq), _ptr(wk), _ptr(wv),
         _ptr(wo), _ptr(saved["q"]), _ptr(saved["k"]), _ptr(saved["v"]), _ptr(saved["o"]),
