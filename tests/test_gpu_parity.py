@@ -20,6 +20,7 @@ from oracle import select as osel
 from oracle import causal as ocau
 from oracle import zones as ozon
 from parity import (BF16_L1_REL, BF16_MAX_ABS, F32_TOL, LSE_TOL, ZONE_TIE, assert_bf16_close,
+                    assert_grad_close,
                     check_fwd_pairs, compare_lists, gpu_lists, grad_stats, host_f64,
                     oracle_layout, parallel_map, sample_pairs, to_dev, to_f64)
 from video_diffusion_block_amd import ops
@@ -149,7 +150,7 @@ def test_small_pipeline_forced_shapes(wl):
     ref = oatt.attn_bwd_gathered(L, perm, q, k, v, do, lists, scale, o=o_gpu)
     for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
         if wl.dtype == "bf16":
-            assert_bf16_close(a, b, name)
+            assert_grad_close(a, b, name)
         else:
             assert np.abs(a - b).max() <= F32_TOL, name
     # the same gradients against the exact oracle (its own O in D = rowsum(dO O))
@@ -381,7 +382,7 @@ def test_select_degenerate_settings(S, tau):
         ref = oatt.attn_bwd_gathered(L, r["perm"], qf, kf, vf, host_f64(do, wl.dtype), got,
                                      1 / np.sqrt(wl.d), o=to_f64(o_r))
         for name, a, b in zip(("dQ", "dK", "dV"), gr, ref):
-            assert_bf16_close(a, b, name)
+            assert_grad_close(a, b, name)
 
 
 NR_CASES = SMALL + [synth.Workload("wide-w", (4, 16, 160), 1, 128, "bf16", "fixed", (2, 8, 8),
@@ -573,13 +574,24 @@ def test_max_blocks_full_lists_attention():
     oq, _ = oatt.attn_bwd_gathered_blocks(L, perm, q, k, v, do, lists, scale, 0,
                                           q_blocks=qblocks, o=o_host)
     for i, (rows, ref) in oq.items():
-        assert_bf16_close(dq[0, rows], ref, f"dQ block {i}")
+        assert_grad_close(dq[0, rows], ref, f"dQ block {i}")
+    # the backward's inputs O and lse are the GPU forward's, checked above on
+    # every row; the reference is the exact gradient given them (P from the
+    # given lse, D from the given O), and the figure against the oracle's own
+    # O and lse is printed beside it
     kblocks = [0, M - 1] + [int(x) for x in rng.choice(np.arange(1, M - 1), 4, replace=False)]
-    ok = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, o_host, keep["lse"], lists,
-                                           scale, 0, kblocks)
+    ok = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, o_host, lse_r, lists, scale, 0,
+                                           kblocks)
     for j, (rows, rdk, rdv) in ok.items():
-        assert_bf16_close(dk[0, rows], rdk, f"dK block {j}")
-        assert_bf16_close(dv[0, rows], rdv, f"dV block {j}")
+        assert_grad_close(dk[0, rows], rdk, f"dK block {j}")
+        assert_grad_close(dv[0, rows], rdv, f"dV block {j}")
+    ok = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, keep["o"], keep["lse"], lists,
+                                           scale, 0, kblocks[:2])
+    for j, (rows, rdk, rdv) in ok.items():
+        for n, got, ref in (("dK", dk[0, rows], rdk), ("dV", dv[0, rows], rdv)):
+            mx, rel = grad_stats(got, ref)
+            print(f"[full lists] {n} block {j} against the oracle's own O and lse: max-abs "
+                  f"{mx:.3g} (max |ref| {np.abs(ref).max():.3g}), L1 {rel:.3g}", flush=True)
 
 
 # ------------------------------------------------------------- zone scoring --
@@ -635,9 +647,10 @@ def test_full_size_workload(name):
     evaluator over all N keys under the explicit mask; every real output row
     finite (outputs start as NaN). The 2K workload adds the backward: dQ on 16
     query blocks and dK, dV on 16 key blocks of every head (the longest list,
-    a partial block and the last block among them), against the oracle given
-    the GPU forward's O (the backward's input) and the oracle's own lse; the
-    same gradients against the exact oracle (its own O) are printed."""
+    a partial block and the last block among them), against the exact
+    gradient given the GPU forward's O and lse (the backward's inputs, both
+    checked against the oracle on every row just before); the same gradients
+    against the exact oracle (its own O and lse) are printed."""
     wl = synth.WORKLOADS[name]
     print(f"\n[{name}] generating inputs", flush=True)
     parts = ("q", "k", "v") + (("video", "audio") if wl.mode == "dynamic" else ()) + \
@@ -729,13 +742,14 @@ def test_full_size_workload(name):
     def one(item):
         h, kind, blocks = item
         out = []
-        for o_in in (o_host, keep["o"]):    # the backward's input O, then the exact O
+        # the backward's inputs (the GPU forward's O and lse), then the oracle's own
+        for o_in, l_in in ((o_host, lse_host), (keep["o"], keep["lse"])):
             if kind == "q":
                 oq, _ = oatt.attn_bwd_gathered_blocks(L, perm, q, k, v, do, lists, scale, h,
                                                       q_blocks=blocks, o=o_in)
                 out.append([("dQ", dq[h, rows], ref) for rows, ref in oq.values()])
             else:
-                okb = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, o_in, keep["lse"],
+                okb = oatt.attn_bwd_key_blocks_from_lse(L, perm, q, k, v, do, o_in, l_in,
                                                         lists, scale, h, blocks)
                 out.append([(n, got[h, rows], ref) for rows, rdk, rdv in okb.values()
                             for n, got, ref in (("dK", dk, rdk), ("dV", dv, rdv))])
@@ -743,10 +757,10 @@ def test_full_size_workload(name):
 
     worst = {}
     for h, (given, exact_o) in parallel_map(one, items):
-        for tag, comps in (("given O", given), ("exact O", exact_o)):
+        for tag, comps in (("given O, lse", given), ("exact O, lse", exact_o)):
             for n, got, ref in comps:
-                if tag == "given O":
-                    assert_bf16_close(got, ref, f"{n} head {h}")
+                if tag == "given O, lse":
+                    assert_grad_close(got, ref, f"{n} head {h}")
                 mxg, relg = grad_stats(got, ref)
                 w = worst.setdefault((tag, n), [0.0, 0.0])
                 w[0], w[1] = max(w[0], mxg), max(w[1], relg)
