@@ -153,12 +153,39 @@ __device__ inline bf16x4 tr_read(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// S^T = K Q^T for this wave's 64 keys of the block in `sk` (two 32x32 tiles).
-// The K fragments are requested four k-steps (eight products) ahead of the
-// products that consume them.
+// The validity words of one key block for this wave's 64 keys.
+struct HalfMeta {
+  uint32_t w0, w1;  // bits of keys 64kh + 0..31 and 64kh + 32..63
+  int count;        // real slots of the block (128 = full, no pad keys)
+};
+
+// Pad keys of a partial key block get the score -2^30 from the matrix unit
+// instead of a per-score mask: the S^T accumulators start from one product
+// whose A operand holds, in k-column 0 of key row l32, 0 for a real key and
+// -2^30 for a pad key, and whose B operand holds 1 in k-row 0 of every query
+// column (pad_bias_b). Real keys start from an exact 0, so their scores are
+// bit-identical to a zero start; a pad key's score is -2^30 (about -1.4e8 in
+// the exponent's units once scaled), whose exponential is exactly 0 next to
+// any real key of the row. Per 32-key tile this is one product and two
+// instructions to form the operand, in place of three instructions per score.
+__device__ inline bf16x8 pad_bias_a(uint32_t word, int l32, int hi) {
+  const bool pad = hi == 0 && !((word >> l32) & 1u);
+  const u32x4 v = {pad ? 0xCE80u : 0u, 0u, 0u, 0u};  // element 0: bf16 -2^30 or 0
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline bf16x8 pad_bias_b(int hi) {
+  const u32x4 v = {hi == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};  // element 0: bf16 1.0 or 0
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// S^T = K Q^T for this wave's 64 keys of the block in `sk` (two 32x32 tiles),
+// starting from the pad-key bias when the block is partial. The K fragments
+// are requested four k-steps (eight products) ahead of the products that
+// consume them.
 template <typename Hook>
 __device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int kswz_lane,
-                                const bf16x8 (&qf)[8], int hi, Hook hook) {
+                                const bf16x8 (&qf)[8], int l32, int hi, const HalfMeta& m,
+                                const bf16x8& bias_b, Hook hook) {
   bf16x8 a[8][2];
   auto load = [&](int st) {
 #pragma unroll
@@ -169,10 +196,16 @@ __device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int 
 #pragma unroll
   for (int st = 0; st < 4; ++st) load(st);
   sched_fence();
+  if (__builtin_amdgcn_readfirstlane(m.count) < kB) {
+    const f32x16 zero = {};
+    s[0] = mfma32x32x16(pad_bias_a(m.w0, l32, hi), bias_b, zero);
+    s[1] = mfma32x32x16(pad_bias_a(m.w1, l32, hi), bias_b, zero);
+  } else {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+  }
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
 #pragma unroll
@@ -180,25 +213,6 @@ __device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int 
     if (st + 4 < 8) load(st + 4);
     hook(st);
     sched_fence();
-  }
-}
-
-// The validity words of one key block for this wave's 64 keys.
-struct HalfMeta {
-  uint32_t w0, w1;  // bits of keys 64kh + 0..31 and 64kh + 32..63
-  int count;        // real slots of the block (128 = full, no masking)
-};
-
-// Pad keys of a partial key block: bit r of the block's mask = slot r real.
-// Lane (l32, hi) holds keys 64kh + 32kt + 8(r/4) + 4hi + r%4 in element r.
-__device__ inline void mask_pad_keys(f32x16 (&s)[2], const HalfMeta& m, int hi) {
-  if (__builtin_amdgcn_readfirstlane(m.count) >= 128) return;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const uint32_t word = (kt ? m.w1 : m.w0) >> (4 * hi);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (!((word >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = -INFINITY;
   }
 }
 
@@ -326,6 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   for (int t = 0; t < 4; ++t)
     voff[t] = (64 * kh + 4 * hi + vy) * kD + 8 * (4 * (t ^ vy) + vx) + 4 * (u & 1);
 
+  const bf16x8 bias_b = pad_bias_b(hi);
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -424,8 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // the one that read it, past that iteration's closing barrier.
   auto walk = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
-    qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, hi, no_hook);
-    mask_pad_keys(s_cur, meta_j, hi);
+    qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, l32, hi, meta_j, bias_b, no_hook);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
     bf16x8 pf8[4];
@@ -456,15 +470,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
         pv_tiles(o, sV[cb], voff, pf8, no_hook);
         rowsum(pf8);
         if (more1) {
-          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, no_hook);
-          mask_pad_keys(s_cur, meta_n, hi);
+          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, no_hook);
         }
       } else {
         pv_tiles(o, sV[cb], voff, pf8, no_hook);
         rowsum(pf8);
         if (more1) {
-          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, hi, no_hook);
-          mask_pad_keys(s_cur, meta_n, hi);
+          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, no_hook);
         }
         if (more1) softmax(pf8, no_hook);
       }
