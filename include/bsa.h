@@ -277,6 +277,23 @@ bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const vo
                         const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
                         float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* bsa_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument, and the call allocates nothing. The per-block table
+ * lives in a static device array of the library (BSA_MAX_BLOCKS x 32 bytes =
+ * 128 KiB, enough for every layout the library accepts; BSA_LAYOUT if a layout
+ * ever needed more), one per GPU, held until the process ends. Its device
+ * address is looked up once per device, on the first call there. Every call on
+ * a GPU shares that GPU's array and rewrites the part it uses before reading
+ * it; calls that overlap in time on one GPU (concurrent streams, or threads)
+ * race on it and must be ordered by the caller. Arguments, outputs and
+ * arithmetic are those of bsa_attn_fwd; this is the one call that keeps state
+ * (the array and the per-device addresses) across calls. */
+bsa_status bsa_attn_fwd_noalloc(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                                const void* kp, const void* vp, const int32_t* counts,
+                                const int32_t* idx, int heads, int d, int dtype, float scale,
+                                void* op, float* lse, void* stream);
+
 /* bsa_attn_fwd writing O and lse straight in raster token order (so that the
  * forward path needs no bsa_unpermute of O):
  *  o    [heads, N, d] out, the rows of the real tokens (every one is written)

@@ -141,6 +141,25 @@ def test_attn_fwd_rejects_misaligned_tensors(lib):
     assert "aligned" in lib.bsa_last_error().decode()
 
 
+def test_attn_fwd_noalloc_validation(lib):
+    """The allocation-free forward validates like bsa_attn_fwd before it
+    touches the device (no GPU here: a valid call would fail at the device
+    lookup, never before)."""
+    c = LAY.c()
+
+    def call(q=FAKE, d=128, dt=1, scale=0.0, zs=FAKE, L=c):
+        return lib.bsa_attn_fwd_noalloc(ctypes.byref(L), zs, q, FAKE, FAKE, FAKE, FAKE, 2, d, dt,
+                                        scale, FAKE, FAKE, None)
+
+    assert call(q=None) == _lib.BSA_INVALID_ARG
+    assert call(q=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG
+    assert call(d=32) == _lib.BSA_UNSUPPORTED
+    assert call(dt=3) == _lib.BSA_INVALID_ARG
+    assert call(scale=float("nan")) == _lib.BSA_INVALID_ARG
+    assert call(L=DYN.c(), zs=None) == _lib.BSA_INVALID_ARG
+    assert call() == _lib.BSA_HIP_ERROR and "scratch" in lib.bsa_last_error().decode()
+
+
 def test_attn_fwd_raster_validation(lib):
     c = LAY.c()
 

@@ -374,7 +374,8 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
                                   const void* qp, const void* kp, const void* vp,
                                   const int32_t* counts, const int32_t* idx, int heads, int d,
                                   int dtype, float scale, void* op, float* lse, void* ws,
-                                  size_t ws_bytes, void* stream, bool raster) {
+                                  size_t ws_bytes, void* stream, bool raster,
+                                  bool static_scratch = false) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
@@ -391,6 +392,16 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
     return fail(BSA_INVALID_ARG, "zone_shape is NULL in dynamic mode");
   if (!(scale >= 0.f) || isinf(scale)) return fail(BSA_INVALID_ARG, "scale must be finite and >= 0");
   const size_t need = bsa::attn_fwd_workspace(L, d, dtype == BSA_BF16);
+  if (static_scratch) {
+    // the library's own scratch array replaces the caller's workspace
+    size_t have = 0;
+    const hipError_t e = bsa::attn_fwd_static_scratch(&ws, &have);
+    if (e != hipSuccess) return hip_status(e, "attn_fwd_noalloc scratch lookup");
+    if (need > have)
+      return fail(BSA_LAYOUT, "attn_fwd_noalloc: the block table needs %zu bytes, its static "
+                  "scratch holds %zu", need, have);
+    ws_bytes = have;
+  }
   if (need && (!ws || ws_bytes < need))
     return fail(BSA_WORKSPACE_TOO_SMALL, "attn_fwd needs %zu workspace bytes, got %zu", need, ws_bytes);
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
@@ -406,6 +417,14 @@ bsa_status bsa_attn_fwd(const bsa_layout* in, const int32_t* zone_shape, const v
                         float* lse, void* ws, size_t ws_bytes, void* stream) {
   return attn_fwd_common(in, zone_shape, qp, kp, vp, counts, idx, heads, d, dtype, scale, op,
                          lse, ws, ws_bytes, stream, false);
+}
+
+bsa_status bsa_attn_fwd_noalloc(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                                const void* kp, const void* vp, const int32_t* counts,
+                                const int32_t* idx, int heads, int d, int dtype, float scale,
+                                void* op, float* lse, void* stream) {
+  return attn_fwd_common(in, zone_shape, qp, kp, vp, counts, idx, heads, d, dtype, scale, op,
+                         lse, nullptr, 0, stream, false, true);
 }
 
 bsa_status bsa_attn_fwd_raster(const bsa_layout* in, const int32_t* zone_shape, const void* qp,

@@ -22,6 +22,8 @@
 //  * attn_fwd_scalar: any dtype (fp32 / bf16), d in {64, 128}, B in {64, 128}.
 //    One thread per query slot, fp32 online softmax, K/V staged through LDS as
 //    fp32. This is the exact-parity path (fp32 inputs) and the fallback.
+#include <mutex>
+
 #include "attn_common.hpp"
 #include "bsa.h"
 #include "kernels.hpp"
@@ -561,7 +563,35 @@ hipError_t launch_scalar(const Lay& L, const int32_t* zone_shape, const void* qp
   return hipGetLastError();
 }
 
+// Scratch memory of the allocation-free forward: the per-block table for the
+// largest layout the library takes (BSA_MAX_BLOCKS blocks of 32 bytes,
+// 128 KiB). Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device
+// array: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)BSA_MAX_BLOCKS * sizeof(BlockMeta);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+hipError_t attn_fwd_static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(lock);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16) { return bf16 && d == kD && L.B == kB; }
 

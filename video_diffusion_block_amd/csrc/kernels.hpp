@@ -65,6 +65,10 @@ hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* 
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
                            void* op, float* lse, void* ws, hipStream_t st, bool raster = false);
 
+// Device address and size of the forward's static scratch array on the
+// current device (looked up once per device; no allocation).
+hipError_t attn_fwd_static_scratch(void** ptr, size_t* bytes);
+
 // Attention backward.
 size_t attn_bwd_workspace(const Lay& L, int heads, int d);
 hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* qp,

@@ -290,6 +290,27 @@ def attn_fwd(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: floa
     return op, lse
 
 
+def attn_fwd_noalloc(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx,
+                     scale: float = 0.0, out=None):
+    """bsa_attn_fwd_noalloc: bsa_attn_fwd with the library's static scratch
+    instead of a workspace (the C call allocates nothing). ``out``: (op, lse)
+    to write into, else they are allocated here like bsa_attn_fwd's."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp, vp, counts, idx)
+    H, Np, d = qp.shape
+    if out is None:
+        op = _empty(qp.shape, qp.dtype, qp.device)
+        lse = _empty((H, Np), torch.float32, qp.device)
+    else:
+        op, lse = out
+        _dev(op, lse)
+    L = layout.c()
+    _lib.check("bsa_attn_fwd_noalloc", lib.bsa_attn_fwd_noalloc(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(counts),
+        _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(op), _ptr(lse), _stream()))
+    return op, lse
+
+
 def attn_fwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scale: float = 0.0):
     """bsa_attn_fwd_raster: o [H, N, d] (raster token order, input dtype) and
     lse [H, N] float32."""
