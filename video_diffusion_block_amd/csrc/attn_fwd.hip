@@ -180,6 +180,52 @@ __device__ inline bf16x8 pad_bias_b(int hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The first four k-steps' K fragments of S^T (for qk_tiles_pre), requested
+// by the caller during the products before it.
+__device__ inline void k_frags(bf16x8 (&a)[4][2], const __bf16* sk, int koff, int kswz_lane, int hi,
+                               int st0) {
+#pragma unroll
+  for (int st = st0; st < st0 + 2; ++st)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      a[st][kt] = *reinterpret_cast<const bf16x8*>(sk + koff + 32 * kt * kD +
+                                                   8 * ((2 * st + hi) ^ kswz_lane));
+}
+template <typename Hook>
+__device__ inline void qk_tiles_pre(f32x16 (&s)[2], const __bf16* sk, int koff, int kswz_lane,
+                                    const bf16x8 (&qf)[8], int l32, int hi, const HalfMeta& m,
+                                    const bf16x8& bias_b, const bf16x8 (&pre)[4][2], Hook hook) {
+  bf16x8 a[8][2];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      a[st][kt] = *reinterpret_cast<const bf16x8*>(sk + koff + 32 * kt * kD +
+                                                   8 * ((2 * st + hi) ^ kswz_lane));
+  };
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) a[st][kt] = pre[st][kt];
+  if (__builtin_amdgcn_readfirstlane(m.count) < kB) {
+    const f32x16 zero = {};
+    s[0] = mfma32x32x16(pad_bias_a(m.w0, l32, hi), bias_b, zero);
+    s[1] = mfma32x32x16(pad_bias_a(m.w1, l32, hi), bias_b, zero);
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+  }
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[st][kt], qf[st], s[kt]);
+    if (st + 4 < 8) load(st + 4);
+    hook(st);
+    sched_fence();
+  }
+}
+
 // S^T = K Q^T for this wave's 64 keys of the block in `sk` (two 32x32 tiles),
 // starting from the pad-key bias when the block is partial. The K fragments
 // are requested four k-steps (eight products) ahead of the products that
@@ -430,10 +476,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // K_{j+1} and V_j, and requests K_{j+2} and V_{j+1} (into the buffers that
   // K_j and V_{j-1} left in iteration j-1) and the facts of block j+2; all of
   // them are waited for at its end, before its one barrier. Only the kh = 0
-  // waves issue these loads, spread over their exponentials: the global-to-LDS
+  // waves issue these loads, one every two exponentials: the global-to-LDS
   // path drains about 64 bytes per clock per CU, a wave that issues into a
   // full queue stalls, and the exponentiating wave has slack where the matrix
-  // wave has none.
+  // wave has none. The loads carry no branch (a branch between the
+  // exponentials lets the compiler sink the exponentials past all sixteen
+  // loads, which then leave as one burst and stall the wave for about a
+  // thousand cycles). In the matrix half, the last two d-tiles of PV_j request
+  // the first four k-steps of K fragments of S_{j+1}, so the S products start
+  // without waiting on LDS.
   // Buffer ownership: iteration 0 refills sK[0] (with K_2) and sM[0] (with the
   // facts of block 2), which every wave reads before the loop (S_0 and block 0's
   // facts); the barrier after S_0 keeps those refills behind the last of
@@ -457,28 +508,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
       const u32x3 mraw = *reinterpret_cast<const u32x3*>(&sM[nb][4 * kh]);
       // wave w (kh = 0) fills parts (w, m) and (w + 4, m) of K_{j+2} and V_{j+1}
+      // Issued unconditionally (no branch between the exponentials, so the
+      // loads stay spread over them): past the end of the list b1 and b2 repeat
+      // the last block, and the buffers they fill are free and never read again.
       auto dma_hook = [&](int k) {
         const int ww = w + 4 * (k & 1), m = (k >> 1) & 3;
-        if (k < 8) {
-          if (more2) dma_part<false>(sK[cb], krs, b2 * kTileBytes, ww, lane, m);
-        } else {
-          if (more1) dma_part<true>(sV[nb], vrs, b1 * kTileBytes, ww, lane, m);
-        }
+        if (k < 8)
+          dma_part<false>(sK[cb], krs, b2 * kTileBytes, ww, lane, m);
+        else
+          dma_part<true>(sV[nb], vrs, b1 * kTileBytes, ww, lane, m);
       };
       if (KH == 0 && more2) fetch_meta(b2, cb);
       const HalfMeta meta_n{mraw.x, mraw.y, (int)mraw.z};
       if (KH == 0) {
         softmax(pf8, dma_hook);
-        pv_tiles(o, sV[cb], voff, pf8, no_hook);
+        bf16x8 kpre[4][2];
+        auto kpre_hook = [&](int t) {
+          if (t >= 2) k_frags(kpre, sK[nb], koff, kswz_lane, hi, 2 * (t - 2));
+        };
+        pv_tiles(o, sV[cb], voff, pf8, kpre_hook);
         rowsum(pf8);
         if (more1) {
-          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, no_hook);
+          qk_tiles_pre(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, kpre, no_hook);
         }
       } else {
-        pv_tiles(o, sV[cb], voff, pf8, no_hook);
+        bf16x8 kpre[4][2];
+        auto kpre_hook = [&](int t) {
+          if (t >= 2) k_frags(kpre, sK[nb], koff, kswz_lane, hi, 2 * (t - 2));
+        };
+        pv_tiles(o, sV[cb], voff, pf8, kpre_hook);
         rowsum(pf8);
         if (more1) {
-          qk_tiles(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, no_hook);
+          qk_tiles_pre(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, kpre, no_hook);
         }
         if (more1) softmax(pf8, no_hook);
       }
