@@ -22,9 +22,12 @@ namespace {
 // ------------------------------------------------------ D = rowsum(dO * O) --
 // G = d / (elements per 16 bytes) lanes per row (8, 16 or 32), one 16-byte
 // chunk of O and dO each; the row sum is a shuffle reduction inside the group.
+// Also writes lse2 = lse log2(e), the row's lse in the units of the matrix
+// kernels' base-2 exponentials (one multiply per row instead of one per score).
 template <typename T>
-__global__ __launch_bounds__(256) void delta_kernel(const T* op, const T* dop, int d,
-                                                    long long rows, float* delta) {
+__global__ __launch_bounds__(256) void delta_kernel(const T* op, const T* dop, const float* lse,
+                                                    int d, long long rows, float* delta,
+                                                    float* lse2) {
   constexpr int EPC = 16 / sizeof(T);
   const int G = d / EPC;
   const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / G;
@@ -44,7 +47,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* op, const T* dop, i
     for (int i = 0; i < 4; ++i) acc += a[i] * b[i];
   }
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (ok && c == 0) delta[r] = acc;
+  if (ok && c == 0) {
+    delta[r] = acc;
+    lse2[r] = lse[r] * kLog2e;
+  }
 }
 
 // ------------------------------------------------ list transpose (CSR->CSC) --
@@ -270,7 +276,7 @@ __device__ inline void tr_offsets(int (&o1)[4], int (&o2)[4], int row0, int lane
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
-    const __bf16* __restrict__ dop, const float* __restrict__ lse,
+    const __bf16* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dqp) {
   __shared__ __align__(16) __bf16 sK[2][kTile];
@@ -329,8 +335,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     dof[s] = *reinterpret_cast<const bf16x8*>(dop + qrow * kD + 16 * s + 8 * hi);
   }
   const float c2 = scale * kLog2e;
-  const float lse2 = lse[qrow] * kLog2e;
+  const float lq2 = lse2[qrow];
   const float dq_d = delta[qrow];
+  const bf16x8 bias_b = pad_bias_b(hi);
 
   const int rowA = 64 * kh + l32;          // row-read operand rows (+32 kt)
   const int fA = uswz_f(l32);
@@ -364,8 +371,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
         dma_part(sK[b ^ 1], krs, bn * kTile * 2, 2 * kt + 1);
         if (kt == 0) fetch_meta(bn, b ^ 1);
       }
+      if (partial) {
+        const f32x16 zero = {};
+        st[kt] = mfma32x32x16(pad_bias_a(kt ? mw1 : mw0, l32, hi), bias_b, zero);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kt][r] = dpt[kt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpt[kt][r] = 0.f;
       const int ro = (rowA + 32 * kt) * kD;
       bf16x8 fa[8], fb[8];
 #pragma unroll
@@ -383,11 +397,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     bf16x8 dsf[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint32_t word = (kt ? mw1 : mw0) >> (4 * hi);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2_fast(fmaf(st[kt][r], c2, -lse2));
-        if (partial && !((word >> (8 * (r >> 2) + (r & 3))) & 1u)) p = 0.f;
+        const float p = exp2_fast(fmaf(st[kt][r], c2, -lq2));  // 0 for pad keys
         dsf[2 * kt + (r >> 3)][r & 7] = (__bf16)(p * (dpt[kt][r] - dq_d));
       }
     }
@@ -452,7 +464,7 @@ constexpr int kMaxList = BSA_MAX_BLOCKS;
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
-    const __bf16* __restrict__ dop, const float* __restrict__ lse,
+    const __bf16* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ tcounts,
     const int32_t* __restrict__ tidx, float scale, float* __restrict__ dkp,
     float* __restrict__ dvp) {
@@ -481,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
     const i32x4 qrs = make_buffer_rsrc(qp + head0 * kD, head_bytes);
     const i32x4 ors = make_buffer_rsrc(dop + head0 * kD, head_bytes);
-    const i32x4 lrs = make_buffer_rsrc(lse + head0, (uint32_t)L.Np * 4);
+    const i32x4 lrs = make_buffer_rsrc(lse2 + head0, (uint32_t)L.Np * 4);
     const i32x4 drs = make_buffer_rsrc(delta + head0, (uint32_t)L.Np * 4);
     // tile load m (0..7) of wave w: LDS slots (4m + w) * 64 + lane, i.e. row
     // 4 (4m + w) + lane / 16, physical chunk lane % 16 (swizzled fetch)
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
       const int q = (lane & 15) ^ uswz_f(r);
       dma16_manual(rs, lds_addr_of(tile + (4 * m + w) * 512), 2 * (r * kD + 8 * q), src);
     };
-    // the 128 lse and delta values of query block ib (512 bytes each): waves 0, 1, lanes 0..31
+    // the 128 lse2 and delta values of query block ib (512 bytes each): waves 0, 1, lanes 0..31
     auto dma_stats = [&](int buf, int ib) {
       if (w < 2 && lane < 32)
         dma16_manual(w == 0 ? lrs : drs, lds_addr_of(w == 0 ? &sL[buf][0] : &sD[buf][0]),
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int r = 4 * g + rr;
-            const float p = exp2_fast(fmaf(sc[r], c2, -l4[g][rr] * kLog2e));
+            const float p = exp2_fast(fmaf(sc[r], c2, -l4[g][rr]));
             pf[r >> 3][r & 7] = (__bf16)p;
             dsf[r >> 3][r & 7] = (__bf16)(p * (dpc[r] - d4[g][rr]));
           }
@@ -698,14 +710,14 @@ hipError_t launch_bwd_scalar(const Lay& L, const int32_t* zs, const T* q, const 
 
 }  // namespace
 
-// Workspace: delta [H, Np] f32 | bitmap [H, M, words] u32 | tcounts [H, M] |
-// tidx [H, M, M] | block table [M]
+// Workspace: delta [H, Np] f32 | lse2 [H, Np] f32 | bitmap [H, M, words] u32 |
+// tcounts [H, M] | tidx [H, M, M] | block table [M]
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attn_bwd_workspace(const Lay& L, int heads, int d) {
   (void)d;
   const size_t words = (L.M + 31) / 32;
-  return align256((size_t)heads * L.Np * sizeof(float)) +
+  return 2 * align256((size_t)heads * L.Np * sizeof(float)) +
          align256((size_t)heads * L.M * words * sizeof(uint32_t)) +
          align256((size_t)heads * L.M * sizeof(int32_t)) +
          align256((size_t)heads * L.M * L.M * sizeof(int32_t)) +
@@ -721,6 +733,8 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   char* p = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(p);
   p += align256((size_t)heads * L.Np * sizeof(float));
+  float* lse2 = reinterpret_cast<float*>(p);
+  p += align256((size_t)heads * L.Np * sizeof(float));
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)heads * L.M * words * sizeof(uint32_t));
   int32_t* tcounts = reinterpret_cast<int32_t*>(p);
@@ -734,10 +748,12 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   const unsigned dgrid = (unsigned)((rows * lanes_per_row + 255) / 256);
   if (bf16)
     delta_kernel<__bf16><<<dgrid, 256, 0, st>>>(static_cast<const __bf16*>(op),
-                                                  static_cast<const __bf16*>(dop), d, rows, delta);
+                                                  static_cast<const __bf16*>(dop), lse, d, rows,
+                                                  delta, lse2);
   else
     delta_kernel<float><<<dgrid, 256, 0, st>>>(static_cast<const float*>(op),
-                                                 static_cast<const float*>(dop), d, rows, delta);
+                                                 static_cast<const float*>(dop), lse, d, rows,
+                                                 delta, lse2);
   bitmap_kernel<<<dim3(L.M, heads), 256, 0, st>>>(L, counts, idx, words, bitmap);
   transpose_kernel<<<dim3(L.M, heads), 256, 0, st>>>(L, bitmap, words, tcounts, tidx);
   hipError_t e = hipGetLastError();
@@ -750,11 +766,11 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
     const __bf16* k = static_cast<const __bf16*>(kp);
     const __bf16* v = static_cast<const __bf16*>(vp);
     const __bf16* dO = static_cast<const __bf16*>(dop);
-    attn_bwd_dkdv_mfma<<<dim3(L.M, heads), 256, 0, st>>>(L, meta, q, k, v, dO, lse, delta,
+    attn_bwd_dkdv_mfma<<<dim3(L.M, heads), 256, 0, st>>>(L, meta, q, k, v, dO, lse2, delta,
                                                         tcounts, tidx, scale,
                                                         static_cast<float*>(dkp),
                                                         static_cast<float*>(dvp));
-    attn_bwd_dq_mfma<<<dim3(L.M, heads), 512, 0, st>>>(L, meta, q, k, v, dO, lse, delta, counts,
+    attn_bwd_dq_mfma<<<dim3(L.M, heads), 512, 0, st>>>(L, meta, q, k, v, dO, lse2, delta, counts,
                                                       idx, scale, static_cast<float*>(dqp));
     return hipGetLastError();
   }

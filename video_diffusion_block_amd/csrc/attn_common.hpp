@@ -38,6 +38,27 @@ __device__ inline f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pad keys of a partial key block get the score -2^30 from the matrix unit
+// instead of a per-score mask (forward and dQ kernels, whose score tiles are
+// S^T, keys by queries): the S^T accumulators start from one product
+// whose A operand holds, in k-column 0 of key row l32, 0 for a real key and
+// -2^30 for a pad key, and whose B operand holds 1 in k-row 0 of every query
+// column (pad_bias_b). Real keys start from an exact 0, so their scores are
+// bit-identical to a zero start; a pad key's score is -2^30 (about -1.4e8 in
+// the exponent's units once scaled), whose exponential is exactly 0 whatever
+// is subtracted from it (a real key's running maximum in the forward, the
+// row's lse in the dQ kernel). Per 32-key tile this is one product and two
+// instructions to form the operand, in place of three instructions per score.
+__device__ inline bf16x8 pad_bias_a(uint32_t word, int l32, int hi) {
+  const bool pad = hi == 0 && !((word >> l32) & 1u);
+  const u32x4 v = {pad ? 0xCE80u : 0u, 0u, 0u, 0u};  // element 0: bf16 -2^30 or 0
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline bf16x8 pad_bias_b(int hi) {
+  const u32x4 v = {hi == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};  // element 0: bf16 1.0 or 0
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Work item of a workgroup of a 2-D grid (x fastest), in an L2-aware order:
 // workgroups are handed to the 8 XCDs round-robin (dispatch b runs on XCD
 // b % 8, each XCD with its own L2), so inside every window of 256 dispatches

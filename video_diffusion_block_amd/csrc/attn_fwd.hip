@@ -161,25 +161,6 @@ struct HalfMeta {
   int count;        // real slots of the block (128 = full, no pad keys)
 };
 
-// Pad keys of a partial key block get the score -2^30 from the matrix unit
-// instead of a per-score mask: the S^T accumulators start from one product
-// whose A operand holds, in k-column 0 of key row l32, 0 for a real key and
-// -2^30 for a pad key, and whose B operand holds 1 in k-row 0 of every query
-// column (pad_bias_b). Real keys start from an exact 0, so their scores are
-// bit-identical to a zero start; a pad key's score is -2^30 (about -1.4e8 in
-// the exponent's units once scaled), whose exponential is exactly 0 next to
-// any real key of the row. Per 32-key tile this is one product and two
-// instructions to form the operand, in place of three instructions per score.
-__device__ inline bf16x8 pad_bias_a(uint32_t word, int l32, int hi) {
-  const bool pad = hi == 0 && !((word >> l32) & 1u);
-  const u32x4 v = {pad ? 0xCE80u : 0u, 0u, 0u, 0u};  // element 0: bf16 -2^30 or 0
-  return __builtin_bit_cast(bf16x8, v);
-}
-__device__ inline bf16x8 pad_bias_b(int hi) {
-  const u32x4 v = {hi == 0 ? 0x3F80u : 0u, 0u, 0u, 0u};  // element 0: bf16 1.0 or 0
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // The first four k-steps' K fragments of S^T (for qk_tiles_pre), requested
 // by the caller during the products before it.
 __device__ inline void k_frags(bf16x8 (&a)[4][2], const __bf16* sk, int koff, int kswz_lane, int hi,
