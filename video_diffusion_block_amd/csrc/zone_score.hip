@@ -14,12 +14,17 @@
 //
 // Kernels:
 //  gram_kernel     G = A A^T on bf16 MFMA (exact products, fp32 sums), tiny;
-//                  the upper tile pairs, stored in fp32 MFMA operand order.
+//                  the upper tile pairs, each split into three bf16 pieces
+//                  (hi + mid + lo: 24 significant bits, as many as fp32) in
+//                  the A2V kernel's operand order.
 //  a2v_kernel      per 256 tokens: logits^T = A X^T on bf16 MFMA (exact products,
 //                  fp32 sums), softmax in fp32 registers (lane-local rows), then
-//                  g^2 = p^T G p as Y = G P^T on fp32 MFMA (32x32x2) over the
-//                  upper tile pairs of the symmetric G and a lane-local dot
-//                  with P. Writes g [N] fp32.
+//                  g^2 = p^T G p as Y = G P^T over the upper tile pairs of the
+//                  symmetric G and a lane-local dot with P. Y is formed on
+//                  bf16 MFMA from three-piece splits of G and P (the six
+//                  products whose pieces carry the top 24 bits; exact
+//                  products, fp32 sums), which matches an fp32 product at a
+//                  sixteenth of the matrix-unit time per term. Writes g [N] fp32.
 //  line_kernel     per (zone, 32-channel chunk): the zone is streamed through
 //                  LDS one t-slice at a time; sum x^2 and the squared line sums
 //                  along t, h, w in fp64 (bf16 inputs make these sums exact), so
@@ -40,18 +45,39 @@ namespace {
 constexpr double kTieRel = 1e-6;
 
 // ------------------------------------------------------------- Gram matrix --
-// One wavefront per tile pair (mt, kt), kt >= mt, of G = A A^T on bf16 MFMA
-// (the products of bf16 values are exact and accumulate in fp32; rows past Na
-// read as zero). The tile is stored in the operand order the A2V kernel's
-// fp32 MFMA takes: lane l = 32 hi + l32 of pair p owns 16 consecutive floats,
-// float r = G[32 mt + l32][32 kt + 8 (r / 4) + 4 hi + r % 4]. The MFMA result
-// of rows kt x columns mt has exactly that lane layout (G is symmetric, and
-// G[i][j], G[j][i] are the same products summed in the same order).
+// x = hi + mid + lo with each piece the bf16 rounding of what the previous
+// ones leave (the two subtractions are exact), so the pieces hold the top 24
+// significant bits of x; the residual is below 2^-24 |x|.
+// Element r of a 16-value lane row goes to element r % 8 of piece[k][r / 8].
+__device__ inline void split3(float x, bf16x8 (&piece)[3][2], int r) {
+  const __bf16 hi = (__bf16)x;
+  const float r1 = x - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  piece[0][r >> 3][r & 7] = hi;
+  piece[1][r >> 3][r & 7] = mid;
+  piece[2][r >> 3][r & 7] = (__bf16)(r1 - (float)mid);
+}
+
+// One workgroup of kGramWaves wavefronts per tile pair (mt, kt), kt >= mt, of
+// G = A A^T on bf16 MFMA (the products of bf16 values are exact and accumulate
+// in fp32; rows past Na read as zero). Wavefront u sums the 64-channel chunks
+// u, u + kGramWaves, ...; the partial tiles are added in wavefront order (a
+// fixed order: deterministic). The tile is stored split into three bf16
+// pieces, in the operand order of the A2V kernel's phase 2: lane
+// l = 32 hi + l32 of pair p owns 16 consecutive values of each piece, value
+// r = G[32 mt + l32][32 kt + 8 (r / 4) + 4 hi + r % 4] (values 8s .. 8s + 7
+// are its A operand of k-step s). The MFMA result of rows kt x columns mt
+// has exactly that lane layout (G is symmetric, and G[i][j], G[j][i] are the
+// same products summed in the same order).
+// Layout of the output: [pair][piece: hi, mid, lo][lane][16] bf16.
+constexpr int kGramWaves = 4;
 __host__ __device__ constexpr int gram_pairs(int mt_count) { return mt_count * (mt_count + 1) / 2; }
 
-__global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int mt_count, int C,
-                                                  float* gsw) {
-  const int p = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kGramWaves) void gram_kernel(const __bf16* A, int Na,
+                                                               int mt_count, int C, __bf16* gsw) {
+  __shared__ f32x16 red[kGramWaves - 1][64];
+  const int p = blockIdx.x, lane = threadIdx.x & 63;
+  const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int mt = 0, rem = p;
   while (rem >= mt_count - mt) rem -= mt_count - mt++;
   const int kt = mt + rem;
@@ -61,7 +87,7 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int m
   const __bf16* pb = A + (size_t)rb * C + 8 * hi;
   f32x16 acc = {};
   const bf16x8 zero = {};
-  for (int c = 0; c < C; c += 64) {
+  for (int c = 64 * u; c < C; c += 64 * kGramWaves) {
     bf16x8 a[4], b[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {  // C is a multiple of 64
@@ -71,10 +97,20 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int m
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma32x32x16(a[s], b[s], acc);
   }
-  float4* out = reinterpret_cast<float4*>(gsw + ((size_t)p * 64 + lane) * 16);
+  if (u > 0) red[u - 1][lane] = acc;
+  __syncthreads();
+  if (u != 0) return;
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    out[v] = make_float4(acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]);
+  for (int v = 0; v < kGramWaves - 1; ++v) acc += red[v][lane];
+  bf16x8 pc[3][2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) split3(acc[r], pc, r);
+  bf16x8* out = reinterpret_cast<bf16x8*>(gsw) + (size_t)p * 3 * 128 + 2 * lane;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    out[128 * k] = pc[k][0];
+    out[128 * k + 1] = pc[k][1];
+  }
 }
 
 // --------------------------------------------------------------- A2V norm --
@@ -84,10 +120,10 @@ __global__ __launch_bounds__(64) void gram_kernel(const __bf16* A, int Na, int m
 // wavefronts, streams through LDS in 64-channel chunks, double-buffered, with
 // hand-issued buffer loads (rows past Na read as zero) laid out piece-major
 // ([8-channel piece][audio row]) so the fragment reads are conflict free.
-// Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p on fp32 MFMA over
-// the tile pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice),
-// each pair's G operands read from the operand-ordered copy the Gram kernel
-// writes, straight into registers, one pair ahead.
+// Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p over the tile
+// pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice), each
+// pair's G pieces (the Gram kernel's three-piece split, in operand order)
+// read straight into registers, one pair ahead.
 constexpr int kA2vWaves = 8;
 constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
 constexpr int kCh = 64;               // channels per A chunk
@@ -95,7 +131,7 @@ constexpr int kCh = 64;               // channels per A chunk
 template <int MT>
 __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, int C, long long N,
                                                              const __bf16* A, int Na,
-                                                             const float* gsw, float inv_sqrt_c,
+                                                             const __bf16* gsw, float inv_sqrt_c,
                                                              float* gout) {
   constexpr int NA_PAD = 32 * MT;
   constexpr int SLOTS = 8 * NA_PAD;               // 16-byte slots per A chunk
@@ -206,198 +242,266 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   z += __shfl_xor(z, 32);
 
   // g^2 z^2 = sum over tile pairs of p_mt . (G[mt][kt] p_kt), kt >= mt, the
-  // off-diagonal pairs twice (G is symmetric). Each pair's G operands (16
-  // floats per lane, stored in operand order) are loaded one pair ahead.
-  const float4* gl = reinterpret_cast<const float4*>(gsw) + 4 * lane;
-  float4 gn[4];
+  // off-diagonal pairs twice (G is symmetric). Y = G[mt][kt] P_kt on bf16
+  // MFMA from the three-piece splits of G (stored by the Gram kernel) and of
+  // P_kt (split once per kt): the six products hi.hi, hi.mid, mid.hi, hi.lo,
+  // mid.mid, lo.hi, smallest first. Lane-local element r of acc[kt] is P at
+  // audio 32 kt + 8 (r / 4) + 4 hi + r % 4, the k index the stored G pieces
+  // use, so elements 8s .. 8s + 7 are the B operand of k-step s as they lie.
+  // Each pair's G pieces (six 16-byte loads per lane) are loaded one pair
+  // ahead.
+  const bf16x8* gl = reinterpret_cast<const bf16x8*>(gsw) + 2 * lane;
+  auto gpair = [&](int mt_, int kt_) { return mt_ * MT - mt_ * (mt_ - 1) / 2 + (kt_ - mt_); };
+  auto gload = [&](bf16x8 (&g)[3][2], int pr) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) gn[v] = gl[v];
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) g[k][s] = gl[384 * pr + 128 * k + s];
+  };
+  bf16x8 gn[3][2];
+  gload(gn, 0);
   float gsq = 0.f;
-  int p = 0;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float part = 0.f;
+  for (int kt = 0; kt < MT; ++kt) {
+    bf16x8 pp[3][2];
 #pragma unroll
-    for (int kt = mt; kt < MT; ++kt, ++p) {
-      float gc[16];
+    for (int r = 0; r < 16; ++r) split3(acc[kt][r], pp, r);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        gc[4 * v] = gn[v].x;
-        gc[4 * v + 1] = gn[v].y;
-        gc[4 * v + 2] = gn[v].z;
-        gc[4 * v + 3] = gn[v].w;
-      }
-      if (p + 1 < gram_pairs(MT)) {
+    for (int mt = 0; mt <= kt; ++mt) {
+      bf16x8 gc[3][2];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) gn[v] = gl[256 * (p + 1) + v];
-      }
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) gc[k][s] = gn[k][s];
+      // next pair in this loop order: (mt + 1, kt), else (0, kt + 1)
+      const int nmt = mt < kt ? mt + 1 : 0, nkt = mt < kt ? kt : kt + 1;
+      if (nkt < MT) gload(gn, gpair(nmt, nkt));
       f32x16 y = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        y = __builtin_amdgcn_mfma_f32_32x32x2f32(gc[r], acc[kt][r], y, 0, 0, 0);
+      for (int s = 0; s < 2; ++s) {
+        y = mfma32x32x16(gc[2][s], pp[0][s], y);  // lo . hi
+        y = mfma32x32x16(gc[1][s], pp[1][s], y);  // mid . mid
+        y = mfma32x32x16(gc[0][s], pp[2][s], y);  // hi . lo
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        y = mfma32x32x16(gc[1][s], pp[0][s], y);  // mid . hi
+        y = mfma32x32x16(gc[0][s], pp[1][s], y);  // hi . mid
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) y = mfma32x32x16(gc[0][s], pp[0][s], y);  // hi . hi
       float d = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) d = fmaf(y[r], acc[mt][r], d);
-      part += kt == mt ? d : 2.f * d;
+      gsq += kt == mt ? d : 2.f * d;
     }
-    gsq += part;
   }
   gsq += __shfl_xor(gsq, 32);
   if (hi == 0 && tok_ok) gout[tok] = sqrtf(fmaxf(gsq, 0.f)) / z;
 }
 
 // ------------------------------------------------------- line sum partials --
-// Partials per (zone, chunk of kLC channels): [0] sum x^2, [1..3] sum over the
-// lines along t, h, w of (line sum)^2 / line length, in fp64 (for bf16 inputs
-// the sums and squares are exact; the division by the length is a multiply by
-// its rounded reciprocal). The zone is held in LDS as t-slices of 16 x 16
-// tokens x kLC channels: w- and h-lines are complete inside a slice, t-lines
-// accumulate in registers across slices. bf16 features: the whole zone (up to
-// 4 slices, 64 KB) is requested at once with direct global->LDS loads (pad
-// tokens read as zero through the buffer bounds), so one memory latency is
-// paid per workgroup; the one-channel fp32 field is staged a slice at a time.
-// Each thread owns fixed lines and the workgroup reduction has a fixed order
-// (deterministic).
+// Partials per (zone, chunk of kLC = 32 channels) of the bf16 features: [0]
+// sum x^2, [1..3] sum over the lines along t, h, w of (line sum)^2 / line
+// length, in fp64 (bf16 inputs make the sums and squares exact; the division
+// by the length is a multiply by its rounded reciprocal). The zone's t-slices
+// (16 x 16 tokens x 32 channels, 16 KB each) stream through two LDS buffers
+// with direct global->LDS loads (pad tokens read as zero through the buffer
+// bounds), one slice ahead of the one being summed; 37 KB of LDS lets four
+// workgroups share a CU. Two walks read a
+// slice: thread (h, channel pair) walks its two w-lines (line sums, sum of
+// squares, and the t-line sums of its 16 tokens, kept in registers across
+// slices); thread (w, channel pair) walks its two h-lines. Token (h, w) sits
+// at LDS position 16 h + (w ^ (h & 3)) (64 bytes each), so the four h (or w)
+// values a wavefront reads at once fall in different bank groups: both walks
+// are conflict free. Pad tokens are zero, so their lines add nothing and no
+// masks are needed. The chunk-0 workgroup of a zone also takes the one-channel
+// fp32 field g when one is given (its sums of fp32 values are exact in fp64
+// too). Every reduction has a fixed order (deterministic).
 constexpr int kLC = 32;   // channels per workgroup
-constexpr int kLT = 512;  // threads per workgroup
-constexpr int kTI = 256 * kLC / kLT;  // t-line items per thread
+constexpr int kLT = 256;  // threads per workgroup
 
-template <typename T>
-__global__ __launch_bounds__(kLT) void line_kernel(Lay L, const T* __restrict__ X, int C,
-                                                   double* __restrict__ part) {
-  constexpr bool kDirect = sizeof(T) == 2;  // bf16: whole zone by direct loads
-  constexpr int kSlice = 16 * 16 * kLC;     // elements of one t-slice: [h][w][c]
-  __shared__ __align__(16) T xs[(kDirect ? 4 : 1) * kSlice];
+__device__ inline double wave_sum_f64(double x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__global__ __launch_bounds__(kLT) void line_kernel(Lay L, const __bf16* __restrict__ X, int C,
+                                                   const float* __restrict__ g,
+                                                   double* __restrict__ xpart,
+                                                   double* __restrict__ gpart) {
+  __shared__ __align__(16) uint32_t xs[2][16 * 16 * kLC / 2];  // [buffer][position][16 dwords]
+  __shared__ float gs[4][256];
   __shared__ double red[4][kLT / 64];
   const int z = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int zzt = z / (L.gzh * L.gzw), zzh = (z / L.gzw) % L.gzh, zzw = z % L.gzw;
   const int t0 = zzt * L.zt, h0 = zzh * L.zh, w0 = zzw * L.zw;
   const int vt = imax(0, imin(L.zt, L.T - t0));
   const int vh = imax(0, imin(L.zh, L.H - h0));
   const int vw = imax(0, imin(L.zw, L.W - w0));
-  const int c0 = chunk * kLC;
-  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int NSEG = kLC / EPC;       // 16-byte segments per token
-  const bool vec = (C % EPC) == 0;
   const double inv_vw = vw ? 1.0 / vw : 0.0, inv_vh = vh ? 1.0 / vh : 0.0;
   const double inv_vt = vt ? 1.0 / vt : 0.0;
-  double q = 0.0, rh = 0.0, rw = 0.0;
-  double tacc[kTI];  // t-line sums of items tid + kLT j: channel item % 32, token item / 32
+
+  // Loads of slice tt into buffer buf: load m (0..3) of wave wv fills 16-byte
+  // slots (4 m + wv) * 64 + lane: position slot / 4, channels 8 (slot % 4) ..
+  // +8. Offsets are relative to the zone's first token (the host requires
+  // zt H W C 2 < 2^31); pad and out-of-grid tokens take an offset past the
+  // buffer and read zero.
+  constexpr uint32_t kPadOff = 0x7ffffff0u;  // >= the buffer size below: reads zero
+  const size_t base = (((size_t)t0 * L.H + h0) * L.W + w0) * (size_t)C + (size_t)chunk * kLC;
+  const size_t left = ((size_t)L.N * C - base) * 2;  // bytes from base to X's end
+  const i32x4 rs = make_buffer_rsrc(X + base, (uint32_t)(left < kPadOff ? left : kPadOff));
+  auto issue = [&](int tt, int buf) {
 #pragma unroll
-  for (int j = 0; j < kTI; ++j) tacc[j] = 0.0;
-  if constexpr (kDirect) {
-    // LDS slot s (16 bytes) = token s / NSEG of the zone ([t][h][w]), segment
-    // s % NSEG; wave u % 8 loads slots 64 u .. 64 u + 63. Offsets are relative
-    // to the zone's first token (the host requires zt H W C 2 < 2^31); pad and
-    // out-of-grid tokens take an offset past the buffer and read zero.
-    constexpr uint32_t kPadOff = 0x7ffffff0u;  // >= the buffer size below: reads zero
-    const size_t base = (((size_t)t0 * L.H + h0) * L.W + w0) * (size_t)C + c0;
-    const size_t left = ((size_t)L.N * C - base) * sizeof(T);  // bytes from base to X's end
-    const i32x4 rs = make_buffer_rsrc(X + base, (uint32_t)(left < kPadOff ? left : kPadOff));
-    const int w = tid >> 6, lane = tid & 63;
-    const int units = vt * 256 * NSEG / 64;  // 16 per slice
-    for (int u = w; u < units; u += kLT / 64) {
-      const int sl = 64 * u + lane, k = sl / NSEG, sg = sl % NSEG;
-      const int tt = k >> 8, th = (k >> 4) & 15, tw = k & 15;
+    for (int m = 0; m < 4; ++m) {
+      const int sl = (4 * m + wv) * 64 + lane;
+      const int pos = sl >> 2, th = pos >> 4, tw = (pos & 15) ^ (th & 3);
       const bool real = th < vh && tw < vw;
-      const int off = real ? (int)((((size_t)tt * L.H + th) * L.W + tw) * (size_t)C * 2 + 16 * sg)
+      const int off = real ? (int)((((size_t)tt * L.H + th) * L.W + tw) * (size_t)C * 2 +
+                                   16 * (sl & 3))
                            : (int)kPadOff;
-      dma16_manual(rs, lds_addr_of(xs + (size_t)64 * u * EPC), off, 0);
+      dma16_manual(rs, lds_addr_of(&xs[buf][(4 * m + wv) * 256]), off, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-  }
-  for (int tt = 0; tt < vt; ++tt) {
-    const T* xsl = xs + (kDirect ? tt * kSlice : 0);
-    if constexpr (!kDirect) {
-      __syncthreads();
-      // stage the slice: token k = 16 th + tw, segment sg
-      for (int e = tid; e < 256 * NSEG; e += kLT) {
-        const int k = e / NSEG, sg = e % NSEG;
-        const int th = k >> 4, tw = k & 15;
-        T* dst = xs + k * kLC + sg * EPC;
-        const int cc = c0 + sg * EPC;
-        if (th < vh && tw < vw) {
-          const long long n = ((long long)(t0 + tt) * L.H + (h0 + th)) * L.W + (w0 + tw);
-          if (vec && cc + EPC <= C) {
-            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(X + n * C + cc);
-          } else {
-            for (int qq = 0; qq < EPC; ++qq) dst[qq] = cc + qq < C ? X[n * C + cc + qq] : (T)0.f;
-          }
-        } else {
-          for (int qq = 0; qq < EPC; ++qq) dst[qq] = (T)0.f;
-        }
-      }
-    }
-    if constexpr (!kDirect) __syncthreads();
-    // w-lines (th, c) and h-lines (tw, c) of this slice, one of each per thread
-    {
-      const int item = tid, c = item & 31, l = item >> 5;
-      double sw = 0.0, sh = 0.0;
-      for (int u = 0; u < 16; ++u) {
-        const double xw = (double)(float)xsl[(l * 16 + u) * kLC + c];  // (th = l, tw = u)
-        const double xh = (double)(float)xsl[(u * 16 + l) * kLC + c];  // (th = u, tw = l)
-        sw += xw;
-        q += xw * xw;
-        sh += xh;
-      }
-      rw += l < vh ? sw * sw * inv_vw : 0.0;
-      rh += l < vw ? sh * sh * inv_vh : 0.0;
-    }
+  };
+  issue(0, 0);
+  if (vt > 1) issue(1, 1);
+  // a = h of the w-walk and w of the h-walk; cp = channel pair (dword) of the token
+  const int a = 4 * wv + (lane >> 4), cp = lane & 15;
+  double tacc[16][2];
 #pragma unroll
-    for (int j = 0; j < kTI; ++j) {
-      const int item = tid + kLT * j;
-      tacc[j] += (double)(float)xsl[(item >> 5) * kLC + (item & 31)];
+  for (int u = 0; u < 16; ++u) tacc[u][0] = tacc[u][1] = 0.0;
+  double q = 0.0, rw = 0.0, rh = 0.0;
+  for (int tt = 0; tt < vt; ++tt) {
+    // this wave's loads of slices 0..tt have landed (4 loads per slice), then
+    // every wave's
+    // this wave's loads of slice tt have landed (the next slice's four may
+    // be in flight), then every wave's
+    if (tt + 1 < vt) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    __syncthreads();
+    const uint32_t* sl = xs[tt & 1];
+    double sw0 = 0.0, sw1 = 0.0, sh0 = 0.0, sh1 = 0.0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t vw_ = sl[(16 * a + (u ^ (a & 3))) * 16 + cp];  // token (h = a, w = u)
+      const uint32_t vh_ = sl[(16 * u + (a ^ (u & 3))) * 16 + cp];  // token (h = u, w = a)
+      const double x0 = (double)__uint_as_float(vw_ << 16);
+      const double x1 = (double)__uint_as_float(vw_ & 0xffff0000u);
+      sw0 += x0;
+      sw1 += x1;
+      q = fma(x0, x0, q);
+      q = fma(x1, x1, q);
+      tacc[u][0] += x0;
+      tacc[u][1] += x1;
+      sh0 += (double)__uint_as_float(vh_ << 16);
+      sh1 += (double)__uint_as_float(vh_ & 0xffff0000u);
+    }
+    rw += (sw0 * sw0 + sw1 * sw1) * inv_vw;
+    rh += (sh0 * sh0 + sh1 * sh1) * inv_vh;
+    if (tt + 2 < vt) {
+      __syncthreads();  // every wave is done with this buffer
+      issue(tt + 2, tt & 1);
     }
   }
   double rt = 0.0;
 #pragma unroll
-  for (int j = 0; j < kTI; ++j) rt += tacc[j] * tacc[j] * inv_vt;
-  // workgroup reduction in a fixed order (deterministic)
-  double vals[4] = {q, rt, rh, rw};
+  for (int u = 0; u < 16; ++u) rt += (tacc[u][0] * tacc[u][0] + tacc[u][1] * tacc[u][1]) * inv_vt;
+
+  // workgroup sums in a fixed order: lanes (butterfly), then waves in order
+  auto block_sum4 = [&](const double (&v)[4], double* out) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    double v = vals[k];
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((tid & 63) == 0) red[k][tid >> 6] = v;
+    for (int k = 0; k < 4; ++k) {
+      const double x = wave_sum_f64(v[k]);
+      if (lane == 0) red[k][wv] = x;
+    }
+    __syncthreads();
+    if (tid < 4) {
+      double sres = 0.0;
+      for (int u = 0; u < kLT / 64; ++u) sres += red[tid][u];
+      out[tid] = sres;
+    }
+  };
+  const double vals[4] = {q, rt, rh, rw};
+  block_sum4(vals, xpart + ((size_t)z * nchunks + chunk) * 4);
+
+  if (g == nullptr || chunk != 0) return;
+  // the field g of the zone: thread (h, w) = (tid / 16, tid % 16) stages its
+  // t-line and sums it; threads 0..63 take the w-lines (t, h), 64..127 the
+  // h-lines (t, w)
+  const int gh_ = tid >> 4, gw_ = tid & 15;
+  for (int tt = 0; tt < 4; ++tt) {
+    float v = 0.f;
+    if (tt < vt && gh_ < vh && gw_ < vw)
+      v = g[((long long)(t0 + tt) * L.H + (h0 + gh_)) * L.W + (w0 + gw_)];
+    gs[tt][tid] = v;
   }
-  __syncthreads();
-  if (tid < 4) {
-    double sres = 0.0;
-    for (int v = 0; v < kLT / 64; ++v) sres += red[tid][v];
-    part[((size_t)z * nchunks + chunk) * 4 + tid] = sres;
+  __syncthreads();  // (also: the X sums have read red)
+  double gq = 0.0, gst = 0.0, gsh = 0.0, gsw = 0.0;
+  {
+    double st = 0.0;
+    for (int tt = 0; tt < vt; ++tt) {
+      const double x = gs[tt][tid];
+      st += x;
+      gq = fma(x, x, gq);
+    }
+    gst = st * st * inv_vt;
   }
+  if (tid < 64) {
+    const int tt = tid >> 4, hh = tid & 15;
+    if (tt < vt) {
+      double sres = 0.0;
+      for (int ww = 0; ww < 16; ++ww) sres += gs[tt][16 * hh + ww];
+      gsw = sres * sres * inv_vw;
+    }
+  } else if (tid < 128) {
+    const int tt = (tid - 64) >> 4, ww = tid & 15;
+    if (tt < vt) {
+      double sres = 0.0;
+      for (int hh = 0; hh < 16; ++hh) sres += gs[tt][16 * hh + ww];
+      gsh = sres * sres * inv_vh;
+    }
+  }
+  const double gvals[4] = {gq, gst, gsh, gsw};
+  block_sum4(gvals, gpart + 4 * (size_t)z);
 }
 
 // ------------------------------------------------------------------ decide --
-__global__ __launch_bounds__(256) void decide_kernel(Lay L, int C, int nchunks,
-                                                     const double* xpart, const double* gpart,
-                                                     int use_audio, int32_t* zone_shape,
-                                                     double* zone_stats, double* scratch) {
-  // scratch: V [nZ][3], G [nZ][3], nz [nZ]
+// One workgroup. Phase 1: thread (zone, component) sums the zone's chunk
+// partials of that component in chunk order. Phase 2: per zone V_a, G_a and
+// the size; the means over non-empty (zone, axis) pairs by a fixed-order tree.
+// Phase 3: per zone r_a, the costs and the tie rule. Deterministic.
+constexpr int kDecideThreads = 1024;
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(
+    Lay L, int C, int nchunks, const double* xpart, const double* gpart, int use_audio,
+    int32_t* zone_shape, double* zone_stats, double* scratch) {
+  // scratch: V [nZ][3], G [nZ][3], nz [nZ], chunk sums [nZ][4]
   double* V = scratch;
   double* G = scratch + 3 * L.nZ;
   double* NZ = scratch + 6 * L.nZ;
-  __shared__ double sv[256], sg[256];
-  __shared__ int scount[256];
+  double* S = scratch + 7 * L.nZ;
+  __shared__ double sv[kDecideThreads], sg[kDecideThreads];
+  __shared__ int scount[kDecideThreads];
   const int tid = threadIdx.x;
+  for (int e = tid; e < 4 * L.nZ; e += kDecideThreads) {
+    const double* p = xpart + (size_t)(e >> 2) * nchunks * 4 + (e & 3);
+    double acc = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < nchunks; ++k) acc += p[4 * k];
+    S[e] = acc;
+  }
+  __syncthreads();
   double accv = 0.0, accg = 0.0;
   int cnt = 0;
-  for (int z = tid; z < L.nZ; z += 256) {
+  for (int z = tid; z < L.nZ; z += kDecideThreads) {
     const int zzt = z / (L.gzh * L.gzw), zzh = (z / L.gzw) % L.gzh, zzw = z % L.gzw;
     const int vt = imax(0, imin(L.zt, L.T - zzt * L.zt));
     const int vh = imax(0, imin(L.zh, L.H - zzh * L.zh));
     const int vw = imax(0, imin(L.zw, L.W - zzw * L.zw));
     const double nz = (double)vt * vh * vw;
     NZ[z] = nz;
-    double q = 0.0, r[3] = {0.0, 0.0, 0.0};
-    for (int k = 0; k < nchunks; ++k) {
-      const double* p = xpart + ((size_t)z * nchunks + k) * 4;
-      q += p[0];
-      r[0] += p[1];
-      r[1] += p[2];
-      r[2] += p[3];
-    }
+    const double q = S[4 * z];
+    const double r[3] = {S[4 * z + 1], S[4 * z + 2], S[4 * z + 3]};
     for (int a = 0; a < 3; ++a) {
       V[3 * z + a] = nz > 0 ? (q - r[a]) / ((double)C * nz) : 0.0;
       G[3 * z + a] = (use_audio && nz > 0) ? (gpart[4 * z] - gpart[4 * z + 1 + a]) / nz : 0.0;
@@ -412,7 +516,7 @@ __global__ __launch_bounds__(256) void decide_kernel(Lay L, int C, int nchunks,
   sg[tid] = accg;
   scount[tid] = cnt;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = kDecideThreads / 2; s > 0; s >>= 1) {
     if (tid < s) {
       sv[tid] += sv[tid + s];
       sg[tid] += sg[tid + s];
@@ -422,7 +526,7 @@ __global__ __launch_bounds__(256) void decide_kernel(Lay L, int C, int nchunks,
   }
   const double vbar = scount[0] ? sv[0] / scount[0] : 0.0;
   const double gbar = scount[0] ? sg[0] / scount[0] : 0.0;
-  for (int z = tid; z < L.nZ; z += 256) {
+  for (int z = tid; z < L.nZ; z += kDecideThreads) {
     double r[3];
     for (int a = 0; a < 3; ++a) {
       r[a] = 0.0;
@@ -462,16 +566,19 @@ __global__ void fill_zero_kernel(int32_t* p, int n) {
 }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+// three bf16 pieces of 64 lanes x 16 values per upper tile pair
+size_t gram_bytes(int mt_count) { return (size_t)gram_pairs(mt_count) * 3 * 64 * 16 * 2; }
 
 }  // namespace
 
-// Workspace: g [N] f32 | gram [pad^2] f32 (upper tile pairs use less) | xpart [nZ][chunks][4] | gpart [nZ][4] | scratch [7 nZ]
+// Workspace: g [N] f32 | gram: pairs x 3 pieces x 2 KB bf16 | xpart [nZ][chunks][4] |
+// gpart [nZ][4] | scratch [11 nZ]
 size_t zone_score_workspace(const Lay& L, int C, int n_audio) {
   const int pad = 32 * ((n_audio + 31) / 32);
   const int chunks = (C + kLC - 1) / kLC;
-  return al256((size_t)L.N * sizeof(float)) + al256((size_t)pad * pad * sizeof(float)) +
+  return al256((size_t)L.N * sizeof(float)) + al256(gram_bytes(pad / 32)) +
          al256((size_t)L.nZ * chunks * 4 * sizeof(double)) +
-         al256((size_t)L.nZ * 4 * sizeof(double)) + al256((size_t)L.nZ * 7 * sizeof(double));
+         al256((size_t)L.nZ * 4 * sizeof(double)) + al256((size_t)L.nZ * 11 * sizeof(double));
 }
 
 hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void* audio,
@@ -486,8 +593,8 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
   char* p = static_cast<char*>(ws);
   float* g = reinterpret_cast<float*>(p);
   p += al256((size_t)L.N * sizeof(float));
-  float* gram = reinterpret_cast<float*>(p);
-  p += al256((size_t)pad * pad * sizeof(float));
+  __bf16* gram = reinterpret_cast<__bf16*>(p);
+  p += al256(gram_bytes(pad / 32));
   double* xpart = reinterpret_cast<double*>(p);
   p += al256((size_t)L.nZ * chunks * 4 * sizeof(double));
   double* gpart = reinterpret_cast<double*>(p);
@@ -498,7 +605,7 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
   const bool use_audio = audio != nullptr && n_audio > 0;
   if (use_audio) {
     const __bf16* A = static_cast<const __bf16*>(audio);
-    gram_kernel<<<gram_pairs(pad / 32), 64, 0, st>>>(A, n_audio, pad / 32, C, gram);
+    gram_kernel<<<gram_pairs(pad / 32), 64 * kGramWaves, 0, st>>>(A, n_audio, pad / 32, C, gram);
     const unsigned grid = (unsigned)((L.N + kTok - 1) / kTok);  // C % 64 == 0 (checked)
     const float isc = 1.0f / sqrtf((float)C);
     switch (pad / 32) {
@@ -508,10 +615,9 @@ hipError_t launch_zone_score(const Lay& L, const void* video, int C, const void*
 #undef BSA_A2V
       default: return hipErrorInvalidValue;
     }
-    line_kernel<float><<<dim3(L.nZ, 1), kLT, 0, st>>>(L, g, 1, gpart);
   }
-  line_kernel<__bf16><<<dim3(L.nZ, chunks), kLT, 0, st>>>(L, X, C, xpart);
-  decide_kernel<<<1, 256, 0, st>>>(L, C, chunks, xpart, gpart, use_audio ? 1 : 0, zone_shape,
+  line_kernel<<<dim3(L.nZ, chunks), kLT, 0, st>>>(L, X, C, use_audio ? g : nullptr, xpart, gpart);
+  decide_kernel<<<1, kDecideThreads, 0, st>>>(L, C, chunks, xpart, gpart, use_audio ? 1 : 0, zone_shape,
                                    zone_stats, scratch);
   return hipGetLastError();
 }
