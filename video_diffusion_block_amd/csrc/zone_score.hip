@@ -115,18 +115,22 @@ __global__ __launch_bounds__(64 * kGramWaves) void gram_kernel(const __bf16* A, 
 
 // --------------------------------------------------------------- A2V norm --
 // 8 wavefronts x 32 tokens per workgroup. Phase 1, logits^T = A X^T on bf16
-// MFMA: X fragments are loaded straight into registers (each token row is read
-// once, by its own wavefront) one channel chunk ahead; A, shared by the
-// wavefronts, streams through LDS in 64-channel chunks, double-buffered, with
-// hand-issued buffer loads (rows past Na read as zero) laid out piece-major
-// ([8-channel piece][audio row]) so the fragment reads are conflict free.
+// MFMA over 64-channel chunks, every operand through LDS by hand-issued direct
+// global->LDS loads (the kernel places its own waits, so no load waits for
+// more than the data the next step uses): A, shared by the wavefronts,
+// double-buffered and laid out piece-major ([8-channel piece][audio row], rows
+// past Na read as zero through the buffer bounds) so the fragment reads are
+// conflict free; X, private to each wavefront, in a ring of three chunks
+// (each token row read once, in whole 128-byte pieces; pieces swizzled by
+// token so the fragment reads are conflict free; rows past N read as zero).
 // Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p over the tile
 // pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice), each
 // pair's G pieces (the Gram kernel's three-piece split, in operand order)
 // read straight into registers, one pair ahead.
 constexpr int kA2vWaves = 8;
 constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
-constexpr int kCh = 64;               // channels per A chunk
+constexpr int kCh = 64;               // channels per chunk
+constexpr int kXRing = 3;             // X chunks per wavefront in LDS
 
 template <int MT>
 __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, int C, long long N,
@@ -134,9 +138,11 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
                                                              const __bf16* gsw, float inv_sqrt_c,
                                                              float* gout) {
   constexpr int NA_PAD = 32 * MT;
-  constexpr int SLOTS = 8 * NA_PAD;               // 16-byte slots per A chunk
-  constexpr int ABUF = SLOTS * 8;                  // bf16 elements per A buffer
-  __shared__ __align__(16) __bf16 abuf[2 * ABUF];  // [2][piece][row][8]
+  constexpr int SLOTS = 8 * NA_PAD;  // 16-byte slots per A chunk: 4 MT wave-loads
+  constexpr int ABUF = SLOTS * 8;    // bf16 elements per A buffer
+  constexpr int kAL = (4 * MT + kA2vWaves - 1) / kA2vWaves;  // A wave-loads per wave, at most
+  __shared__ __align__(16) __bf16 abuf[2 * ABUF];                      // [2][piece][row][8]
+  __shared__ __align__(16) __bf16 xbuf[kXRing][kA2vWaves][32 * kCh];  // [ring][wave][token][piece][8]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -144,35 +150,36 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   const long long tok = n0 + l32;
   const bool tok_ok = tok < N;
   const int nchunks = C / kCh;
+  constexpr int kPadOff = 0x7ffffff0;  // an offset past every buffer below: reads zero
 
-  // A chunk ch: LDS slot s = piece * NA_PAD + row <- A[row][64 ch + 8 piece ..]
-  // (zero for rows past Na); thread tid stages slots tid + 512 j.
-  constexpr int kAJ = (SLOTS + 64 * kA2vWaves - 1) / (64 * kA2vWaves);
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto load_a = [&](int ch, u32x4 (&ar)[kAJ]) {
+  // A chunk ch into buffer bf: wave-load L = kA2vWaves m + w (L < 4 MT) fills
+  // slots 64 L + lane; slot s = piece * NA_PAD + row takes A[row][64 ch +
+  // 8 piece .. +8] (Na C 2 <= 4 MiB: offsets fit in 32 bits).
+  const i32x4 ars = make_buffer_rsrc(A, (uint32_t)Na * C * 2);
+  auto dma_a = [&](int ch, int bf) {
 #pragma unroll
-    for (int j = 0; j < kAJ; ++j) {
-      const int sl = tid + 64 * kA2vWaves * j;
-      const int piece = sl / NA_PAD, r = sl - piece * NA_PAD;
-      ar[j] = (sl < SLOTS && r < Na)
-                  ? *reinterpret_cast<const u32x4*>(A + (size_t)r * C + kCh * ch + 8 * piece)
-                  : zero4;
+    for (int m = 0; m < kAL; ++m) {
+      const int L = kA2vWaves * m + w;
+      if (L < 4 * MT) {
+        const int sl = 64 * L + lane;
+        const int piece = sl / NA_PAD, r = sl - piece * NA_PAD;
+        const int off = r < Na ? (r * C + kCh * ch + 8 * piece) * 2 : kPadOff;
+        dma16_manual(ars, lds_addr_of(abuf + bf * ABUF + 64 * L * 8), off, 0);
+      }
     }
   };
-  auto store_a = [&](const u32x4 (&ar)[kAJ], int bf) {
+  // X chunk ch into ring slot rs: wave-load m fills this wave's slots
+  // 64 m + lane: token n = slot / 8 (of the wave's 32), stored piece slot % 8
+  // holds logical piece (slot % 8) ^ (n % 8), channels 64 ch + 8 piece .. +8.
+  // The buffer covers the wave's rows that exist (32 C 2 <= 512 KiB).
+  const long long xrows = N - n0 < 0 ? 0 : (N - n0 < 32 ? N - n0 : 32);
+  const i32x4 xrs = make_buffer_rsrc(X + (n0 < N ? n0 : 0) * C, (uint32_t)(xrows * C * 2));
+  auto dma_x = [&](int ch, int rs) {
 #pragma unroll
-    for (int j = 0; j < kAJ; ++j) {
-      const int sl = tid + 64 * kA2vWaves * j;
-      if (sl < SLOTS) *reinterpret_cast<u32x4*>(abuf + bf * ABUF + sl * 8) = ar[j];
+    for (int m = 0; m < 4; ++m) {
+      const int n = 8 * m + (lane >> 3), q = (lane & 7) ^ (n & 7);
+      dma16_manual(xrs, lds_addr_of(&xbuf[rs][w][64 * m * 8]), (n * C + kCh * ch + 8 * q) * 2, 0);
     }
-  };
-  // X fragments of chunk ch: lane holds X[tok][64 ch + 16 ks + 8 hi .. +8]
-  // (tokens past N read the last token; their results are not written)
-  const long long tokc = tok_ok ? tok : N - 1;
-  auto load_x = [&](int ch, bf16x8 (&xf)[4]) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      xf[ks] = *reinterpret_cast<const bf16x8*>(X + tokc * C + kCh * ch + 16 * ks + 8 * hi);
   };
 
   f32x16 acc[MT];
@@ -181,42 +188,39 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
-  // Pipeline: X fragments three chunks ahead (a ring of four register sets),
-  // A one chunk ahead in registers and one more in LDS (double buffer). All
-  // loads are ordinary loads, so the compiler's waits cover exactly the data
-  // each step uses. Iteration ch: A(ch+1) registers -> LDS; load A(ch+2) and
-  // X(ch+3); multiply chunk ch; barrier.
-  bf16x8 xr[4][4];
-  u32x4 ar[kAJ];
-  load_a(0, ar);
-  load_x(0, xr[0]);
-  if (1 < nchunks) load_x(1, xr[1]);
-  if (2 < nchunks) load_x(2, xr[2]);
-  store_a(ar, 0);
-  if (1 < nchunks) load_a(1, ar);
-  __syncthreads();
+  // Pipeline: A one chunk ahead, X two ahead. Step ch: wait for A(ch) and
+  // X(ch) (the only loads issued after A(ch) are X(ch+1)'s four), barrier
+  // (A(ch) complete for every wave; every wave is done with the other A
+  // buffer), request A(ch+1) and X(ch+2) (into the ring slot this wave read
+  // in step ch-1), multiply chunk ch.
+  dma_a(0, 0);
+  dma_x(0, 0);
+  if (1 < nchunks) dma_x(1, 1);
   auto step = [&](int ch, auto ring) {
-    constexpr int R = decltype(ring)::value;  // ch % 4
-    if (ch + 1 < nchunks) store_a(ar, (R + 1) & 1);
-    if (ch + 2 < nchunks) load_a(ch + 2, ar);
-    if (ch + 3 < nchunks) load_x(ch + 3, xr[(R + 3) & 3]);
-    const __bf16* ab = abuf + (R & 1) * ABUF;
+    constexpr int R = decltype(ring)::value;  // ch % 3
+    if (ch + 1 < nchunks) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+    __syncthreads();
+    if (ch + 1 < nchunks) dma_a(ch + 1, (ch + 1) & 1);
+    if (ch + 2 < nchunks) dma_x(ch + 2, (R + 2) % kXRing);
+    const __bf16* ab = abuf + (ch & 1) * ABUF;
+    const __bf16* xb = &xbuf[R][w][0];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bx =
+          *reinterpret_cast<const bf16x8*>(xb + (l32 * 8 + ((2 * ks + hi) ^ (l32 & 7))) * 8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 af =
             *reinterpret_cast<const bf16x8*>(ab + ((2 * ks + hi) * NA_PAD + 32 * mt + l32) * 8);
-        acc[mt] = mfma32x32x16(af, xr[R][ks], acc[mt]);
+        acc[mt] = mfma32x32x16(af, bx, acc[mt]);
       }
     }
-    __syncthreads();
   };
-  for (int ch = 0; ch < nchunks; ch += 4) {
+  for (int ch = 0; ch < nchunks; ch += 3) {
     step(ch, std::integral_constant<int, 0>{});
     if (ch + 1 < nchunks) step(ch + 1, std::integral_constant<int, 1>{});
     if (ch + 2 < nchunks) step(ch + 2, std::integral_constant<int, 2>{});
-    if (ch + 3 < nchunks) step(ch + 3, std::integral_constant<int, 3>{});
   }
 
   // softmax over the audio axis; lane holds audio 32mt + 8(r/4) + 4hi + r%4
