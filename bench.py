@@ -12,7 +12,8 @@ Prints one JSON line: value = executed attention TFLOP/s over the whole layer
 time (the layer's executed attention FLOPs / ms per layer), plus ms per layer,
 per-stage times, the roofline of the dominant kernel (attention forward, bf16
 MFMA) measured with HIP events on the launch stream, and the fp64 CPU oracle's
-rate on a bounded sample of the same workload.
+rate on the same layer (the whole layer; --cpu-sample times a bounded sample
+and scales it).
 
 Options: --workload NAME runs another workload of the measurement plan
 (720p-dyn, 1080p, 2k; 2k adds the backward); --copy-calib runs only a plain
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", action="store_true",
+                    help="time the oracle on a bounded sample (6 heads) instead of the whole layer")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--norm-rope", action="store_true",
                     help="fuse RMSNorm + 3-D RoPE of Q and K into the gather (bsa_permute_norm_rope)")
@@ -405,13 +408,15 @@ def main():
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, counts)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, counts, sample=args.cpu_sample)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, inp, counts_gpu):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to the
-    same unit (executed attention TFLOP/s over the layer)."""
+def cpu_baseline(wl, inp, counts_gpu, sample: bool = False):
+    """The fp64 oracle on the host cores, in the same unit (executed attention
+    TFLOP/s over the layer): by default the whole layer (selection for every
+    head, gathered attention for every (head, query block) pair); with
+    ``sample`` a bounded sample (6 heads, 420 query blocks each) scaled up."""
     import numpy as np
 
     import synth
@@ -419,7 +424,9 @@ def cpu_baseline(wl, inp, counts_gpu):
     from oracle import pipeline as opipe
 
     threads = len(os.sched_getaffinity(0))
-    hs = 6  # heads of the sample (about 10 s of oracle work at 720p)
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():  # numpy's BLAS pool size
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    hs = 6 if sample else wl.heads
     q = synth.bf16_bits_to_f64(inp["q"][:hs])
     k = synth.bf16_bits_to_f64(inp["k"][:hs])
     v = synth.bf16_bits_to_f64(inp["v"][:hs])
@@ -427,19 +434,32 @@ def cpu_baseline(wl, inp, counts_gpu):
     r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau)
     t_sel = time.perf_counter() - t0
     L = r["layout"]
-    rng = np.random.default_rng(0)
-    nonempty = np.nonzero(r["counts"] > 0)[0]
-    per_head = min(420, len(nonempty))
-    pairs = [(h, int(i)) for h in range(hs) for i in rng.choice(nonempty, per_head, replace=False)]
+    B = L.block_tokens
+    total_pairs = int(counts_gpu.sum())
+    flops = total_pairs * 4.0 * B * B * wl.d
+    if sample:
+        rng = np.random.default_rng(0)
+        nonempty = np.nonzero(r["counts"] > 0)[0]
+        per_head = min(420, len(nonempty))
+        pairs = [(h, int(i)) for h in range(hs) for i in rng.choice(nonempty, per_head, replace=False)]
+    else:
+        pairs = None  # every (head, query block)
     t0 = time.perf_counter()
     oatt.attn_fwd_gathered(L, r["perm"], q, k, v, r["lists"], 1 / np.sqrt(wl.d), pairs=pairs)
     t_att = time.perf_counter() - t0
-    B = L.block_tokens
+    if not sample:
+        oracle_pairs = int(sum(len(r["lists"][h][i]) for h in range(hs) for i in range(L.n_blocks)))
+        layer_s = t_sel + t_att
+        return {"value": round(flops / layer_s / 1e12, 5),
+                "unit": "TFLOP/s (executed attention FLOPs per layer time)",
+                "cores": threads, "kind": "oracle",
+                "layer_s": round(layer_s, 1),
+                "sample": f"whole layer: oracle selection for all {wl.heads} heads "
+                          f"({t_sel:.1f} s) and gathered fp64 attention for every "
+                          f"(head, query block) ({oracle_pairs} block pairs, {t_att:.1f} s)"}
     sample_pairs = sum(len(r["lists"][h][i]) for h, i in pairs)
     per_pair = t_att / sample_pairs
-    total_pairs = int(counts_gpu.sum())
     layer_s = t_sel * wl.heads / hs + per_pair * total_pairs
-    flops = total_pairs * 4.0 * B * B * wl.d
     return {"value": round(flops / layer_s / 1e12, 5),
             "unit": "TFLOP/s (executed attention FLOPs per layer time)",
             "cores": threads, "kind": "oracle",
