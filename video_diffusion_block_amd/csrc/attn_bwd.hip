@@ -371,15 +371,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
         dma_part(sK[b ^ 1], krs, bn * kTile * 2, 2 * kt + 1);
         if (kt == 0) fetch_meta(bn, b ^ 1);
       }
-      if (partial) {
-        const f32x16 zero = {};
-        st[kt] = mfma32x32x16(pad_bias_a(kt ? mw1 : mw0, l32, hi), bias_b, zero);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dpt[kt][r] = 0.f;
       const int ro = (rowA + 32 * kt) * kD;
       bf16x8 fa[8], fb[8];
 #pragma unroll
@@ -388,11 +379,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
         fa[s] = *reinterpret_cast<const bf16x8*>(sk + off);
         fb[s] = *reinterpret_cast<const bf16x8*>(sv + off);
       }
+      // k-step 0 from an immediate zero accumulator (no register clearing);
+      // a partial block's pad keys get the -2^30 bias product last (it adds
+      // an exact 0 to every real key's score)
+      const f32x16 zero = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        st[kt] = mfma32x32x16(fa[s], qf[s], st[kt]);
-        dpt[kt] = mfma32x32x16(fb[s], dof[s], dpt[kt]);
+        st[kt] = mfma32x32x16(fa[s], qf[s], s == 0 ? zero : st[kt]);
+        dpt[kt] = mfma32x32x16(fb[s], dof[s], s == 0 ? zero : dpt[kt]);
       }
+      if (partial) st[kt] = mfma32x32x16(pad_bias_a(kt ? mw1 : mw0, l32, hi), bias_b, st[kt]);
     }
     bf16x8 dsf[4];
 #pragma unroll

@@ -187,18 +187,23 @@ __device__ inline void qk_tiles_pre(f32x16 (&s)[2], const __bf16* sk, int koff, 
   for (int st = 0; st < 4; ++st)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) a[st][kt] = pre[st][kt];
+  // k-step 0 starts from the pad-key bias (partial block) or from an
+  // immediate zero accumulator (full block: no register clearing)
+  const f32x16 zero = {};
   if (__builtin_amdgcn_readfirstlane(m.count) < kB) {
-    const f32x16 zero = {};
     s[0] = mfma32x32x16(pad_bias_a(m.w0, l32, hi), bias_b, zero);
     s[1] = mfma32x32x16(pad_bias_a(m.w1, l32, hi), bias_b, zero);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[0][kt], qf[0], s[kt]);
   } else {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[0][kt], qf[0], zero);
   }
+  load(4);
+  hook(0);
+  sched_fence();
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
+  for (int st = 1; st < 8; ++st) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[st][kt], qf[st], s[kt]);
     if (st + 4 < 8) load(st + 4);
@@ -225,18 +230,23 @@ __device__ inline void qk_tiles(f32x16 (&s)[2], const __bf16* sk, int koff, int 
 #pragma unroll
   for (int st = 0; st < 4; ++st) load(st);
   sched_fence();
+  // k-step 0 starts from the pad-key bias (partial block) or from an
+  // immediate zero accumulator (full block: no register clearing)
+  const f32x16 zero = {};
   if (__builtin_amdgcn_readfirstlane(m.count) < kB) {
-    const f32x16 zero = {};
     s[0] = mfma32x32x16(pad_bias_a(m.w0, l32, hi), bias_b, zero);
     s[1] = mfma32x32x16(pad_bias_a(m.w1, l32, hi), bias_b, zero);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[0][kt], qf[0], s[kt]);
   } else {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[0][kt], qf[0], zero);
   }
+  load(4);
+  hook(0);
+  sched_fence();
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
+  for (int st = 1; st < 8; ++st) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(a[st][kt], qf[st], s[kt]);
     if (st + 4 < 8) load(st + 4);
