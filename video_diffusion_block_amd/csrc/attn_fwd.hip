@@ -302,10 +302,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const int qg = w & 3, kh = w >> 2;
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t row = (size_t)h * L.M + i;
-  const int n = counts[row];
   const int32_t* lst = idx + row * L.M;
   const size_t head0 = (size_t)h * L.Np;
   const int q = 32 * qg + l32;  // this lane's query inside the block
+  // One memory round trip for the row's count, its first two list entries
+  // (every row has room for M entries; they are used only where the count
+  // covers them) and this lane's Q^T fragments (B operand of S^T = K Q^T:
+  // Q[q][16s + 8hi .. +8]).
+  const int n = counts[row];
+  const int blk0_list = lst[0];
+  const int blk1_list = L.M > 1 ? lst[1] : 0;
+  bf16x8 qf[8];
+  {
+    const __bf16* qrow = qp + (head0 + (size_t)i * kB + q) * kD + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+  }
   // where this lane's output row goes: its slot of the permuted [H, Np, d]
   // layout, or (raster) its token's row of [H, N, d] (pad slots: nowhere)
   size_t orow_i = head0 + (size_t)i * kB + q;
@@ -350,17 +362,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 
   // prologue: the list into LDS; tiles K0, V0 (and K1), block 0's mask words
   for (int e = tid; e < n; e += kThreads) sL[e] = lst[e];
-  const int blk0 = lst[0];
-  const int blk1 = n > 1 ? lst[1] : 0;
+  const int blk0 = blk0_list;
+  const int blk1 = n > 1 ? blk1_list : 0;
   dma_tile<false>(sK[0], krs, blk0 * kTileBytes, w, lane);
   dma_tile<true>(sV[0], vrs, blk0 * kTileBytes, w, lane);
-  // Q^T fragments (B operand of S^T = K Q^T): lane holds Q[q][16s + 8hi .. +8].
-  bf16x8 qf[8];
-  {
-    const __bf16* qrow = qp + (head0 + (size_t)i * kB + q) * kD + 8 * hi;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
-  }
   fetch_meta(blk0, 0);
   fetch_meta(blk1, 1);
   dma_tile<false>(sK[1], krs, blk1 * kTileBytes, w, lane);  // (block 0 again if n = 1)
