@@ -161,7 +161,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const __bf16* __rest
 // direct buffer loads (the XOR swizzle applied on the fetch side: LDS slot s of
 // a tile holds row s / 8, logical chunk (s % 8) ^ (row % 8)); rows past M or N
 // read zero through the buffer bounds. Needs K % 64 == 0 and each operand's
-// rows below 2^31 bytes from the tile's first row.
+// rows below 2^31 bytes from the tile's first row. Without a k split the tiles
+// are taken in the L2-aware order (the tiles of one 256-row panel of A run on
+// one XCD).
 constexpr int kBM = 256, kBN = 256;
 constexpr int kBThreads = 512;
 
@@ -174,7 +176,9 @@ __global__ __launch_bounds__(kBThreads) void gemm_nt_big_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  int tx = blockIdx.x, ty = blockIdx.y;
+  if (gridDim.z == 1) xcd_item(tx, ty);
+  const int m0 = ty * kBM, n0 = tx * kBN;
   const int wm = w >> 1, wn = w & 1;  // rows 64 wm .., columns 128 wn ..
   const uint32_t abytes = (uint32_t)std::min<long long>((long long)(M - m0) * lda * 2, 0x7fffffffLL);
   const uint32_t bbytes = (uint32_t)std::min<long long>((long long)(N - n0) * ldb * 2, 0x7fffffffLL);
