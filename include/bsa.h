@@ -270,8 +270,11 @@ bsa_status bsa_select_causal(const bsa_layout* L, const int32_t* zone_shape, con
  *  ws          workspace of bsa_workspace_size(BSA_CALL_ATTN_FWD, ...) bytes (a
  *              per-block table; 0 bytes, ws may be NULL, when that size is 0)
  *  qp, kp, vp and op must be 16-byte aligned (BSA_INVALID_ARG otherwise).
- *  Supported: dtype BSA_BF16 or BSA_F32, d in {64, 128}, B in {64, 128}; the
- *  bf16 MFMA kernel runs for d = 128, B = 128, the others take a scalar kernel. */
+ *  Supported: dtype BSA_BF16 or BSA_F32, d in {64, 128}, B in {64, 128}. Only
+ *  bf16 with d = 128 and B = 128 runs on the matrix cores; every other
+ *  supported configuration (fp32, d = 64, 64-token blocks) takes a scalar
+ *  kernel (one thread per query, K and V staged as fp32 in LDS): a correct
+ *  but far slower path, meant for checking, not for speed. */
 bsa_status bsa_attn_fwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
                         const void* kp, const void* vp, const int32_t* counts,
                         const int32_t* idx, int heads, int d, int dtype, float scale, void* op,
@@ -322,7 +325,9 @@ bsa_status bsa_attn_fwd_raster(const bsa_layout* L, const int32_t* zone_shape, c
  *  dqp, dkp, dvp [heads, Np, d] float32 out, whatever `dtype` is (gradients
  *              are accumulated and returned in fp32); pad slots get zeros.
  *  qp, kp, vp, op, dop must be 16-byte aligned (BSA_INVALID_ARG otherwise).
- *  The key-major (transposed) lists are built in the workspace. */
+ *  The key-major (transposed) lists are built in the workspace. As for the
+ *  forward, only bf16 with d = 128 and B = 128 runs on the matrix cores; the
+ *  other supported configurations take scalar kernels (far slower). */
 bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
                         const void* kp, const void* vp, const void* op, const void* dop,
                         const float* lse, const int32_t* counts, const int32_t* idx,
