@@ -23,15 +23,16 @@
 //                  symmetric G and a lane-local dot with P. Y is formed on
 //                  bf16 MFMA from three-piece splits of G and P (the six
 //                  products whose pieces carry the top 24 bits; exact
-//                  products, fp32 sums), which matches an fp32 product at a
-//                  sixteenth of the matrix-unit time per term. Writes g [N] fp32.
+//                  products, fp32 sums), which matches an fp32 product in
+//                  6/16 of its matrix-unit time. Writes g [N] fp32.
 //  line_kernel     per (zone, 32-channel chunk): the zone is streamed through
 //                  LDS one t-slice at a time; sum x^2 and the squared line sums
 //                  along t, h, w in fp64 (bf16 inputs make these sums exact), so
-//                  V_a = (sum x^2 - sum_lines S^2/len) / (C n_z).
-//                  The same kernel with one channel handles g.
-//  decide_kernel   one workgroup: reduce the partials in a fixed order, the
-//                  means, r, the costs and the tie rule; writes the shape ids.
+//                  V_a = (sum x^2 - sum_lines S^2/len) / (C n_z). The chunk-0
+//                  workgroup of each zone also sums the one-channel field g.
+//  decide_kernel   one workgroup: sum the chunk partials in a fixed order,
+//                  the means, r, the costs and the tie rule; writes the shape
+//                  ids.
 #include <math.h>
 
 #include <type_traits>
