@@ -603,7 +603,7 @@ def _zone_case(grid, C, na, seed=4):
 
 @pytest.mark.parametrize("grid,C,na", [((8, 32, 48), 256, 40), ((5, 20, 36), 128, 0),
                                        ((13, 45, 80), 512, 200), ((6, 20, 30), 192, 256),
-                                       ((4, 17, 33), 64, 1)])
+                                       ((4, 17, 33), 64, 1), ((1, 3, 5), 64, 3)])
 def test_zone_score_small(grid, C, na):
     X, A = _zone_case(grid, C, na)
     lay = ops.BSALayout.dynamic(grid)
