@@ -373,7 +373,7 @@ size_t bsa_xattn_bwd_workspace_size(int n_video, int n_audio, int C, int heads);
  *  q, k, v, o, lse           bsa_xattn_fwd's outputs
  *  dy [N, C] bf16            output gradient
  *  dx [N, C], da [n_audio, C], dwq, dwk, dwv [D, C], dwo [C, D]   float out
- *  ws  workspace of bsa_xattn_bwd_workspace_size(...) bytes
+ *  ws  workspace of bsa_xattn_bwd_workspace_size(...) bytes, 16-byte aligned
  *  Sizes and alignment as bsa_xattn_fwd. */
 bsa_status bsa_xattn_bwd(int n_video, int n_audio, int C, int heads, int d, const void* x,
                          const void* a, const void* wq, const void* wk, const void* wv,

@@ -322,11 +322,13 @@ def test_xattn_bwd_validation(lib):
     assert need > 0
     assert lib.bsa_xattn_bwd_workspace_size(1000, 300, 256, 2) == 0
 
-    def call(Na=200, d=128, wsb=need, ptr=FAKE):
+    def call(Na=200, d=128, wsb=need, ptr=FAKE, ws=FAKE):
         return lib.bsa_xattn_bwd(1000, Na, 256, 2, d, ptr, *([FAKE] * 9), FAKE, FAKE,
-                                 *([FAKE] * 6), FAKE, wsb, None)
+                                 *([FAKE] * 6), ws, wsb, None)
 
     assert call(Na=0) == _lib.BSA_INVALID_ARG
     assert call(d=96) == _lib.BSA_UNSUPPORTED
     assert call(ptr=None) == _lib.BSA_INVALID_ARG
     assert call(wsb=need - 1) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert call(ws=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG   # misaligned workspace
+    assert "workspace" in lib.bsa_last_error().decode()

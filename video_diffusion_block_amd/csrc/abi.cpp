@@ -512,6 +512,8 @@ bsa_status bsa_xattn_bwd(int n_video, int n_audio, int C, int heads, int d, cons
   const size_t need = bsa::xattn_bwd_workspace(n_video, n_audio, C, heads);
   if (!ws || ws_bytes < need)
     return fail(BSA_WORKSPACE_TOO_SMALL, "xattn_bwd needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 16)
+    return fail(BSA_INVALID_ARG, "the workspace must be 16-byte aligned");
   typedef const __bf16* cb;
   return hip_status(bsa::launch_xattn_bwd(n_video, n_audio, heads, (cb)x, (cb)a, C, (cb)wq,
                                           (cb)wk, (cb)wv, (cb)wo, (cb)q, (cb)k, (cb)v, (cb)o, lse,

@@ -17,8 +17,9 @@
 //                    k-contiguous), 128 x 128 tiles, 64-deep k steps staged in
 //                    LDS (XOR-swizzled 16-byte chunks, double-buffered), fp32
 //                    accumulation, bf16 or fp32 output (optionally added to C).
-//  transpose_kernel  bf16 [R, Cc] -> [Cc, ldo] through LDS, columns R..ldo-1
-//                    zero (so transposed rows are whole 16-byte chunks).
+//  transpose16_kernel bf16 [R, Cc] -> [Cc, ldo], columns R..ldo-1 zero (so
+//                    transposed rows are whole 16-byte chunks): 8 x 8 blocks per
+//                    lane transposed in registers, 16-byte loads and stores.
 //  xattn_fwd_kernel  per (256 queries, head): K_h, V_h of every audio token in
 //                    LDS; per wave 32 queries, S^T = K Q^T and O^T += V^T P^T on
 //                    MFMA over 64-key chunks with an online softmax; writes O
@@ -260,19 +261,34 @@ __global__ __launch_bounds__(kBThreads) void gemm_nt_big_kernel(
 }
 
 // -------------------------------------------------------------- transpose --
-__global__ __launch_bounds__(256) void transpose_kernel(const __bf16* __restrict__ src, int R,
-                                                        int Cc, int lds, __bf16* __restrict__ dst,
-                                                        int ldo) {
-  __shared__ __bf16 t[64][65];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    t[r][c] = (r0 + r < R && c0 + c < Cc) ? src[(size_t)(r0 + r) * lds + c0 + c] : (__bf16)0.f;
+// bf16 [R, Cc] -> [Cc, ldo] for 16-byte aligned rows (lds, ldo, Cc multiples of 8). Lane
+// (cb = lane % 8, rb = lane / 8) of wave w loads an 8 x 8 block, src rows r + 0..7 (one
+// 16-byte load each; rows past R read as zeros) and columns c + 0..7, and stores its
+// transpose as dst rows c + 0..7, columns r + 0..7 (one 16-byte store each). Every load and
+// store instruction of a wave covers eight whole 128-byte row segments.
+__global__ __launch_bounds__(256) void transpose16_kernel(const __bf16* __restrict__ src, int R,
+                                                          int Cc, int lds,
+                                                          __bf16* __restrict__ dst, int ldo) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + 8 * (lane & 7);
+  const long long r = ((long long)blockIdx.y * 4 + w) * 64 + 8 * (lane >> 3);
+  if (c >= Cc || r >= ldo) return;
+  u32x4 in[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    in[i] = r + i < R ? *reinterpret_cast<const u32x4*>(src + (size_t)(r + i) * lds + c) : z;
   }
-  __syncthreads();
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int c = e >> 6, r = e & 63;  // dst row c0 + c, column r0 + r
-    if (c0 + c < Cc && r0 + r < ldo) dst[(size_t)(c0 + c) * ldo + r0 + r] = t[r][c];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // dst row c + j, columns r + 2m and r + 2m + 1: element j of src rows r + 2m, r + 2m + 1
+    u32x4 out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = in[2 * m][j >> 1], b = in[2 * m + 1][j >> 1];
+      out[m] = (j & 1) ? (a >> 16) | (b & 0xffff0000u) : (a & 0xffffu) | (b << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst + (size_t)(c + j) * ldo + r) = out;
   }
 }
 
@@ -746,8 +762,11 @@ hipError_t launch_gemm_nt_splitk(const __bf16* A, int lda, const __bf16* B, int 
 
 hipError_t launch_transpose(const __bf16* src, int R, int Cc, int lds, __bf16* dst, int ldo,
                             hipStream_t st) {
-  dim3 grid((Cc + 63) / 64, (ldo + 63) / 64);
-  transpose_kernel<<<grid, 256, 0, st>>>(src, R, Cc, lds, dst, ldo);
+  // every caller passes C, D (multiples of 64) or padded token counts and 16-byte aligned rows
+  if (((lds | ldo | Cc) & 7) != 0 || (((uintptr_t)src | (uintptr_t)dst) & 15) != 0)
+    return hipErrorInvalidValue;
+  dim3 grid((Cc + 63) / 64, (ldo + 255) / 256);
+  transpose16_kernel<<<grid, 256, 0, st>>>(src, R, Cc, lds, dst, ldo);
   return hipGetLastError();
 }
 
