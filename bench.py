@@ -2,11 +2,12 @@
 
 One step = one BSA attention layer forward on the 720p workload (13x45x80 =
 46 800 latent tokens, 40 heads, d = 128, bf16, fixed 2x8x8 blocks, sparsity
-0.85, tau = 0.20): zone scoring (a no-op fill for a fixed layout), gather of
-Q/K/V with the block means of Q and K pooled on the way, hybrid selection, and
-the block-sparse attention forward writing O in raster order. Inputs are
-seeded synthetic latents (smooth field + noise), resident in HBM before timing
-starts.
+0.85, tau = 0.20): zone scoring (a no-op fill for a fixed layout), the block
+means of Q and K pooled from the token-order tensors, hybrid selection, and the
+block-sparse attention forward, whose tile loads gather Q, K, V into block
+order from the token-order tensors and which writes O in raster order (no
+block-ordered copy of Q, K or V is stored). Inputs are seeded synthetic
+latents (smooth field + noise), resident in HBM before timing starts.
 
 Prints one JSON line: value = executed attention TFLOP/s over the whole layer
 time (the layer's executed attention FLOPs / ms per layer), plus ms per layer,
@@ -16,8 +17,10 @@ rate on the same layer (the whole layer; --cpu-sample times a bounded sample
 and scales it).
 
 Options: --workload NAME runs another workload of the measurement plan
-(720p-dyn, 1080p, 2k; 2k adds the backward); --copy-calib runs only a plain
-1 GiB device copy (the calibration kernel for HBM byte counters); --unfused
+(720p-dyn, 1080p, 2k; 2k adds the backward, which needs block-ordered copies
+and so gathers them); --copy-calib runs only a plain 1 GiB device copy (the
+calibration kernel for HBM byte counters); --permuted (block-ordered copies of
+Q, K, V gathered with the pooling, then the attention on them), --unfused
 (separate gather and pool+select calls), --norm-rope (RMSNorm + 3-D RoPE of Q
 and K in the gather), --causal-frames F (frame-chunk causal selection) and
 --reuse-every R (zone shapes and lists recomputed every R steps, reused in
@@ -60,6 +63,9 @@ def parse():
                          "workload's token count instead of the BSA layer")
     ap.add_argument("--unfused", action="store_true",
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
+    ap.add_argument("--permuted", action="store_true",
+                    help="store block-ordered Q, K, V (bsa_permute_pool) and run "
+                         "bsa_attn_fwd_raster on them instead of bsa_attn_fwd_gather")
     return ap.parse_args()
 
 
@@ -94,7 +100,9 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
     alg = {}
     if "unpermute" in stage_ms:
         alg["unpermute"] = 2 * H * N * d * e           # O: read real slots, write raster rows
-    if "permute" in stage_ms:
+    if "pool" in stage_ms:                             # Q, K read; fp64 block means written
+        alg["pool"] = 2 * H * N * d * e + 2 * H * M * d * 8
+    elif "permute" in stage_ms:
         alg["permute"] = 3 * H * (N + Np) * d * e      # Q, K, V: read real rows, write padded
         alg["pool_select"] = 2 * H * N * d * e         # pooling reads the real rows of Qp, Kp
     else:                                              # + the fp64 block means of Q and K
@@ -270,8 +278,12 @@ def main():
 
     # forward-only sequences write O in raster order from the attention kernel
     # (bsa_attn_fwd_raster); the backward needs the permuted O, so a backward
-    # workload keeps bsa_attn_fwd + bsa_unpermute
+    # workload keeps bsa_attn_fwd + bsa_unpermute. The default forward-only
+    # sequence also reads Q, K, V in token order (bsa_attn_fwd_gather: every
+    # block shape of these layouts is a multiple of 4 tokens wide)
     raster = not wl.backward and not args.unfused
+    gather = (raster and not args.permuted and not args.norm_rope and
+              all(shp[2] % 4 == 0 for shp in lay.shapes))
     state = {"step": 0}
 
     def step(record):
@@ -289,16 +301,28 @@ def main():
         mark(None)
         if reuse:   # zone shapes and lists of the last refresh; this step's Q, K, V
             zs, counts, idx = state["zs"], state["counts"], state["idx"]
-            qp, kp, vp = ops.permute(lay, zs, [q, k, v])
-            mark("permute")
-            o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
-            mark("attn_fwd")
+            if gather:
+                o, lse = ops.attn_fwd_gather(lay, zs, q, k, v, counts, idx)
+            else:
+                qp, kp, vp = ops.permute(lay, zs, [q, k, v])
+                mark("reuse_permute")
+                o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
+            mark("reuse_attn_fwd")
             if record:
                 ev_marks.append(marks)
             return
         zs = ops.zone_score(lay, video, audio)
         mark("zone_score")
-        if args.unfused:
+        if gather:
+            _, (qbar, kbar) = ops.permute_pool(lay, zs, [q, k], npool=2, store=False)
+            mark("pool")
+            if args.causal_frames:
+                counts, idx = ops.select_causal(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau,
+                                                args.causal_frames)
+            else:
+                counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
+            mark("select")
+        elif args.unfused:
             qp, kp, vp = ops.permute(lay, zs, [q, k, v])
             mark("permute")
             counts, idx = ops.pool_select(lay, zs, qp, kp, wl.sparsity_1e4, wl.tau)
@@ -316,7 +340,10 @@ def main():
             else:
                 counts, idx = ops.select(lay, zs, qbar, kbar, wl.sparsity_1e4, wl.tau)
             mark("select")
-        if raster:
+        if gather:
+            o, lse = ops.attn_fwd_gather(lay, zs, q, k, v, counts, idx)
+            mark("attn_fwd")
+        elif raster:
             o, lse = ops.attn_fwd_raster(lay, zs, qp, kp, vp, counts, idx)
             mark("attn_fwd")
         else:
@@ -346,13 +373,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # stage times: refresh steps under their stage names, reuse steps (which
-    # gather without pooling and skip zone scoring and selection) under
-    # "reuse_<stage>"
+    # skip zone scoring, pooling and selection) under "reuse_<stage>"
     ev = {}
     for marks in ev_marks:
-        reuse_step = marks[1][0] == "permute" and args.reuse_every > 1
         for (_, a), (name, b) in zip(marks, marks[1:]):
-            ev.setdefault(("reuse_" if reuse_step else "") + name, []).append(a.elapsed_time(b))
+            ev.setdefault(name, []).append(a.elapsed_time(b))
     stage_ms = {s: float(np.mean(v)) for s, v in ev.items()}
     ms_per_step = wall * 1e3 / args.steps
 
@@ -387,7 +412,8 @@ def main():
                    "blocks": sizes["n_blocks"], "sparsity": wl.sparsity_1e4 / 1e4, "tau": wl.tau,
                    "mode": wl.mode, "backward": wl.backward,
                    "sequence": ("unfused" if args.unfused else
-                                "norm_rope+pool" if args.norm_rope else "pool") +
+                                "norm_rope+pool" if args.norm_rope else
+                                "pool, gathering attention" if gather else "pool") +
                                (", raster O" if raster else "") +
                                (f", causal chunks of {args.causal_frames} frames"
                                 if args.causal_frames else "") +
@@ -396,7 +422,7 @@ def main():
                    "mean_list": round(pairs / max(1, int((counts > 0).sum())), 2)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": {
-            "kernel": "attn_fwd_mfma",
+            "kernel": "attn_fwd_mfma<true>" if gather else "attn_fwd_mfma<false>",
             "bound": "mfma",
             "achieved": round(fwd_flops / (attn_ms * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16_TFLOPS,

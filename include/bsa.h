@@ -162,6 +162,9 @@ bsa_status bsa_permute(const bsa_layout* L, const int32_t* zone_shape, int ntens
  *  npool   0..ntensors tensors to pool (0 = plain bsa_permute)
  *  means   [host] array of npool device pointers, each [heads, n_blocks, d]
  *          double out: mean of the block's real slots (0 for an empty block)
+ *  dst     as bsa_permute, except that dst[i] may be NULL for a pooled tensor
+ *          (i < npool): it is read and pooled, and no gathered copy is stored
+ *          (the path of bsa_attn_fwd_gather, which gathers Q, K, V itself)
  *  Other arguments as bsa_permute; pooling needs d in {64, 128}. */
 bsa_status bsa_permute_pool(const bsa_layout* L, const int32_t* zone_shape, int ntensors,
                             const void* const* src, void* const* dst, int heads, int d,
@@ -306,6 +309,26 @@ bsa_status bsa_attn_fwd_noalloc(const bsa_layout* L, const int32_t* zone_shape, 
  *  The backward takes the permuted O of bsa_attn_fwd. */
 bsa_status bsa_attn_fwd_raster(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
                                const void* kp, const void* vp, const int32_t* counts,
+                               const int32_t* idx, int heads, int d, int dtype, float scale,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* bsa_attn_fwd_raster reading Q, K and V in raster token order too [Prism
+ * §Blocks: attention runs on the tokens regrouped into the zones' blocks;
+ * here the regrouping is done by the attention's own tile loads, so the
+ * forward path stores no block-ordered copy of Q, K or V]:
+ *  q, k, v  [heads, N, d] bf16, the token-order tensors bsa_permute would take
+ *  o        [heads, N, d] out, lse [heads, N] float out (as bsa_attn_fwd_raster)
+ *  ws       workspace of bsa_workspace_size(BSA_CALL_ATTN_FWD, ...) bytes
+ *  Same lists, arithmetic and results as bsa_permute followed by
+ *  bsa_attn_fwd_raster, for finite inputs (a pad slot's key and value rows are
+ *  read from whatever token sits at its place on the grid, or as zeros past
+ *  the last token, and take no weight: the scores of pad keys are masked).
+ *  Supported for bf16, d = 128, 128-token blocks, every candidate block shape
+ *  of a width that is a multiple of 4, and Np * 256 < 2^31 (BSA_UNSUPPORTED
+ *  otherwise: then use bsa_permute + bsa_attn_fwd_raster). q, k, v, o 16-byte
+ *  aligned. */
+bsa_status bsa_attn_fwd_gather(const bsa_layout* L, const int32_t* zone_shape, const void* q,
+                               const void* k, const void* v, const int32_t* counts,
                                const int32_t* idx, int heads, int d, int dtype, float scale,
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 

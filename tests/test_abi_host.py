@@ -136,6 +136,29 @@ def test_attn_fwd_validation(lib):
     assert _attn_fwd(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
 
 
+def _attn_fwd_gather(lib, L=LAY, q=FAKE, o=FAKE, d=128, dt=1, zs=FAKE, wsb=1 << 40):
+    c = L.c()
+    return lib.bsa_attn_fwd_gather(ctypes.byref(c), zs, q, FAKE, FAKE, FAKE, FAKE, 2, d, dt, 0.0,
+                                   o, FAKE, FAKE, wsb, None)
+
+
+def test_attn_fwd_gather_validation(lib):
+    assert _attn_fwd_gather(lib, q=None) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd_gather(lib, o=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG
+    assert _attn_fwd_gather(lib, dt=0) == _lib.BSA_UNSUPPORTED     # fp32: the MFMA kernel only
+    assert _attn_fwd_gather(lib, d=64) == _lib.BSA_UNSUPPORTED
+    assert _attn_fwd_gather(lib, wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
+    assert _attn_fwd_gather(lib, L=DYN, zs=None) == _lib.BSA_INVALID_ARG
+    # a block two tokens wide: its rows do not come in runs of four tokens
+    narrow = BSALayout.fixed((13, 45, 80), (2, 32, 2))
+    assert _attn_fwd_gather(lib, L=narrow) == _lib.BSA_UNSUPPORTED
+    assert "multiples of 4" in lib.bsa_last_error().decode()
+    # dynamic layouts: every candidate shape must qualify
+    mixed = BSALayout.dynamic((13, 45, 80), zone=(4, 16, 16), shapes=((2, 8, 8), (4, 16, 2)))
+    assert mixed.sizes()["n_blocks"] > 0
+    assert _attn_fwd_gather(lib, L=mixed) == _lib.BSA_UNSUPPORTED
+
+
 def test_attn_fwd_rejects_misaligned_tensors(lib):
     assert _attn_fwd(lib, q=ctypes.c_void_p(0x1008)) == _lib.BSA_INVALID_ARG
     assert "aligned" in lib.bsa_last_error().decode()
@@ -216,6 +239,13 @@ def test_permute_pool_validation(lib):
     assert call(d=96) == _lib.BSA_UNSUPPORTED             # pooling needs d in {64, 128}
     assert call(dt=5) == _lib.BSA_INVALID_ARG
     assert "npool" in (call(npool=4) and lib.bsa_last_error().decode())
+    # a missing dst is allowed only for a pooled tensor (pool without storing)
+    nodst = (ctypes.c_void_p * 3)(None, None, None)
+    assert lib.bsa_permute_pool(ctypes.byref(c), None, 3, arr, nodst, 2, 128, 1, 2, means,
+                                None) == _lib.BSA_INVALID_ARG   # tensor 2 is not pooled
+    assert "tensor 2" in lib.bsa_last_error().decode()
+    assert lib.bsa_permute(ctypes.byref(c), None, 1, arr, nodst, 2, 128, 1,
+                           None) == _lib.BSA_INVALID_ARG        # nothing pooled: dst required
 
 
 def test_permute_norm_rope_validation(lib):

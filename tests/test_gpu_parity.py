@@ -477,6 +477,50 @@ def test_attn_fwd_raster(wl):
     assert np.array_equal(lse_r.cpu().numpy(), lse_raster(L, perm, g["lse"].cpu().numpy()))
 
 
+GATHER_CASES = [
+    SMALL[0],   # ragged dynamic grid, three candidate shapes
+    SMALL[3],   # ragged fixed grid (W = 30: partial blocks wrap into the next row)
+    # one partial block: every list is that block (the prefetch ring repeats it)
+    synth.Workload("one-block", (1, 3, 5), 2, 128, "bf16", "fixed", (2, 8, 8), 0, 0.2),
+    # every key block listed (36-block lists), 16-token-wide blocks
+    synth.Workload("full-lists", (4, 24, 40), 3, 128, "bf16", "fixed", (1, 8, 16), 0, 0.2),
+]
+
+
+@pytest.mark.parametrize("wl", GATHER_CASES, ids=lambda w: w.name)
+def test_attn_fwd_gather(wl):
+    """bsa_attn_fwd_gather (Q, K, V read in token order) writes bitwise what
+    bsa_permute + bsa_attn_fwd_raster write on the same lists, within the
+    oracle's bounds; bsa_permute_pool with no stored copies gives the same
+    block means as with them."""
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    L = oracle_layout(wl)
+    rng = np.random.default_rng(21)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    print(f"[{wl.name}] blocks {L.n_blocks}, zone shapes {np.bincount(zs).tolist()}", flush=True)
+    g = run_gpu(wl, inp, zone_shape=zs, fused=True)
+    outs, means = ops.permute_pool(g["lay"], g["zs"], [g["q"], g["k"]], npool=2, store=False)
+    assert outs == [None, None]
+    _, means_ref = ops.permute_pool(g["lay"], g["zs"], [g["q"], g["k"]], npool=2)
+    for a, b in zip(means, means_ref):
+        assert torch.equal(a, b)
+    o_g, lse_g = ops.attn_fwd_gather(g["lay"], g["zs"], g["q"], g["k"], g["v"], g["counts"],
+                                     g["idx"])
+    o_r, lse_r = ops.attn_fwd_raster(g["lay"], g["zs"], g["qp"], g["kp"], g["vp"], g["counts"],
+                                     g["idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+    assert torch.equal(lse_g, lse_r)
+    q, k, v = (host_f64(inp[p], wl.dtype) for p in "qkv")
+    perm = olay.permutation(L, zs)
+    lists = gpu_lists(g["counts"], g["idx"])
+    lens = [len(x) for row in lists for x in row]
+    print(f"[{wl.name}] list lengths {min(lens)}..{max(lens)}", flush=True)
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, perm, q, k, v, lists, 1 / np.sqrt(wl.d))
+    assert_bf16_close(to_f64(o_g), o_ref, "O")
+    assert np.abs(to_f64(lse_g) - lse_ref).max() <= LSE_TOL
+
+
 def test_cdf_branch_lists():
     """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
     top-k (s = 0.93), so most lists have n = m > k."""
@@ -674,7 +718,16 @@ def test_full_size_workload(name):
               f"gap between a zone's two lowest costs {gap.min():.3g}", flush=True)
     o_r, lse_r = ops.attn_fwd_raster(g["lay"], g["zs"], g["qp"], g["kp"], g["vp"], g["counts"],
                                      g["idx"])
-    assert torch.equal(o_r, g["o"])          # the benchmark's raster-output forward
+    assert torch.equal(o_r, g["o"])          # the raster-output forward
+    if not wl.backward:                      # the benchmark's forward-only sequence
+        _, means = ops.permute_pool(g["lay"], g["zs"], [g["q"], g["k"]], npool=2, store=False)
+        counts_g, idx_g = ops.select(g["lay"], g["zs"], means[0], means[1], wl.sparsity_1e4,
+                                     wl.tau)
+        assert torch.equal(counts_g, g["counts"]) and torch.equal(idx_g, g["idx"])
+        o_g, lse_g = ops.attn_fwd_gather(g["lay"], g["zs"], g["q"], g["k"], g["v"], g["counts"],
+                                         g["idx"])
+        assert torch.equal(o_g, g["o"]) and torch.equal(lse_g, lse_r)
+        del o_g, lse_g, means
     print(f"[{name}] oracle selection", flush=True)
     q, k = (synth.bf16_bits_to_f64(inp[p]) for p in "qk")
     r = opipe.run_selection(wl.grid, wl.mode, wl.block, q, k, wl.sparsity_1e4, wl.tau,

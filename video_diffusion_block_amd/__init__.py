@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     BSALayout,
     attn_bwd,
     attn_fwd,
+    attn_fwd_gather,
     attn_fwd_raster,
     permute,
     permute_norm_rope,

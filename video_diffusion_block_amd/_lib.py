@@ -79,6 +79,9 @@ SIGNATURES = {
     "bsa_attn_fwd_raster": (ctypes.c_int, [LayoutP, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp,
                                            ctypes.c_size_t, vp]),
+    "bsa_attn_fwd_gather": (ctypes.c_int, [LayoutP, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp,
+                                           ctypes.c_size_t, vp]),
     "bsa_attn_bwd": (ctypes.c_int, [LayoutP, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]),

@@ -211,8 +211,11 @@ static bsa_status permute_common(const bsa_layout* in, const int32_t* zone_shape
   BSA_TRY(check_dtype_d(dtype, d));
   if (ntensors < 1 || ntensors > 4) return fail(BSA_INVALID_ARG, "ntensors = %d out of [1, 4]", ntensors);
   if (!src || !dst) return fail(BSA_INVALID_ARG, "src/dst pointer arrays are NULL");
+  // a pooled tensor may have no dst (bsa_permute_pool only): it is read and
+  // pooled, and its gathered copy is not stored
   for (int i = 0; i < ntensors; ++i)
-    if (!src[i] || !dst[i]) return fail(BSA_INVALID_ARG, "tensor %d pointer is NULL", i);
+    if (!src[i] || (!dst[i] && (inverse || nrope > 0 || i >= npool)))
+      return fail(BSA_INVALID_ARG, "tensor %d pointer is NULL", i);
   for (int i = 0; i < ntensors; ++i)
     if (reinterpret_cast<uintptr_t>(src[i]) % 16 || reinterpret_cast<uintptr_t>(dst[i]) % 16)
       return fail(BSA_INVALID_ARG, "tensor %d: src and dst must be 16-byte aligned", i);
@@ -375,7 +378,7 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
                                   const int32_t* counts, const int32_t* idx, int heads, int d,
                                   int dtype, float scale, void* op, float* lse, void* ws,
                                   size_t ws_bytes, void* stream, bool raster,
-                                  bool static_scratch = false) {
+                                  bool static_scratch = false, bool gather = false) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
@@ -383,6 +386,9 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
   if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
   if (raster && !bsa::attn_fwd_uses_mfma(L, d, dtype == BSA_BF16))
     return fail(BSA_UNSUPPORTED, "raster output needs bf16, d = 128 and 128-token blocks");
+  if (gather && !bsa::attn_fwd_gather_ok(L, d, dtype == BSA_BF16))
+    return fail(BSA_UNSUPPORTED, "the gathered forward needs bf16, d = 128, 128-token blocks, "
+                "block widths that are multiples of 4 and Np * 256 < 2^31");
   if (!qp || !kp || !vp || !counts || !idx || !op || !lse)
     return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
   for (const void* p : {qp, kp, vp, static_cast<const void*>(op)})
@@ -407,7 +413,7 @@ static bsa_status attn_fwd_common(const bsa_layout* in, const int32_t* zone_shap
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
   return hip_status(bsa::launch_attn_fwd(L, zone_shape, qp, kp, vp, counts, idx, heads, d,
                                          dtype == BSA_BF16, sc, op, lse, ws,
-                                         static_cast<hipStream_t>(stream), raster),
+                                         static_cast<hipStream_t>(stream), raster, gather),
                     "attn_fwd");
 }
 
@@ -433,6 +439,14 @@ bsa_status bsa_attn_fwd_raster(const bsa_layout* in, const int32_t* zone_shape, 
                                void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return attn_fwd_common(in, zone_shape, qp, kp, vp, counts, idx, heads, d, dtype, scale, o,
                          lse, ws, ws_bytes, stream, true);
+}
+
+bsa_status bsa_attn_fwd_gather(const bsa_layout* in, const int32_t* zone_shape, const void* q,
+                               const void* k, const void* v, const int32_t* counts,
+                               const int32_t* idx, int heads, int d, int dtype, float scale,
+                               void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd_common(in, zone_shape, q, k, v, counts, idx, heads, d, dtype, scale, o, lse, ws,
+                         ws_bytes, stream, true, false, true);
 }
 
 bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,

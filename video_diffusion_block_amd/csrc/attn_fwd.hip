@@ -122,6 +122,44 @@ __device__ inline void dma_tile(__bf16* tile, const i32x4& rsrc, int src, int w,
   for (int m = 0; m < 4; ++m) dma_part<kIsV>(tile, rsrc, src, w, lane, m);
 }
 
+// Gathered tiles (rows read straight from the token-order [H, N, d] tensors).
+// Every block shape here has a width that is a multiple of 4, so the four
+// rows 4g .. 4g + 3 of a load are four consecutive raster tokens: the load's
+// source is the row group's token, origin + rel(g), plus the lane's own part
+// (row 4g + lane / 16, the chunk its swizzle asks for). rel(g) is the raster
+// offset of slot 4g inside a block of shape s, times the 256-byte row. The
+// buffer resource of a block starts at its origin's row and ends at the
+// head's last token, so a load's offset is rel(g) plus the lane's part (the
+// same for every block of one shape) and the hardware range check turns a pad
+// row past the last token into zeros.
+__device__ inline int group_rel_bytes(const Lay& L, int s, int g) {
+  const int bw = L.sh[s][2], bh = L.sh[s][1];
+  const int r = 4 * g;
+  const int rw = r % bw, rh = (r / bw) % bh, rt = r / (bw * bh);
+  return 2 * kD * ((rt * L.H + rh) * L.W + rw);
+}
+// The lane's part: row lane / 16 of the group, its swizzled chunk. It does not
+// depend on the group (the swizzles see row & 15 = (4 g + lane / 16) & 15 with
+// g = 8m + w', and 4 g & 15 = 4 w' & 15, the same for w' = w and w + 4).
+template <bool kIsV>
+__device__ inline int gather_lane_off(int w, int lane) {
+  const int u = lane >> 4, r = 4 * w + u;
+  const int q = kIsV ? vswz(r, lane & 15) : kswz(r, lane & 15);
+  return 2 * (u * kD + 8 * q);
+}
+// Part m (0..3) of wave w (0..7): LDS slots (8m + w) * 64 + lane, row group
+// g = 8m + w, from byte `voff` (rel(g) plus the lane's part) of the block's
+// resource.
+__device__ inline void dma_gather(__bf16* tile, const i32x4& rsrc, int voff, int w, int m) {
+  dma16_manual(rsrc, lds_addr_of(tile + (8 * m + w) * 512), voff, 0);
+}
+// The resource of a block whose origin is token `origin` of a head starting at
+// `head`: rows origin .. N-1 (none for an origin past the last token).
+__device__ inline i32x4 block_rsrc(const __bf16* head, long long n_tokens, int origin) {
+  const long long rows = n_tokens > origin ? n_tokens - origin : 0;
+  return make_buffer_rsrc(head + (size_t)origin * kD, (uint32_t)(rows * kD * 2));
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): vmcnt(0) and lgkmcnt(0), each leaving the others free. Issued
 // as builtins so that the compiler's own wait-count tracking sees them.
@@ -285,16 +323,24 @@ __device__ inline void pv_tiles(f32x16 (&o)[4], const __bf16* sv, const int (&vo
   }
 }
 
+// kGather: qp, kp, vp are the token-order [H, N, d] tensors (the block
+// order is applied inside the tile loads) and the output is in raster order.
+template <bool kGather>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ idx, float scale_log2,
     __bf16* __restrict__ op, float* __restrict__ lse, const int32_t* __restrict__ zone_shape,
     int raster) {
-  __shared__ __align__(16) __bf16 sK[2][kTile];  // 2 x 32 KB
-  __shared__ __align__(16) __bf16 sV[2][kTile];  // 2 x 32 KB
-  __shared__ int32_t sL[kMaxList];               // the row's key-block list (16 KB)
+  // (the swizzles assume 256-byte aligned tile rows)
+  __shared__ __align__(1024) __bf16 sK[2][kTile];  // 2 x 32 KB
+  __shared__ __align__(1024) __bf16 sV[2][kTile];  // 2 x 32 KB
+  // The row's key-block list (16 KB): block ids, or gathered, each block's
+  // origin and shape packed as origin * 4 + shape (the ids then sit in sB).
+  __shared__ int32_t sL[kMaxList];
+  __shared__ uint16_t sB[kGather ? kMaxList : 2];
   __shared__ __align__(16) uint32_t sM[2][64];   // block facts of blocks j, j+1 (8 copies each)
+  __shared__ __align__(16) int sRel[kGather ? 4 * 32 : 4];  // rel(g) bytes, [shape][w][k]
   int i, h;  // (query block, head)
   xcd_item(i, h);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -312,20 +358,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const int n = counts[row];
   const int blk0_list = lst[0];
   const int blk1_list = L.M > 1 ? lst[1] : 0;
+  // where this lane's output row goes: its slot of the permuted [H, Np, d]
+  // layout, or (raster) its token's row of [H, N, d] (pad slots: nowhere);
+  // gathered, the query row comes from that token's row too (a pad slot reads
+  // token 0 and writes nothing)
+  size_t orow_i = head0 + (size_t)i * kB + q;
+  bool o_real = true;
   bf16x8 qf[8];
-  {
+  if (!kGather) {
     const __bf16* qrow = qp + (head0 + (size_t)i * kB + q) * kD + 8 * hi;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
-  // where this lane's output row goes: its slot of the permuted [H, Np, d]
-  // layout, or (raster) its token's row of [H, N, d] (pad slots: nowhere)
-  size_t orow_i = head0 + (size_t)i * kB + q;
-  bool o_real = true;
-  if (raster) {
+  if (kGather || raster) {
     const long long tok = slot_token(L, block_box(L, zone_shape, i), q);
     o_real = tok >= 0;
     orow_i = (size_t)h * L.N + (size_t)(o_real ? tok : 0);
+  }
+  if (kGather) {  // a pad slot's query is zero, as in the permuted layout
+    const __bf16* qrow = qp + orow_i * kD + 8 * hi;
+    const bf16x8 zq = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+      qf[s] = o_real ? x : zq;
+    }
   }
 
   if (n == 0) {  // empty list (an all-pad query block): zeros, lse = -inf
@@ -336,9 +393,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     }
     return;
   }
-  const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
-  const i32x4 krs = make_buffer_rsrc(kp + head0 * kD, head_bytes);
-  const i32x4 vrs = make_buffer_rsrc(vp + head0 * kD, head_bytes);
+  // the buffer resources cover the head's rows: Np permuted slots, or N
+  // tokens (gathered: a pad row's source past the last token reads zeros)
+  const size_t src0 = kGather ? (size_t)h * L.N : head0;
+  const uint32_t head_bytes = (uint32_t)((kGather ? (size_t)L.N : (size_t)L.Np) * kD * 2);
+  const i32x4 krs = make_buffer_rsrc(kp + src0 * kD, head_bytes);
+  const i32x4 vrs = make_buffer_rsrc(vp + src0 * kD, head_bytes);
   const i32x4 mrs = make_buffer_rsrc(meta, (uint32_t)L.M * sizeof(BlockMeta));
   constexpr int kTileBytes = kTile * 2;
 
@@ -361,14 +421,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   };
 
   // prologue: the list into LDS; tiles K0, V0 (and K1), block 0's mask words
-  for (int e = tid; e < n; e += kThreads) sL[e] = lst[e];
+  for (int e = tid; e < n; e += kThreads) {
+    const int b = lst[e];
+    if (kGather) {
+      sB[e] = (uint16_t)b;
+      sL[e] = (int)meta[b].origin() * 4 + meta[b].shape();
+    } else {
+      sL[e] = b;
+    }
+  }
   const int blk0 = blk0_list;
   const int blk1 = n > 1 ? blk1_list : 0;
-  dma_tile<false>(sK[0], krs, blk0 * kTileBytes, w, lane);
-  dma_tile<true>(sV[0], vrs, blk0 * kTileBytes, w, lane);
+  // gathered loads: this lane's parts of the K and V row groups, and the
+  // rel(g) table of every shape for the loop's loads (waves 0..3, loads k)
+  const __bf16* k_head = kp + src0 * kD;
+  const __bf16* v_head = vp + src0 * kD;
+  const int lane_k = kGather ? gather_lane_off<false>(w, lane) : 0;
+  const int lane_v = kGather ? gather_lane_off<true>(w, lane) : 0;
+  if (kGather) {
+    for (int e = tid; e < L.n_shapes * 32; e += kThreads)
+      sRel[e] = group_rel_bytes(L, e >> 5, ((e >> 3) & 3) + 4 * (e & 7));
+    const int s0 = meta[blk0].shape(), s1 = meta[blk1].shape();
+    const int o0 = (int)meta[blk0].origin(), o1 = (int)meta[blk1].origin();
+    const i32x4 k0 = block_rsrc(k_head, L.N, o0), v0 = block_rsrc(v_head, L.N, o0);
+    const i32x4 k1 = block_rsrc(k_head, L.N, o1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r0 = group_rel_bytes(L, s0, 8 * m + w);
+      dma_gather(sK[0], k0, lane_k + r0, w, m);
+      dma_gather(sV[0], v0, lane_v + r0, w, m);
+      dma_gather(sK[1], k1, lane_k + group_rel_bytes(L, s1, 8 * m + w), w, m);
+    }
+  } else {
+    dma_tile<false>(sK[0], krs, blk0 * kTileBytes, w, lane);
+    dma_tile<true>(sV[0], vrs, blk0 * kTileBytes, w, lane);
+    dma_tile<false>(sK[1], krs, blk1 * kTileBytes, w, lane);  // (block 0 again if n = 1)
+  }
   fetch_meta(blk0, 0);
   fetch_meta(blk1, 1);
-  dma_tile<false>(sK[1], krs, blk1 * kTileBytes, w, lane);  // (block 0 again if n = 1)
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
@@ -493,28 +583,60 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
     barrier();
     bf16x8 pf8[4];
     if (KH == 1) softmax(pf8, no_hook);
-    // ids of blocks j+1 and j+2 (carried in scalar registers; the next one is
-    // read from LDS an iteration ahead)
+    // list entries of blocks j+1 and j+2 (ids, or gathered, packed origins and
+    // shapes; then also block j+2's id), carried in scalar registers; the next
+    // ones are read from LDS an iteration ahead
     int b1 = __builtin_amdgcn_readfirstlane(sL[min(1, n - 1)]);
     int b2 = __builtin_amdgcn_readfirstlane(sL[min(2, n - 1)]);
+    int id2 = kGather ? __builtin_amdgcn_readfirstlane((int)sB[min(2, n - 1)]) : 0;
+    // gathered: the offsets of this wave's eight K and eight V loads for the
+    // shape they were last formed for (re-formed when a block's shape differs)
+    int vk[8] = {}, vv[8] = {};
+    int sk_cur = -1, sv_cur = -1;
     for (int j = 0; j < n; ++j) {
       const int cb = j & 1, nb = cb ^ 1;
       const bool more1 = j + 1 < n, more2 = j + 2 < n;
       const int b3 = sL[min(j + 3, n - 1)];
+      const int id3 = kGather ? (int)sB[min(j + 3, n - 1)] : 0;
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
       const u32x3 mraw = *reinterpret_cast<const u32x3*>(&sM[nb][4 * kh]);
+      // gathered: the resources of K_{j+2} (block j+2's origin) and V_{j+1}
+      // (block j+1's), and the load offsets of their shapes
+      i32x4 krs_t = krs, vrs_t = vrs;
+      if (kGather && KH == 0) {
+        const int sk = b2 & 3, sv = b1 & 3;
+        krs_t = block_rsrc(k_head, L.N, b2 >> 2);
+        vrs_t = block_rsrc(v_head, L.N, b1 >> 2);
+        if (sk != sk_cur) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) vk[k] = lane_k + sRel[32 * sk + 8 * w + k];
+          sk_cur = sk;
+        }
+        if (sv != sv_cur) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) vv[k] = lane_v + sRel[32 * sv + 8 * w + k];
+          sv_cur = sv;
+        }
+      }
       // wave w (kh = 0) fills parts (w, m) and (w + 4, m) of K_{j+2} and V_{j+1}
       // Issued unconditionally (no branch between the exponentials, so the
       // loads stay spread over them): past the end of the list b1 and b2 repeat
       // the last block, and the buffers they fill are free and never read again.
       auto dma_hook = [&](int k) {
         const int ww = w + 4 * (k & 1), m = (k >> 1) & 3;
-        if (k < 8)
-          dma_part<false>(sK[cb], krs, b2 * kTileBytes, ww, lane, m);
-        else
-          dma_part<true>(sV[nb], vrs, b1 * kTileBytes, ww, lane, m);
+        if (kGather) {
+          if (k < 8)
+            dma_gather(sK[cb], krs_t, vk[k], ww, m);
+          else
+            dma_gather(sV[nb], vrs_t, vv[k - 8], ww, m);
+        } else {
+          if (k < 8)
+            dma_part<false>(sK[cb], krs, b2 * kTileBytes, ww, lane, m);
+          else
+            dma_part<true>(sV[nb], vrs, b1 * kTileBytes, ww, lane, m);
+        }
       };
-      if (KH == 0 && more2) fetch_meta(b2, cb);
+      if (KH == 0 && more2) fetch_meta(kGather ? id2 : b2, cb);
       const HalfMeta meta_n{mraw.x, mraw.y, (int)mraw.z};
       if (KH == 0) {
         softmax(pf8, dma_hook);
@@ -541,6 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
       }
       b1 = b2;
       b2 = __builtin_amdgcn_readfirstlane(b3);
+      if (kGather) id2 = __builtin_amdgcn_readfirstlane(id3);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       barrier();
     }
@@ -656,19 +779,36 @@ size_t attn_fwd_workspace(const Lay& L, int d, bool bf16) {
   return attn_fwd_uses_mfma(L, d, bf16) ? (size_t)L.M * sizeof(BlockMeta) : 0;
 }
 
+bool attn_fwd_gather_ok(const Lay& L, int d, bool bf16) {
+  if (!attn_fwd_uses_mfma(L, d, bf16)) return false;
+  for (int s = 0; s < L.n_shapes; ++s)
+    if (L.sh[s][2] % 4 != 0) return false;
+  // every source byte offset (origin + rel(g) + the lane's part, below the
+  // padded grid's Np rows) must fit the 32-bit signed offsets used
+  return (long long)L.Np * kD * 2 < (1ll << 31);
+}
+
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, void* ws, hipStream_t st, bool raster) {
+                           void* op, float* lse, void* ws, hipStream_t st, bool raster,
+                           bool gather) {
+  if (gather && !attn_fwd_gather_ok(L, d, bf16)) return hipErrorInvalidValue;
   if (attn_fwd_uses_mfma(L, d, bf16)) {
     BlockMeta* meta = static_cast<BlockMeta*>(ws);
     hipError_t e = launch_block_meta(L, zone_shape, meta, st);
     if (e != hipSuccess) return e;
     dim3 grid(L.M, heads);
-    attn_fwd_mfma<<<grid, kThreads, 0, st>>>(
-        L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
-        static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e, static_cast<__bf16*>(op),
-        lse, zone_shape, raster ? 1 : 0);
+    if (gather)
+      attn_fwd_mfma<true><<<grid, kThreads, 0, st>>>(
+          L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
+          static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e,
+          static_cast<__bf16*>(op), lse, zone_shape, 1);
+    else
+      attn_fwd_mfma<false><<<grid, kThreads, 0, st>>>(
+          L, meta, static_cast<const __bf16*>(qp), static_cast<const __bf16*>(kp),
+          static_cast<const __bf16*>(vp), counts, idx, scale * kLog2e,
+          static_cast<__bf16*>(op), lse, zone_shape, raster ? 1 : 0);
     return hipGetLastError();
   }
   if (raster) return hipErrorInvalidValue;  // (the raster output needs the MFMA kernel)

@@ -28,12 +28,15 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
 
 // Per-block facts the attention kernels need inside their loops: bit r of
 // mask word r / 32 (r < B) = slot r is real; count = real slots. Stored as two
-// 16-byte halves, half h = {word 2h, word 2h + 1, count, 0}, so that a reader
-// of slots 64h .. 64h + 63 gets its words and the count in one load.
+// 16-byte halves, half h = {word 2h, word 2h + 1, count, x_h}, so that a reader
+// of slots 64h .. 64h + 63 gets its words and the count in one load; x_0 is
+// the block origin's raster token index on the padded grid and x_1 its shape id.
 struct BlockMeta {
   uint32_t half[2][4];
   __host__ __device__ uint32_t mask(int k) const { return half[k >> 1][k & 1]; }
   __host__ __device__ int count() const { return (int)half[0][2]; }
+  __host__ __device__ uint32_t origin() const { return half[0][3]; }
+  __host__ __device__ int shape() const { return (int)half[1][3]; }
 };
 hipError_t launch_block_meta(const Lay& L, const int32_t* zone_shape, BlockMeta* meta,
                              hipStream_t st);
@@ -58,12 +61,16 @@ hipError_t launch_select(const Lay& L, const BlockMeta* meta, const double* logi
 // needs attn_fwd_workspace() bytes (the block table). raster (MFMA kernel
 // only): O and lse are written in raster token order, [heads, N, d] and
 // [heads, N], instead of the permuted [heads, Np, d] and [heads, Np].
+// gather (MFMA kernel, layouts with attn_fwd_gather_ok): Q, K, V are read in
+// raster token order, [heads, N, d], and O, lse are written in it.
 bool attn_fwd_uses_mfma(const Lay& L, int d, bool bf16);
+bool attn_fwd_gather_ok(const Lay& L, int d, bool bf16);
 size_t attn_fwd_workspace(const Lay& L, int d, bool bf16);
 hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const int32_t* counts,
                            const int32_t* idx, int heads, int d, bool bf16, float scale,
-                           void* op, float* lse, void* ws, hipStream_t st, bool raster = false);
+                           void* op, float* lse, void* ws, hipStream_t st, bool raster = false,
+                           bool gather = false);
 
 // Device address and size of the forward's static scratch array on the
 // current device (looked up once per device; no allocation).

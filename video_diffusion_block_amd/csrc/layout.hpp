@@ -39,11 +39,16 @@ struct Box {
 __host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
 __host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
 
+// Shape id of block b's zone (ids come from device memory; an out-of-range id
+// is clamped).
+__host__ __device__ inline int shape_id(const Lay& L, const int32_t* zone_shape, int b) {
+  return zone_shape ? imin(imax(zone_shape[b / L.bpz], 0), L.n_shapes - 1) : 0;
+}
+
 __host__ __device__ inline Box block_box(const Lay& L, const int32_t* zone_shape, int b) {
   const int z = b / L.bpz;
   const int local = b - z * L.bpz;
-  // shape ids come from device memory; an out-of-range id is clamped
-  const int s = zone_shape ? imin(imax(zone_shape[z], 0), L.n_shapes - 1) : 0;
+  const int s = shape_id(L, zone_shape, b);
   Box x;
   x.bt = L.sh[s][0];
   x.bh = L.sh[s][1];

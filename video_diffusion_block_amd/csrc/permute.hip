@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
         }
         v = make_uint4(ov[0], ov[1], ov[2], ov[3]);
       }
-      dst[padded0 + e] = v;
+      if (dst) dst[padded0 + e] = v;  // (no dst: pooled only)
       if (kEpc > 0 && pooled && n >= 0) {
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -198,6 +198,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
 
 // One workgroup of two wavefronts per block: wavefront v evaluates slots
 // 64v .. 64v + 63, one per lane, and a ballot forms the two validity words.
+// The spare words carry the block's origin as a raster token index on the
+// padded grid, (t0 H + h0) W + w0, and its shape id, for kernels that read the
+// block's rows straight from the token-order tensors.
 __global__ __launch_bounds__(128) void block_meta_kernel(Lay L, const int32_t* zone_shape,
                                                          BlockMeta* meta) {
   const int b = blockIdx.x, r = threadIdx.x, v = r >> 6;
@@ -210,7 +213,8 @@ __global__ __launch_bounds__(128) void block_meta_kernel(Lay L, const int32_t* z
     half[0] = (uint32_t)word;
     half[1] = (uint32_t)(word >> 32);
     half[2] = count;
-    half[3] = 0u;
+    half[3] = v == 0 ? (uint32_t)(((long long)x.t0 * L.H + x.h0) * L.W + x.w0)
+                     : (uint32_t)shape_id(L, zone_shape, b);
   }
 }
 

@@ -153,20 +153,24 @@ def permute(layout: BSALayout, zone_shape, tensors):
     return outs
 
 
-def permute_pool(layout: BSALayout, zone_shape, tensors, npool: int = 2):
+def permute_pool(layout: BSALayout, zone_shape, tensors, npool: int = 2, store: bool = True):
     """bsa_permute_pool: the gathered tensors (as permute) and the fp64 block
-    means [H, M, d] of the first npool of them, from one launch."""
+    means [H, M, d] of the first npool of them, from one launch. store=False
+    (pooled tensors only, ntensors == npool): the means alone, no gathered
+    copies (outs is then a list of None)."""
     lib = _lib.load()
     _dev(zone_shape, *tensors)
     sz = layout.sizes()
-    outs = [_empty((t.shape[0], sz["n_padded"], t.shape[2]), t.dtype, t.device)
+    if not store and npool != len(tensors):
+        raise ValueError("store=False pools every tensor it is given (npool == len(tensors))")
+    outs = [_empty((t.shape[0], sz["n_padded"], t.shape[2]), t.dtype, t.device) if store else None
             for t in tensors]
     means = [_empty((t.shape[0], sz["n_blocks"], t.shape[2]), torch.float64, t.device)
              for t in tensors[:npool]]
     H, _, d = tensors[0].shape
     n = len(tensors)
     src_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in tensors])
-    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    dst_arr = (ctypes.c_void_p * n)(*[t.data_ptr() if t is not None else None for t in outs])
     mean_arr = (ctypes.c_void_p * max(npool, 1))(*[t.data_ptr() for t in means])
     L = layout.c()
     _lib.check("bsa_permute_pool", lib.bsa_permute_pool(
@@ -325,6 +329,25 @@ def attn_fwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scal
     _lib.check("bsa_attn_fwd_raster", lib.bsa_attn_fwd_raster(
         ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(counts),
         _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+        _stream()))
+    return o, lse
+
+
+def attn_fwd_gather(layout: BSALayout, zone_shape, q, k, v, counts, idx, scale: float = 0.0):
+    """bsa_attn_fwd_gather: q, k, v in raster token order [H, N, d] (bf16);
+    o [H, N, d] and lse [H, N] float32 in the same order."""
+    lib = _lib.load()
+    _dev(zone_shape, q, k, v, counts, idx)
+    H, N, d = q.shape
+    if N != layout.sizes()["n_tokens"]:
+        raise ValueError(f"q has {N} tokens, the layout {layout.sizes()['n_tokens']}")
+    o = _empty((H, N, d), q.dtype, q.device)
+    lse = _empty((H, N), torch.float32, q.device)
+    ws = _workspace(_lib.BSA_CALL_ATTN_FWD, layout, H, d, q.device)
+    L = layout.c()
+    _lib.check("bsa_attn_fwd_gather", lib.bsa_attn_fwd_gather(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(q), _ptr(k), _ptr(v), _ptr(counts),
+        _ptr(idx), H, d, _dtype(q), float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
         _stream()))
     return o, lse
 
