@@ -283,7 +283,7 @@ def main():
     # block shape of these layouts is a multiple of 4 tokens wide)
     raster = not wl.backward and not args.unfused
     gather = (raster and not args.permuted and not args.norm_rope and
-              all(shp[2] % 4 == 0 for shp in lay.shapes))
+              ops.gather_supported(lay, q.dtype, wl.d))
     state = {"step": 0}
 
     def step(record):

@@ -294,15 +294,17 @@ def test_select_causal_full_size(name):
 
 def test_reused_selection_schedule():
     """ReusedSelection over 4 steps, lists refreshed every 2 (whole run as the
-    middle segment): a refresh step equals the direct bsa_permute_pool +
-    bsa_select + bsa_attn_fwd_raster calls on that step's inputs; a reuse step
-    equals bsa_permute + bsa_attn_fwd_raster of the step's own Q, K, V under
-    the previous step's lists (bitwise)."""
+    middle segment; this bf16 layout takes the gathering forward): a refresh
+    step equals the direct bsa_permute_pool + bsa_select + bsa_attn_fwd_raster
+    calls on that step's inputs; a reuse step equals bsa_permute +
+    bsa_attn_fwd_raster of the step's own Q, K, V under the previous step's
+    lists (bitwise)."""
     from video_diffusion_block_amd.schedule import ReusedSelection
     wl = SMALL[3]
     inp = synth.make_inputs(wl, parts=("q", "k", "v"))
     lay = layout_of(wl)
     base = [to_dev(inp[p], wl.dtype) for p in "qkv"]
+    assert ops.gather_supported(lay, base[0].dtype, wl.d)
     gen = torch.Generator(device="cuda").manual_seed(3)
     layer = ReusedSelection(lay, wl.sparsity_1e4, wl.tau, total_steps=4, every=2, middle=(0.0, 1.0))
     assert layer.plan == [True, False, True, False]

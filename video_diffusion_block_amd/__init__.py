@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     attn_bwd,
     attn_fwd,
     attn_fwd_gather,
+    gather_supported,
     attn_fwd_raster,
     permute,
     permute_norm_rope,

@@ -333,6 +333,13 @@ def attn_fwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, counts, idx, scal
     return o, lse
 
 
+def gather_supported(layout: BSALayout, dtype, d: int) -> bool:
+    """Whether bsa_attn_fwd_gather takes this configuration: bf16, d = 128,
+    128-token blocks, every candidate block shape a multiple of 4 tokens wide."""
+    return (dtype == torch.bfloat16 and d == 128 and layout.sizes()["block_tokens"] == 128
+            and all(int(shp[2]) % 4 == 0 for shp in layout.shapes))
+
+
 def attn_fwd_gather(layout: BSALayout, zone_shape, q, k, v, counts, idx, scale: float = 0.0):
     """bsa_attn_fwd_gather: q, k, v in raster token order [H, N, d] (bf16);
     o [H, N, d] and lse [H, N] float32 in the same order."""

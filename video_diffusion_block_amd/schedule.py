@@ -52,7 +52,11 @@ class ReusedSelection:
     ``layer(step, q, k, v, video, audio)`` returns (O [H, N, d], lse [H, N])
     in raster order; ``layer.refreshed`` says whether the last call
     recomputed the selection. ``frames_per_chunk`` > 0 selects with the
-    frame-chunk causal rule (bsa_select_causal)."""
+    frame-chunk causal rule (bsa_select_causal). Where bsa_attn_fwd_gather
+    takes the configuration, no block-ordered copy is made: a refresh step
+    pools the block means from the token-order Q, K, and every step's
+    attention gathers Q, K, V itself (same results as the gather +
+    bsa_attn_fwd_raster sequence used otherwise)."""
 
     def __init__(self, layout: "ops.BSALayout", sparsity_1e4: int, tau: float,
                  total_steps: int, every: int, middle=MIDDLE, frames_per_chunk: int = 0):
@@ -66,9 +70,13 @@ class ReusedSelection:
 
     def __call__(self, step: int, q, k, v, video=None, audio=None):
         lay = self.layout
+        gather = ops.gather_supported(lay, q.dtype, q.shape[2])
         if self.plan[step] or self.idx is None:
             zs = ops.zone_score(lay, video, audio)
-            (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
+            if gather:
+                _, (qbar, kbar) = ops.permute_pool(lay, zs, [q, k], npool=2, store=False)
+            else:
+                (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs, [q, k, v], npool=2)
             if self.frames_per_chunk:
                 counts, idx = ops.select_causal(lay, zs, qbar, kbar, self.sparsity_1e4, self.tau,
                                                 self.frames_per_chunk)
@@ -77,6 +85,9 @@ class ReusedSelection:
             self.zone_shape, self.counts, self.idx = zs, counts, idx
             self.refreshed = True
         else:
-            qp, kp, vp = ops.permute(lay, self.zone_shape, [q, k, v])
+            if not gather:
+                qp, kp, vp = ops.permute(lay, self.zone_shape, [q, k, v])
             self.refreshed = False
+        if gather:
+            return ops.attn_fwd_gather(lay, self.zone_shape, q, k, v, self.counts, self.idx)
         return ops.attn_fwd_raster(lay, self.zone_shape, qp, kp, vp, self.counts, self.idx)
