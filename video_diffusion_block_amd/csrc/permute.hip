@@ -66,10 +66,14 @@ constexpr int kPermThreads = 256;
 // lane's partial block sums need one LDS reduction over its column.
 // kChunks: the row's 16-byte chunk count when it is known at compile time (16
 // for bf16 and 32 for fp32 rows of d = 128), else 0 and `chunks_rt` gives it.
-// The instantiations of the four uses (the Q/K/V gather with pooling, the
-// plain gather, the bf16 scatter of O and the fp32 scatter of gradients) are
-// distinct kernels, so per-kernel counters and traces tell them apart.
-template <bool kInverse, int kEpc, bool kNR, int kChunks>
+// The instantiations of the five uses (the Q/K/V gather with pooling, the
+// pooling of Q and K alone, the plain gather, the bf16 scatter of O and the
+// fp32 scatter of gradients) are distinct kernels, so per-kernel counters and
+// traces tell them apart.
+// kStore = false: pooling only (no dst); then a thread's loads are all issued
+// before any of them is used (with stores, one chunk at a time measured
+// faster: the batched form needs more registers per lane).
+template <bool kInverse, int kEpc, bool kNR, int kChunks, bool kStore = true>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int32_t* zone_shape,
                                                                PtrPack P, int chunks_rt,
                                                                PoolPack pool, NormRope nr) {
@@ -117,67 +121,96 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Lay L, const int3
     }
   }
 
-  for (int e = threadIdx.x; e < total; e += kPermThreads) {
-    const int r = e / chunks;
-    const int c = e - r * chunks;
-    int tt = 0, hh = 0, ww = 0;
-    const long long n = kNR ? slot_token_at(L, x, r, tt, hh, ww) : slot_token(L, x, r);
-    if (!kInverse) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (n >= 0) v = src[raster0 + n * chunks + c];
-      if (kNR && transformed) {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        float f[kAcc];
+  if (!kStore) {
+    // pooling only: a thread's chunks (8 for a 128-slot block of bf16 d = 128
+    // rows) are all requested before any is summed, so that their round trips
+    // to memory overlap
+    constexpr int kU = 8;
+    for (int e0 = threadIdx.x; e0 < total; e0 += kU * kPermThreads) {
+      uint4 vv[kU];
+      bool real[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e = e0 + u * kPermThreads;
+        const int r = e / chunks;
+        const long long n = e < total ? slot_token(L, x, r) : -1;
+        real[u] = n >= 0;
+        vv[u] = real[u] ? src[raster0 + n * chunks + (e - r * chunks)] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (!real[u]) continue;
+        const uint32_t wv[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
 #pragma unroll
         for (int k = 0; k < kAcc; ++k)
-          f[k] = kEpc == 8 ? __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16))
-                           : __uint_as_float(wv[k]);
-        // RMSNorm: the row's chunks are the `chunks` adjacent lanes
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < kAcc; ++k) ss = fmaf(f[k], f[k], ss);
-        for (int o = chunks >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        const float inv = rsqrtf(ss / (float)d + nr.eps);
-#pragma unroll
-        for (int k = 0; k < kAcc; ++k) f[k] *= inv * gam[k];
-        // rotary embedding (pad rows are zero and stay zero)
-#pragma unroll
-        for (int p = 0; p < kAcc / 2; ++p) {
-          const int pos = axis[p] == 0 ? tt : axis[p] == 1 ? hh : ww;
-          float rev = (float)pos * rate[p];
-          rev -= floorf(rev);
-          const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-          const float a0 = f[2 * p], a1 = f[2 * p + 1];
-          f[2 * p] = a0 * cs - a1 * sn;
-          f[2 * p + 1] = a0 * sn + a1 * cs;
-        }
-        uint32_t ov[4];
-        if (kEpc == 8) {
-          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            ov[k] = __builtin_bit_cast(uint32_t, bf16x2v{(__bf16)f[2 * k], (__bf16)f[2 * k + 1]});
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) ov[k] = __float_as_uint(f[k]);
-        }
-        v = make_uint4(ov[0], ov[1], ov[2], ov[3]);
+          acc[k] += (double)(kEpc == 8 ? __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u)
+                                                                  : (wv[k >> 1] << 16))
+                                       : __uint_as_float(wv[k]));
       }
-      if (dst) dst[padded0 + e] = v;  // (no dst: pooled only)
-      if (kEpc > 0 && pooled && n >= 0) {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < kAcc; ++k) {
-          float f;
-          if (kEpc == 8)  // two bf16 per word, element 2i in the low half
-            f = __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16));
-          else
-            f = __uint_as_float(wv[k]);
-          acc[k] += (double)f;
+    }
+  } else {
+    for (int e = threadIdx.x; e < total; e += kPermThreads) {
+      const int r = e / chunks;
+      const int c = e - r * chunks;
+      int tt = 0, hh = 0, ww = 0;
+      const long long n = kNR ? slot_token_at(L, x, r, tt, hh, ww) : slot_token(L, x, r);
+      if (!kInverse) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n >= 0) v = src[raster0 + n * chunks + c];
+        if (kNR && transformed) {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+          float f[kAcc];
+  #pragma unroll
+          for (int k = 0; k < kAcc; ++k)
+            f[k] = kEpc == 8 ? __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16))
+                             : __uint_as_float(wv[k]);
+          // RMSNorm: the row's chunks are the `chunks` adjacent lanes
+          float ss = 0.f;
+  #pragma unroll
+          for (int k = 0; k < kAcc; ++k) ss = fmaf(f[k], f[k], ss);
+          for (int o = chunks >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+          const float inv = rsqrtf(ss / (float)d + nr.eps);
+  #pragma unroll
+          for (int k = 0; k < kAcc; ++k) f[k] *= inv * gam[k];
+          // rotary embedding (pad rows are zero and stay zero)
+  #pragma unroll
+          for (int p = 0; p < kAcc / 2; ++p) {
+            const int pos = axis[p] == 0 ? tt : axis[p] == 1 ? hh : ww;
+            float rev = (float)pos * rate[p];
+            rev -= floorf(rev);
+            const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+            const float a0 = f[2 * p], a1 = f[2 * p + 1];
+            f[2 * p] = a0 * cs - a1 * sn;
+            f[2 * p + 1] = a0 * sn + a1 * cs;
+          }
+          uint32_t ov[4];
+          if (kEpc == 8) {
+            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  #pragma unroll
+            for (int k = 0; k < 4; ++k)
+              ov[k] = __builtin_bit_cast(uint32_t, bf16x2v{(__bf16)f[2 * k], (__bf16)f[2 * k + 1]});
+          } else {
+  #pragma unroll
+            for (int k = 0; k < 4; ++k) ov[k] = __float_as_uint(f[k]);
+          }
+          v = make_uint4(ov[0], ov[1], ov[2], ov[3]);
         }
+        if (dst) dst[padded0 + e] = v;  // (no dst: pooled only)
+        if (kEpc > 0 && pooled && n >= 0) {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  #pragma unroll
+          for (int k = 0; k < kAcc; ++k) {
+            float f;
+            if (kEpc == 8)  // two bf16 per word, element 2i in the low half
+              f = __uint_as_float((k & 1) ? (wv[k >> 1] & 0xffff0000u) : (wv[k >> 1] << 16));
+            else
+              f = __uint_as_float(wv[k]);
+            acc[k] += (double)f;
+          }
+        }
+      } else if (n >= 0) {
+        dst[raster0 + n * chunks + c] = src[padded0 + e];
       }
-    } else if (n >= 0) {
-      dst[raster0 + n * chunks + c] = src[padded0 + e];
     }
   }
   if (kEpc > 0 && pooled) {
@@ -248,6 +281,9 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
   dim3 grid(L.M, heads, ntensors);
 #define BSA_PERMUTE(INV, EPC, NR, CH) \
   permute_kernel<INV, EPC, NR, CH><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, chunks, Q, R)
+#define BSA_POOL_ONLY(EPC, CH) \
+  permute_kernel<false, EPC, false, CH, false><<<grid, kPermThreads, 0, st>>>(L, zone_shape, P, \
+                                                                            chunks, Q, R)
 #define BSA_PERMUTE_ROWS(INV, EPC, NR) \
   do {                                 \
     if (chunks == 16)                  \
@@ -257,8 +293,16 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
     else                               \
       BSA_PERMUTE(INV, EPC, NR, 0);    \
   } while (0)
+  bool pool_only = !inverse && nrope == 0 && npool == ntensors && (epc == 8 || epc == 4);
+  for (int i = 0; i < ntensors; ++i) pool_only = pool_only && dst[i] == nullptr;
   if (inverse)
     BSA_PERMUTE_ROWS(true, 0, false);
+  else if (pool_only && epc == 8 && chunks == 16)
+    BSA_POOL_ONLY(8, 16);
+  else if (pool_only && epc == 8)
+    BSA_POOL_ONLY(8, 0);
+  else if (pool_only)
+    BSA_POOL_ONLY(4, 0);
   else if (npool == 0 && nrope == 0)
     BSA_PERMUTE_ROWS(false, 0, false);
   else if (nrope == 0 && epc == 8)
@@ -272,6 +316,7 @@ hipError_t launch_permute(const Lay& L, const int32_t* zone_shape, int ntensors,
   else
     return hipErrorInvalidValue;
 #undef BSA_PERMUTE_ROWS
+#undef BSA_POOL_ONLY
 #undef BSA_PERMUTE
   return hipGetLastError();
 }
