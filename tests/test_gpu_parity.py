@@ -523,6 +523,43 @@ def test_attn_fwd_gather(wl):
     assert np.abs(to_f64(lse_g) - lse_ref).max() <= LSE_TOL
 
 
+@pytest.mark.parametrize("grid,mode,block,shapes", [
+    # 4-token-wide blocks next to wider ones (row groups of 4 = whole block rows)
+    ((5, 20, 36), "dynamic", (4, 16, 16), ((2, 16, 4), (4, 4, 8), (1, 8, 16))),
+    # W = 30: the last block of each row holds 2 real columns of 4; its pad
+    # row groups wrap into the next grid row
+    ((3, 40, 30), "fixed", (1, 32, 4), None),
+], ids=["narrow-dyn", "narrow-fixed"])
+def test_attn_fwd_gather_narrow_shapes(grid, mode, block, shapes):
+    """bsa_attn_fwd_gather with 4-token-wide block shapes: bitwise the
+    permuted path (bsa_permute_pool + bsa_attn_fwd_raster) on the same lists,
+    and the oracle's O and lse."""
+    wl = synth.Workload("narrow", grid, 2, 128, "bf16", mode, block, 8000, 0.2)
+    inp = synth.make_inputs(wl, parts=("q", "k", "v"))
+    if mode == "fixed":
+        lay, L = ops.BSALayout.fixed(grid, block), olay.make_layout(grid, mode, block)
+    else:
+        lay = ops.BSALayout.dynamic(grid, block, shapes=shapes)
+        L = olay.make_layout(grid, mode, block, candidates=shapes)
+    rng = np.random.default_rng(31)
+    zs = rng.integers(0, len(L.shapes), L.n_zones).astype(np.int32)
+    zs_dev = torch.as_tensor(zs).cuda()
+    q, k, v = (to_dev(inp[p], "bf16") for p in "qkv")
+    assert ops.gather_supported(lay, q.dtype, 128)
+    (qp, kp, vp), (qbar, kbar) = ops.permute_pool(lay, zs_dev, [q, k, v], npool=2)
+    counts, idx = ops.select(lay, zs_dev, qbar, kbar, wl.sparsity_1e4, wl.tau)
+    o_r, lse_r = ops.attn_fwd_raster(lay, zs_dev, qp, kp, vp, counts, idx)
+    o_g, lse_g = ops.attn_fwd_gather(lay, zs_dev, q, k, v, counts, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r) and torch.equal(lse_g, lse_r)
+    perm = olay.permutation(L, zs)
+    lists = gpu_lists(counts, idx)
+    qf, kf, vf = (synth.bf16_bits_to_f64(inp[p]) for p in "qkv")
+    o_ref, lse_ref = oatt.attn_fwd_gathered(L, perm, qf, kf, vf, lists, 1 / np.sqrt(128))
+    assert_bf16_close(to_f64(o_g), o_ref, "O")
+    assert np.abs(to_f64(lse_g) - lse_ref).max() <= LSE_TOL
+
+
 def test_cdf_branch_lists():
     """Near-flat pooled rows: the CDF prefix (tau = 0.2) is longer than the
     top-k (s = 0.93), so most lists have n = m > k."""
@@ -600,7 +637,12 @@ def test_max_blocks_full_lists_attention():
     grads = ops.attn_bwd(lay, zs, qp, kp, vp, op, dop, lse, counts, idx)
     (o,) = ops.unpermute(lay, zs, [op])
     dq, dk, dv = (to_f64(x) for x in ops.unpermute(lay, zs, list(grads)))
+    # the gathering forward at the largest layout (full 4096-entry lists in its
+    # packed LDS list) writes what the forward + scatter wrote
+    o_g, lse_g = ops.attn_fwd_gather(lay, zs, q_d, k_d, v_d, counts, idx)
     torch.cuda.synchronize()
+    assert torch.equal(o_g, o)
+    del o_g, lse_g
     print("[full lists] gpu done; oracle", flush=True)
     L = oracle_layout(wl)
     perm = olay.permutation(L, np.zeros(L.n_zones, np.int32))
