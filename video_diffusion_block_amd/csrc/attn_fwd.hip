@@ -132,6 +132,9 @@ __device__ inline void dma_tile(__bf16* tile, const i32x4& rsrc, int src, int w,
 // head's last token, so a load's offset is rel(g) plus the lane's part (the
 // same for every block of one shape) and the hardware range check turns a pad
 // row past the last token into zeros.
+// (s uniform over the wavefront, so that L.sh[s] is a scalar load: indexed by
+// a per-lane id it would be a vector load, waited for behind every load in
+// flight)
 __device__ inline int group_rel_bytes(const Lay& L, int s, int g) {
   const int bw = L.sh[s][2], bh = L.sh[s][1];
   const int r = 4 * g;
@@ -156,8 +159,10 @@ __device__ inline void dma_gather(__bf16* tile, const i32x4& rsrc, int voff, int
 // The resource of a block whose origin is token `origin` of a head starting at
 // `head`: rows origin .. N-1 (none for an origin past the last token).
 __device__ inline i32x4 block_rsrc(const __bf16* head, long long n_tokens, int origin) {
+  origin = __builtin_amdgcn_readfirstlane(origin);  // (uniform: the resource is scalar)
   const long long rows = n_tokens > origin ? n_tokens - origin : 0;
-  return make_buffer_rsrc(head + (size_t)origin * kD, (uint32_t)(rows * kD * 2));
+  return make_buffer_rsrc(head + (size_t)origin * kD,
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(rows * kD * 2)));
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
@@ -351,13 +356,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const int32_t* lst = idx + row * L.M;
   const size_t head0 = (size_t)h * L.Np;
   const int q = 32 * qg + l32;  // this lane's query inside the block
-  // One memory round trip for the row's count, its first two list entries
-  // (every row has room for M entries; they are used only where the count
-  // covers them) and this lane's Q^T fragments (B operand of S^T = K Q^T:
+  // One memory round trip for the row's count, its list (every row has room
+  // for M entries; they are read ahead of the count and kept only where the
+  // count covers them) and this lane's Q^T fragments (B operand of S^T = K Q^T:
   // Q[q][16s + 8hi .. +8]).
-  const int n = counts[row];
-  const int blk0_list = lst[0];
-  const int blk1_list = L.M > 1 ? lst[1] : 0;
+  const int n = __builtin_amdgcn_readfirstlane(counts[row]);
+  const int blk0_list = __builtin_amdgcn_readfirstlane(lst[0]);
+  const int blk1_list = __builtin_amdgcn_readfirstlane(L.M > 1 ? lst[1] : 0);
+  constexpr int kLU = kMaxList / kThreads;  // list entries per thread
+  int ent[kLU];
+#pragma unroll
+  for (int u = 0; u < kLU; ++u) {
+    const int e = tid + u * kThreads;
+    ent[u] = e < L.M ? lst[e] : 0;
+  }
   // where this lane's output row goes: its slot of the permuted [H, Np, d]
   // layout, or (raster) its token's row of [H, N, d] (pad slots: nowhere);
   // gathered, the query row comes from that token's row too (a pad slot reads
@@ -370,7 +382,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
   }
-  if (kGather || raster) {
+  if (kGather) {
+    // from the query block's table entry (no zone-shape lookup): slot q is
+    // real iff its mask bit is set, and then its token is the block's origin
+    // plus the slot's raster offset in the block's shape
+    const BlockMeta& mi = meta[i];
+    const int si = __builtin_amdgcn_readfirstlane(mi.shape());
+    const int bw = L.sh[si][2], bh = L.sh[si][1];
+    const int k = q >> 5;
+    const uint32_t word = k == 0 ? mi.half[0][0] : k == 1 ? mi.half[0][1]
+                          : k == 2 ? mi.half[1][0] : mi.half[1][1];
+    o_real = (word >> (q & 31)) & 1u;
+    const int rel = ((q / (bw * bh)) * L.H + (q / bw) % bh) * L.W + q % bw;
+    orow_i = (size_t)h * L.N + (size_t)(o_real ? (long long)mi.origin() + rel : 0);
+  } else if (raster) {
     const long long tok = slot_token(L, block_box(L, zone_shape, i), q);
     o_real = tok >= 0;
     orow_i = (size_t)h * L.N + (size_t)(o_real ? tok : 0);
@@ -420,16 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
                     __builtin_amdgcn_readfirstlane(m.count)};
   };
 
-  // prologue: the list into LDS; tiles K0, V0 (and K1), block 0's mask words
-  for (int e = tid; e < n; e += kThreads) {
-    const int b = lst[e];
-    if (kGather) {
-      sB[e] = (uint16_t)b;
-      sL[e] = (int)meta[b].origin() * 4 + meta[b].shape();
-    } else {
-      sL[e] = b;
-    }
-  }
+  // prologue: tiles K0, V0 (and K1), block 0's mask words; then the list
+  // into LDS (after the tile loads are on their way)
   const int blk0 = blk0_list;
   const int blk1 = n > 1 ? blk1_list : 0;
   // gathered loads: this lane's parts of the K and V row groups, and the
@@ -439,10 +456,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   const int lane_k = kGather ? gather_lane_off<false>(w, lane) : 0;
   const int lane_v = kGather ? gather_lane_off<true>(w, lane) : 0;
   if (kGather) {
-    for (int e = tid; e < L.n_shapes * 32; e += kThreads)
-      sRel[e] = group_rel_bytes(L, e >> 5, ((e >> 3) & 3) + 4 * (e & 7));
-    const int s0 = meta[blk0].shape(), s1 = meta[blk1].shape();
-    const int o0 = (int)meta[blk0].origin(), o1 = (int)meta[blk1].origin();
+    for (int s = 0; s < L.n_shapes; ++s)
+      if (tid < 32) sRel[32 * s + tid] = group_rel_bytes(L, s, ((tid >> 3) & 3) + 4 * (tid & 7));
+    const int s0 = __builtin_amdgcn_readfirstlane(meta[blk0].shape());
+    const int s1 = __builtin_amdgcn_readfirstlane(meta[blk1].shape());
+    const int o0 = __builtin_amdgcn_readfirstlane((int)meta[blk0].origin());
+    const int o1 = __builtin_amdgcn_readfirstlane((int)meta[blk1].origin());
     const i32x4 k0 = block_rsrc(k_head, L.N, o0), v0 = block_rsrc(v_head, L.N, o0);
     const i32x4 k1 = block_rsrc(k_head, L.N, o1);
 #pragma unroll
@@ -459,6 +478,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   }
   fetch_meta(blk0, 0);
   fetch_meta(blk1, 1);
+#pragma unroll
+  for (int u = 0; u < kLU; ++u) {
+    const int e = tid + u * kThreads;
+    if (e < n) {
+      if (kGather) {
+        sB[e] = (uint16_t)ent[u];
+        sL[e] = (int)meta[ent[u]].origin() * 4 + meta[ent[u]].shape();
+      } else {
+        sL[e] = ent[u];
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // K operand (A of S^T): row 64kh + 32kt + l32, chunk (2st + hi) ^ (l32 & 15).
