@@ -188,6 +188,27 @@ __device__ inline uint64_t rank_key(double v) {
   const uint64_t mono = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
   return ~mono;
 }
+// The full key of the one candidate whose top bits (those at and above
+// `shift`) equal `prefix` (a bin that holds exactly one element).
+template <int C>
+__device__ inline uint64_t sole_key(const double (&key)[C], uint64_t prefix, int shift) {
+  const uint64_t mask = ~0ull << shift;
+  uint64_t mine = 0;
+  bool have = false;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    if (key[e] != -INFINITY) {
+      const uint64_t u = rank_key(key[e]);
+      if ((u & mask) == prefix) {
+        mine = u;
+        have = true;
+      }
+    }
+  }
+  const int src = __ffsll((long long)__ballot(have)) - 1;
+  const uint32_t lo = __shfl((uint32_t)mine, src), hi = __shfl((uint32_t)(mine >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
 template <typename T>
 __device__ inline T wave_exclusive_scan(T v, int lane) {
   T incl = v;
@@ -315,6 +336,10 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
       prefix |= (uint64_t)digit << shift;
       remaining -= cb;
       count_eq = ce;
+      if (ce == 1) {  // one element left in range: it is the cut (later
+        prefix = sole_key(key, prefix, shift);  // passes would only confirm it)
+        break;
+      }
     }
     // ties on the logit: the `remaining` smallest ids among the equal ones
     int id_cut = INT_MAX;
@@ -412,6 +437,10 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(Lay L, const BlockMe
         cbefore = __shfl(cbin, src);
         count_eq = __shfl(ceq, src);
         prefix |= (uint64_t)digit << shift;
+        if (count_eq == 1) {  // as above: the crossing is this one element
+          prefix = sole_key(key, prefix, shift);
+          break;
+        }
       }
       // equal logits at the crossing: take them in id order until tau
       int cut = INT_MAX, taken = count_eq;
