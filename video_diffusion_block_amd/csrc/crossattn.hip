@@ -812,7 +812,10 @@ XBwdWs xattn_bwd_layout(int N, int Na, int C, int heads) {
   w.kpad = 128 * ((Na + 127) / 128);
   const int kblocks = w.kpad / 128;
   const int ntiles = (N + kKQ - 1) / kKQ;
-  w.splits = (512 + heads * kblocks - 1) / (heads * kblocks);
+  // query splits of the dK/dV pass: as many as keep every (split, key block,
+  // head) workgroup resident at once (two per CU by LDS, 512 on 256 CUs);
+  // one more and the excess would run as a second, nearly empty round
+  w.splits = 512 / (heads * kblocks);
   if (w.splits > ntiles) w.splits = ntiles;
   if (w.splits < 1) w.splits = 1;
   w.npad = up64(N);
