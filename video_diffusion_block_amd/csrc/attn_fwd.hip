@@ -18,7 +18,11 @@
 //    transposing LDS read (ds_read_b64_tr_b16), so V is never transposed in
 //    registers. The next key block's global loads are in flight while the
 //    current one is computed. Pad keys of partial blocks are masked from a
-//    per-block 128-bit validity mask (computed once per call).
+//    per-block 128-bit validity mask (computed once per call). Two instances:
+//    <false> reads the block-ordered [H, Np, d] tensors; <true> reads the
+//    token-order [H, N, d] tensors and does the block gather in its own tile
+//    loads (per-block buffer resources based at the block's origin token),
+//    so no block-ordered copy of Q, K or V is ever stored.
 //  * attn_fwd_scalar: any dtype (fp32 / bf16), d in {64, 128}, B in {64, 128}.
 //    One thread per query slot, fp32 online softmax, K/V staged through LDS as
 //    fp32. This is the exact-parity path (fp32 inputs) and the fallback.
