@@ -65,7 +65,9 @@ def parse():
                     help="time bsa_permute + bsa_pool_select instead of bsa_permute_pool + bsa_select")
     ap.add_argument("--permuted", action="store_true",
                     help="store block-ordered Q, K, V (bsa_permute_pool) and run "
-                         "bsa_attn_fwd_raster on them instead of bsa_attn_fwd_gather")
+                         "bsa_attn_fwd_raster on them instead of bsa_attn_fwd_gather; with "
+                         "the backward, bsa_attn_bwd + bsa_unpermute of the gradients instead "
+                         "of bsa_attn_bwd_raster")
     return ap.parse_args()
 
 
@@ -114,6 +116,7 @@ def hbm_stages(wl, sizes, stage_ms, copy_gbps):
         alg["zone_score"] = N * wl.video_channels * e + wl.n_audio * wl.video_channels * e
     if wl.backward:
         alg["permute_dO"] = H * (N + Np) * d * e
+    if "unpermute_grads" in stage_ms:
         alg["unpermute_grads"] = 3 * 2 * H * N * d * 4  # fp32 dQ, dK, dV
     out = {}
     for stage, nbytes in alg.items():
@@ -354,10 +357,14 @@ def main():
         if wl.backward:
             (dop,) = ops.permute(lay, zs, [do])
             mark("permute_dO")
-            grads = ops.attn_bwd(lay, zs, qp, kp, vp, op, dop, lse, counts, idx)
-            mark("attn_bwd")
-            ops.unpermute(lay, zs, list(grads))
-            mark("unpermute_grads")
+            if args.permuted or args.unfused:
+                grads = ops.attn_bwd(lay, zs, qp, kp, vp, op, dop, lse, counts, idx)
+                mark("attn_bwd")
+                ops.unpermute(lay, zs, list(grads))
+                mark("unpermute_grads")
+            else:  # gradients written in raster order by the backward kernels
+                grads = ops.attn_bwd_raster(lay, zs, qp, kp, vp, op, dop, lse, counts, idx)
+                mark("attn_bwd")
         state.update(zs=zs, counts=counts, idx=idx)
         if record:
             ev_marks.append(marks)
@@ -415,6 +422,8 @@ def main():
                                 "norm_rope+pool" if args.norm_rope else
                                 "pool, gathering attention" if gather else "pool") +
                                (", raster O" if raster else "") +
+                               (", raster gradients" if wl.backward and not (args.permuted or
+                                                                           args.unfused) else "") +
                                (f", causal chunks of {args.causal_frames} frames"
                                 if args.causal_frames else "") +
                                (f", lists reused for {args.reuse_every} steps"

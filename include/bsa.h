@@ -357,6 +357,22 @@ bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const vo
                         int heads, int d, int dtype, float scale, void* dqp, void* dkp,
                         void* dvp, void* ws, size_t ws_bytes, void* stream);
 
+/* bsa_attn_bwd writing dQ, dK and dV straight in raster token order [Prism
+ * §Blocks: attention runs on the tokens regrouped into the zones' blocks, so
+ * its gradients are in block order and go back to the latent token order the
+ * rest of the model uses; Prism §Data: training runs BSA]:
+ *  dq, dk, dv  [heads, N, d] float32 out, the rows of the real tokens (every
+ *              one is written; bitwise the rows bsa_unpermute would take from
+ *              bsa_attn_bwd's outputs)
+ *  Same arithmetic and other arguments as bsa_attn_bwd (the inputs stay in
+ *  block order); supported for the bf16, d = 128, 128-token-block
+ *  configuration (BSA_UNSUPPORTED otherwise). */
+bsa_status bsa_attn_bwd_raster(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
+                               const void* kp, const void* vp, const void* op, const void* dop,
+                               const float* lse, const int32_t* counts, const int32_t* idx,
+                               int heads, int d, int dtype, float scale, void* dq, void* dk,
+                               void* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Audio-to-video cross-attention layer, forward [Prism §Blocks: the zone's
  * block shape uses the feature norm of the audio-to-video cross-attention, in
  * which video tokens attend to the audio tokens]. Reading implemented (the

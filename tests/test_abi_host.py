@@ -209,6 +209,20 @@ def test_attn_bwd_validation(lib):
     assert call(d=48) == _lib.BSA_UNSUPPORTED
 
 
+def test_attn_bwd_raster_validation(lib):
+    c = LAY.c()
+
+    def call(d=128, dt=1, ptr=FAKE, wsb=1 << 40, L=c):
+        return lib.bsa_attn_bwd_raster(ctypes.byref(L), FAKE, ptr, *([FAKE] * 7), 2, d, dt, 0.0,
+                                       FAKE, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(ptr=None) == _lib.BSA_INVALID_ARG
+    assert call(d=64) == _lib.BSA_UNSUPPORTED       # raster gradients: the MFMA kernels only
+    assert "raster" in lib.bsa_last_error().decode()
+    assert call(dt=0) == _lib.BSA_UNSUPPORTED       # fp32
+    assert call(wsb=16) == _lib.BSA_WORKSPACE_TOO_SMALL
+
+
 def test_permute_validation(lib):
     c = LAY.c()
     arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)

@@ -8,6 +8,7 @@ from . import ops  # noqa: F401
 from .ops import (  # noqa: F401
     BSALayout,
     attn_bwd,
+    attn_bwd_raster,
     attn_fwd,
     attn_fwd_gather,
     gather_supported,

@@ -449,16 +449,19 @@ bsa_status bsa_attn_fwd_gather(const bsa_layout* in, const int32_t* zone_shape, 
                          ws_bytes, stream, true, false, true);
 }
 
-bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
-                        const void* kp, const void* vp, const void* op, const void* dop,
-                        const float* lse, const int32_t* counts, const int32_t* idx, int heads,
-                        int d, int dtype, float scale, void* dqp, void* dkp, void* dvp,
-                        void* ws, size_t ws_bytes, void* stream) {
+static bsa_status attn_bwd_common(const bsa_layout* in, const int32_t* zone_shape,
+                                  const void* qp, const void* kp, const void* vp, const void* op,
+                                  const void* dop, const float* lse, const int32_t* counts,
+                                  const int32_t* idx, int heads, int d, int dtype, float scale,
+                                  void* dqp, void* dkp, void* dvp, void* ws, size_t ws_bytes,
+                                  void* stream, bool raster) {
   bsa::Lay L;
   BSA_TRY(make_lay(in, &L));
   BSA_TRY(check_heads(heads));
   BSA_TRY(check_dtype_d(dtype, d));
   if (d != 64 && d != 128) return fail(BSA_UNSUPPORTED, "d = %d; 64 or 128 supported", d);
+  if (raster && !bsa::attn_fwd_uses_mfma(L, d, dtype == BSA_BF16))
+    return fail(BSA_UNSUPPORTED, "raster gradients need bf16, d = 128 and 128-token blocks");
   if (!qp || !kp || !vp || !op || !dop || !lse || !counts || !idx || !dqp || !dkp || !dvp)
     return fail(BSA_INVALID_ARG, "a tensor pointer is NULL");
   for (const void* p : {qp, kp, vp, op, dop})
@@ -473,8 +476,26 @@ bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const v
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
   return hip_status(bsa::launch_attn_bwd(L, zone_shape, qp, kp, vp, op, dop, lse, counts, idx,
                                          heads, d, dtype == BSA_BF16, sc, dqp, dkp, dvp, ws,
-                                         static_cast<hipStream_t>(stream)),
+                                         static_cast<hipStream_t>(stream), raster),
                     "attn_bwd");
+}
+
+bsa_status bsa_attn_bwd(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                        const void* kp, const void* vp, const void* op, const void* dop,
+                        const float* lse, const int32_t* counts, const int32_t* idx, int heads,
+                        int d, int dtype, float scale, void* dqp, void* dkp, void* dvp,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_common(in, zone_shape, qp, kp, vp, op, dop, lse, counts, idx, heads, d, dtype,
+                         scale, dqp, dkp, dvp, ws, ws_bytes, stream, false);
+}
+
+bsa_status bsa_attn_bwd_raster(const bsa_layout* in, const int32_t* zone_shape, const void* qp,
+                               const void* kp, const void* vp, const void* op, const void* dop,
+                               const float* lse, const int32_t* counts, const int32_t* idx,
+                               int heads, int d, int dtype, float scale, void* dq, void* dk,
+                               void* dv, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_common(in, zone_shape, qp, kp, vp, op, dop, lse, counts, idx, heads, d, dtype,
+                         scale, dq, dk, dv, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

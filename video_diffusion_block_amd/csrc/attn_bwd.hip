@@ -273,12 +273,21 @@ __device__ inline void tr_offsets(int (&o1)[4], int (&o2)[4], int row0, int lane
 //   S^T = K Q^T, dP^T = V dO^T, P^T = exp(S^T scale - lse), dS^T = P^T (dP^T - D),
 //   dQ^T += K^T dS^T  (K^T through transposed LDS reads).
 // 8 wavefronts: wave w owns queries 32 (w % 4) .. +32 and keys 64 (w / 4) .. +64.
+// Raster token of slot r of a block, from its table entry (origin, shape); r
+// must be a real slot. The entry is read at a uniform index, so L.sh[shape]
+// is a scalar load.
+__device__ inline long long slot_raster(const Lay& L, const BlockMeta& m, int r) {
+  const int s = __builtin_amdgcn_readfirstlane(m.shape());
+  const int bw = L.sh[s][2], bh = L.sh[s][1];
+  return (long long)m.origin() + ((r / (bw * bh)) * L.H + (r / bw) % bh) * L.W + r % bw;
+}
+
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     Lay L, const BlockMeta* __restrict__ meta, const __bf16* __restrict__ qp,
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
     const __bf16* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ idx, float scale, float* __restrict__ dqp) {
+    const int32_t* __restrict__ idx, float scale, float* __restrict__ dqp, int raster) {
   __shared__ __align__(16) __bf16 sK[2][kTile];
   __shared__ __align__(16) __bf16 sV[2][kTile];
   __shared__ int32_t sList[BSA_MAX_BLOCKS];      // the row's key-block list
@@ -293,14 +302,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   const int32_t* lst = idx + row * L.M;
   const size_t head0 = (size_t)h * L.Np;
   const int q = 32 * qg + l32;
-  const size_t qrow = head0 + (size_t)i * kB + q;
   const bool q_real = (meta[i].mask(q >> 5) >> (q & 31)) & 1u;
+  // the lane's row of the block-ordered inputs, and its dQ row: the same slot
+  // of [H, Np, d], or (raster) its token's row of [H, N, d] (pad slots there
+  // have no row and write nothing)
+  const size_t qrow = head0 + (size_t)i * kB + q;
+  const size_t orow =
+      raster ? (size_t)h * L.N + (size_t)(q_real ? slot_raster(L, meta[i], q) : 0) : qrow;
+  const bool q_write = q_real || !raster;
 
   if (n == 0) {
-    if (kh == 0)
+    if (kh == 0 && q_write)
       for (int e = 8 * hi; e < kD; e += 16)
-        *reinterpret_cast<f32x4*>(dqp + qrow * kD + e) = f32x4{0.f, 0.f, 0.f, 0.f},
-        *reinterpret_cast<f32x4*>(dqp + qrow * kD + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dqp + orow * kD + e) = f32x4{0.f, 0.f, 0.f, 0.f},
+        *reinterpret_cast<f32x4*>(dqp + orow * kD + e + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
   const uint32_t head_bytes = (uint32_t)L.Np * kD * 2;
@@ -428,8 +443,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
       for (int r = 0; r < 16; ++r) xo[256 * (16 * t + r)] = acc[t][r];
   }
   __syncthreads();
-  if (kh == 0) {
-    float* out = dqp + qrow * kD;
+  if (kh == 0 && q_write) {
+    float* out = dqp + orow * kD;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -463,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     const __bf16* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ tcounts,
     const int32_t* __restrict__ tidx, float scale, float* __restrict__ dkp,
-    float* __restrict__ dvp) {
+    float* __restrict__ dvp, int raster) {
   __shared__ __align__(16) __bf16 sQ[2][kTile];
   __shared__ __align__(16) __bf16 sO[2][kTile];
   __shared__ __align__(16) float sL[2][kB];
@@ -666,14 +681,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
       asm volatile("s_barrier" ::: "memory");
     }
   }
-  // lane holds rows key 32w + 8(r/4) + 4hi + r%4, column d = 32t + l32
+  // lane holds rows key 32w + 8(r/4) + 4hi + r%4, column d = 32t + l32;
+  // raster: the key's token row of [H, N, d] (pad slots have none)
   const BlockMeta& mj = meta[j];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
     const bool real = (mj.mask(key >> 5) >> (key & 31)) & 1u;
-    float* dkr = dkp + (kbase + key) * kD + l32;
-    float* dvr = dvp + (kbase + key) * kD + l32;
+    if (raster && !real) continue;
+    const size_t krow = raster ? (size_t)h * L.N + (size_t)slot_raster(L, mj, key) : kbase + key;
+    float* dkr = dkp + krow * kD + l32;
+    float* dvr = dvp + krow * kD + l32;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       dkr[32 * t] = real ? dk[t][r] * scale : 0.f;
@@ -724,7 +742,7 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
                            const void* kp, const void* vp, const void* op, const void* dop,
                            const float* lse, const int32_t* counts, const int32_t* idx,
                            int heads, int d, bool bf16, float scale, void* dqp, void* dkp,
-                           void* dvp, void* ws, hipStream_t st) {
+                           void* dvp, void* ws, hipStream_t st, bool raster) {
   const int words = (L.M + 31) / 32;
   char* p = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(p);
@@ -765,11 +783,13 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
     attn_bwd_dkdv_mfma<<<dim3(L.M, heads), 256, 0, st>>>(L, meta, q, k, v, dO, lse2, delta,
                                                         tcounts, tidx, scale,
                                                         static_cast<float*>(dkp),
-                                                        static_cast<float*>(dvp));
+                                                        static_cast<float*>(dvp), raster ? 1 : 0);
     attn_bwd_dq_mfma<<<dim3(L.M, heads), 512, 0, st>>>(L, meta, q, k, v, dO, lse2, delta, counts,
-                                                      idx, scale, static_cast<float*>(dqp));
+                                                      idx, scale, static_cast<float*>(dqp),
+                                                      raster ? 1 : 0);
     return hipGetLastError();
   }
+  if (raster) return hipErrorInvalidValue;  // (raster gradients need the MFMA kernels)
 
 #define BSA_BWD(T, D)                                                                        \
   return launch_bwd_scalar<T, D>(                                                            \

@@ -76,13 +76,15 @@ hipError_t launch_attn_fwd(const Lay& L, const int32_t* zone_shape, const void* 
 // current device (looked up once per device; no allocation).
 hipError_t attn_fwd_static_scratch(void** ptr, size_t* bytes);
 
-// Attention backward.
+// Attention backward. raster (MFMA kernels only: bf16, d = 128, B = 128):
+// dQ, dK, dV are written in raster token order, [heads, N, d], instead of
+// the permuted [heads, Np, d].
 size_t attn_bwd_workspace(const Lay& L, int heads, int d);
 hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* qp,
                            const void* kp, const void* vp, const void* op, const void* dop,
                            const float* lse, const int32_t* counts, const int32_t* idx,
                            int heads, int d, bool bf16, float scale, void* dqp, void* dkp,
-                           void* dvp, void* ws, hipStream_t st);
+                           void* dvp, void* ws, hipStream_t st, bool raster = false);
 
 // A2V cross-attention layer. C[M,N] = sum_k A[m][k] B[n][k] (bf16, K a
 // multiple of 8, rows 16-byte aligned), fp32 accumulation, bf16 or fp32 out

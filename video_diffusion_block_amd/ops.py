@@ -375,6 +375,24 @@ def attn_bwd(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, id
     return dq, dk, dv
 
 
+def attn_bwd_raster(layout: BSALayout, zone_shape, qp, kp, vp, op, dop, lse, counts, idx,
+                    scale: float = 0.0):
+    """bsa_attn_bwd_raster: dq, dk, dv [H, N, d] float32 in raster token order
+    (inputs in block order, as bsa_attn_bwd)."""
+    lib = _lib.load()
+    _dev(zone_shape, qp, kp, vp, op, dop, lse, counts, idx)
+    H, Np, d = qp.shape
+    N = layout.sizes()["n_tokens"]
+    dq, dk, dv = (_empty((H, N, d), torch.float32, qp.device) for _ in range(3))
+    ws = _workspace(_lib.BSA_CALL_ATTN_BWD, layout, H, d, qp.device)
+    L = layout.c()
+    _lib.check("bsa_attn_bwd_raster", lib.bsa_attn_bwd_raster(
+        ctypes.byref(L), _ptr(zone_shape), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), _ptr(dop),
+        _ptr(lse), _ptr(counts), _ptr(idx), H, d, _dtype(qp), float(scale), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
+
+
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
