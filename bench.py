@@ -18,7 +18,7 @@ and scales it).
 
 Options: --workload NAME runs another workload of the measurement plan
 (720p-dyn, 1080p, 2k; 2k adds the backward, which needs block-ordered copies
-and so gathers them); --copy-calib runs only a plain 1 GiB device copy (the
+and so gathers them, and which writes the gradients in raster order); --copy-calib runs only a plain 1 GiB device copy (the
 calibration kernel for HBM byte counters); --permuted (block-ordered copies of
 Q, K, V gathered with the pooling, then the attention on them), --unfused
 (separate gather and pool+select calls), --norm-rope (RMSNorm + 3-D RoPE of Q
