@@ -348,9 +348,11 @@ bsa_status bsa_attn_fwd_gather(const bsa_layout* L, const int32_t* zone_shape, c
  *  dqp, dkp, dvp [heads, Np, d] float32 out, whatever `dtype` is (gradients
  *              are accumulated and returned in fp32); pad slots get zeros.
  *  qp, kp, vp, op, dop must be 16-byte aligned (BSA_INVALID_ARG otherwise).
- *  The key-major (transposed) lists are built in the workspace. As for the
- *  forward, only bf16 with d = 128 and B = 128 runs on the matrix cores; the
- *  other supported configurations take scalar kernels (far slower). */
+ *  The key-major (transposed) lists are built in the workspace, with the
+ *  order in which the dK/dV pass takes the key blocks (longest list first).
+ *  As for the forward, only bf16 with d = 128 and B = 128 runs on the matrix
+ *  cores; the other supported configurations take scalar kernels (far
+ *  slower). */
 bsa_status bsa_attn_bwd(const bsa_layout* L, const int32_t* zone_shape, const void* qp,
                         const void* kp, const void* vp, const void* op, const void* dop,
                         const float* lse, const int32_t* counts, const int32_t* idx,

@@ -100,6 +100,54 @@ __global__ __launch_bounds__(256) void transpose_kernel(Lay L, const uint32_t* b
   if (tid == 0) tcounts[row] = base;
 }
 
+// The key blocks of head h by decreasing key-major list length (equal lengths
+// in any order): order[h * M + r] is the r-th longest. The dK/dV pass takes
+// its workgroups in this order. Its work per key block grows with the list
+// length (0 for pad blocks, up to several hundred listed query blocks), and
+// with the longest lists started first the short ones fill in the last wave
+// of workgroups instead of one long list running on alone. The outputs do not
+// depend on the order. A counting sort: lengths histogram, exclusive scan from
+// the longest length down, then each block takes the next slot of its length.
+__global__ __launch_bounds__(1024) void longest_first_kernel(Lay L, const int32_t* tcounts,
+                                                             int32_t* order) {
+  __shared__ int slot[BSA_MAX_BLOCKS + 1];  // per length: count, then next free rank
+  __shared__ int part[1024];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int nl = L.M + 1;  // lengths 0..M
+  const int32_t* len = tcounts + (size_t)h * L.M;
+  for (int b = tid; b < nl; b += 1024) slot[b] = 0;
+  __syncthreads();
+  for (int j = tid; j < L.M; j += 1024) atomicAdd(&slot[min(max(len[j], 0), L.M)], 1);
+  __syncthreads();
+  // thread t owns the lengths M - t*S .. M - t*S - S + 1 (longest first)
+  const int S = (nl + 1023) / 1024;
+  int own = 0;
+  for (int s = 0; s < S; ++s) {
+    const int r = tid * S + s;
+    if (r < nl) own += slot[L.M - r];
+  }
+  part[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int rank = part[tid] - own;  // blocks longer than this thread's lengths
+  for (int s = 0; s < S; ++s) {
+    const int r = tid * S + s;
+    if (r < nl) {
+      const int c = slot[L.M - r];
+      slot[L.M - r] = rank;
+      rank += c;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < L.M; j += 1024)
+    order[(size_t)h * L.M + atomicAdd(&slot[min(max(len[j], 0), L.M)], 1)] = j;
+}
+
 // ------------------------------------------------------------ dK/dV, scalar --
 template <typename T, int D>
 __global__ __launch_bounds__(128) void dkdv_scalar(Lay L, const int32_t* zone_shape, const T* qp,
@@ -477,14 +525,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     const __bf16* __restrict__ kp, const __bf16* __restrict__ vp,
     const __bf16* __restrict__ dop, const float* __restrict__ lse2,
     const float* __restrict__ delta, const int32_t* __restrict__ tcounts,
-    const int32_t* __restrict__ tidx, float scale, float* __restrict__ dkp,
-    float* __restrict__ dvp, int raster) {
+    const int32_t* __restrict__ tidx, const int32_t* __restrict__ order, float scale,
+    float* __restrict__ dkp, float* __restrict__ dvp, int raster) {
   __shared__ __align__(16) __bf16 sQ[2][kTile];
   __shared__ __align__(16) __bf16 sO[2][kTile];
   __shared__ __align__(16) float sL[2][kB];
   __shared__ __align__(16) float sD[2][kB];
   __shared__ int32_t sList[kMaxList];
-  const int j = blockIdx.x, h = blockIdx.y;
+  // workgroup x of head h takes the key block of the x-th longest list
+  const int h = blockIdx.y;
+  const int j = __builtin_amdgcn_readfirstlane(order[(size_t)h * L.M + blockIdx.x]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -735,7 +785,8 @@ size_t attn_bwd_workspace(const Lay& L, int heads, int d) {
          align256((size_t)heads * L.M * words * sizeof(uint32_t)) +
          align256((size_t)heads * L.M * sizeof(int32_t)) +
          align256((size_t)heads * L.M * L.M * sizeof(int32_t)) +
-         align256((size_t)L.M * sizeof(BlockMeta));
+         align256((size_t)L.M * sizeof(BlockMeta)) +
+         align256((size_t)heads * L.M * sizeof(int32_t));
 }
 
 hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* qp,
@@ -756,6 +807,8 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   int32_t* tidx = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)heads * L.M * L.M * sizeof(int32_t));
   BlockMeta* meta = reinterpret_cast<BlockMeta*>(p);
+  p += align256((size_t)L.M * sizeof(BlockMeta));
+  int32_t* order = reinterpret_cast<int32_t*>(p);
 
   const long long rows = (long long)heads * L.Np;
   const int lanes_per_row = d * (bf16 ? 2 : 4) / 16;
@@ -776,12 +829,13 @@ hipError_t launch_attn_bwd(const Lay& L, const int32_t* zone_shape, const void* 
   if (bf16 && d == kD && L.B == kB) {
     e = launch_block_meta(L, zone_shape, meta, st);
     if (e != hipSuccess) return e;
+    longest_first_kernel<<<heads, 1024, 0, st>>>(L, tcounts, order);
     const __bf16* q = static_cast<const __bf16*>(qp);
     const __bf16* k = static_cast<const __bf16*>(kp);
     const __bf16* v = static_cast<const __bf16*>(vp);
     const __bf16* dO = static_cast<const __bf16*>(dop);
     attn_bwd_dkdv_mfma<<<dim3(L.M, heads), 256, 0, st>>>(L, meta, q, k, v, dO, lse2, delta,
-                                                        tcounts, tidx, scale,
+                                                        tcounts, tidx, order, scale,
                                                         static_cast<float*>(dkp),
                                                         static_cast<float*>(dvp), raster ? 1 : 0);
     attn_bwd_dq_mfma<<<dim3(L.M, heads), 512, 0, st>>>(L, meta, q, k, v, dO, lse2, delta, counts,
