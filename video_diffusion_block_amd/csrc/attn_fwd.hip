@@ -613,6 +613,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
   // the one that read it, past that iteration's closing barrier.
   auto walk = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
+    // Pad halves. When a block's upper 64 keys are all pad (the last frames
+    // of a block that sticks out of a grid of 13 frames, say), the kh = 1
+    // wave's scores there all carry the pad bias and add nothing to O or the
+    // row sum. That wave then skips S and the exponentials of the block and
+    // sets its P to zero. It still runs the block's PV product (exact zeros
+    // added) when the next block has real keys, and skips it only when the
+    // next block is a pad half too or there is none: so its matrix half keeps
+    // facing the other wave's exponentials. Skipping the PV product as well
+    // made the wave's next exponentials overlap the other wave's, and the
+    // kernel slower. The decision is per block and half, the same in every
+    // lane; S and the exponentials of block 0 are always computed (before the
+    // loop).
+    bool skip_cur = KH == 1 && (meta_j.w0 | meta_j.w1) == 0u;
     qk_tiles(s_cur, sK[0], koff, kswz_lane, qf, l32, hi, meta_j, bias_b, no_hook);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier();
@@ -685,16 +698,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_mfma(
           qk_tiles_pre(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, kpre, no_hook);
         }
       } else {
+        const bool skip_n = __builtin_amdgcn_readfirstlane(mraw.x | mraw.y) == 0;
         bf16x8 kpre[4][2];
         auto kpre_hook = [&](int t) {
           if (t >= 2) k_frags(kpre, sK[nb], koff, kswz_lane, hi, 2 * (t - 2));
         };
-        pv_tiles(o, sV[cb], voff, pf8, kpre_hook);
-        rowsum(pf8);
-        if (more1) {
-          qk_tiles_pre(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, kpre, no_hook);
+        if (!(skip_cur && (skip_n || !more1))) {
+          pv_tiles(o, sV[cb], voff, pf8, kpre_hook);
+          rowsum(pf8);
         }
-        if (more1) softmax(pf8, no_hook);
+        if (more1 && !skip_n) {
+          qk_tiles_pre(s_cur, sK[nb], koff, kswz_lane, qf, l32, hi, meta_n, bias_b, kpre, no_hook);
+          softmax(pf8, no_hook);
+        } else {
+          const bf16x8 z = {};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pf8[c] = z;
+        }
+        skip_cur = skip_n;
       }
       b1 = b2;
       b2 = __builtin_amdgcn_readfirstlane(b3);
