@@ -151,21 +151,15 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def skipped_pad_half_flops(lay, zs, counts, idx, B, d):
-    """FLOPs of the selected block pairs that the forward kernel does not
-    issue: for a listed key block whose upper 64 keys are all pad, the upper
-    key-half wave skips that half's S product (not for the first list entry,
-    which every wave computes before its loop) and, when the next listed
-    block is such a block too or it is the last one, that half's PV product
-    (B^2 d FLOPs each). Pad slots are found by permuting a tensor of ones."""
+def skipped_pair_products(pad_hi, counts, idx):
+    """Number of half-block products (B^2 d FLOPs each) of the selected pairs
+    that the forward kernel does not issue. pad_hi[j]: key block j's upper 64
+    keys are all pad. For such a listed block the upper key-half wave skips
+    that half's S product (not for the first list entry, which every wave
+    computes before its loop) and, when the next listed block is such a block
+    too or it is the last one, that half's PV product."""
     import torch
-    from video_diffusion_block_amd import ops
-    N = lay.sizes()["n_tokens"]
-    ones = torch.ones((1, N, d), dtype=torch.bfloat16, device=counts.device)
-    (perm,) = ops.permute(lay, zs, [ones])
     M = counts.shape[1]
-    real = perm[0, :, 0] != 0
-    pad_hi = ~real.view(M, B)[:, B // 2:].any(dim=1)
     n = counts.long()
     j = torch.arange(M, device=counts.device)
     valid = j[None, None, :] < n[..., None]
@@ -176,7 +170,21 @@ def skipped_pad_half_flops(lay, zs, counts, idx, B, d):
     skip_s = p.clone()
     skip_s[..., 0] = False
     skip_pv = p & (nxt | last)
-    return float(int(skip_s.sum()) + int(skip_pv.sum())) * B * B * d
+    return int(skip_s.sum()) + int(skip_pv.sum())
+
+
+def skipped_pad_half_flops(lay, zs, counts, idx, B, d):
+    """FLOPs of the selected block pairs that the forward kernel does not
+    issue (skipped_pair_products x B^2 d). Pad slots are found by permuting a
+    tensor of ones."""
+    import torch
+    from video_diffusion_block_amd import ops
+    N = lay.sizes()["n_tokens"]
+    ones = torch.ones((1, N, d), dtype=torch.bfloat16, device=counts.device)
+    (perm,) = ops.permute(lay, zs, [ones])
+    M = counts.shape[1]
+    pad_hi = ~(perm[0, :, 0] != 0).view(M, B)[:, B // 2:].any(dim=1)
+    return float(skipped_pair_products(pad_hi, counts, idx)) * B * B * d
 
 
 def copy_calib():
