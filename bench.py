@@ -434,7 +434,9 @@ def main():
     layer_flops = fwd_flops + bwd_flops
     attn_ms = stage_ms["attn_fwd"]
     value = layer_flops / (ms_per_step * 1e-3) / 1e12
-    # the forward kernel's issued matrix-unit work (the roofline's figure)
+    # the forward kernel's issued matrix-unit work: the pair FLOPs minus the
+    # products it skips on key halves that are all pad (reported beside the
+    # roofline, whose figure is the per-pair executed work)
     fwd_issued = fwd_flops - skipped_pad_half_flops(lay, state["zs"], state["counts"],
                                                     state["idx"], B, d)
 
@@ -472,11 +474,14 @@ def main():
         "roofline": {
             "kernel": "attn_fwd_mfma<true>" if gather else "attn_fwd_mfma<false>",
             "bound": "mfma",
-            "achieved": round(fwd_issued / (attn_ms * 1e-3) / 1e12, 2),
+            "achieved": round(fwd_flops / (attn_ms * 1e-3) / 1e12, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(fwd_issued / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "frac": round(fwd_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "work": "4 B^2 d FLOPs per selected (query block, key block) pair",
             "issued_of_pair_flops": round(fwd_issued / max(fwd_flops, 1.0), 4),
+            "issued_achieved": round(fwd_issued / (attn_ms * 1e-3) / 1e12, 2),
+            "issued_frac": round(fwd_issued / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": None if args.causal_frames else measured_traffic(wl.name),
         },
         "hbm_stages": hbm_stages(wl, sizes, stage_ms, device_copy_gbps()),

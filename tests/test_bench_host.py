@@ -1,6 +1,6 @@
 """Host-side bookkeeping of bench.py: the count of half-block products the
-forward kernel skips on key halves that are all pad (the roofline's issued
-FLOPs), against a direct walk over the lists."""
+forward kernel skips on key halves that are all pad (the issued FLOPs reported
+beside the roofline), against a direct walk over the lists."""
 import os
 import sys
 
