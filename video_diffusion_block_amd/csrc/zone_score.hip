@@ -125,9 +125,20 @@ __global__ __launch_bounds__(64 * kGramWaves) void gram_kernel(const __bf16* A, 
 // (each token row read once, in whole 128-byte pieces; pieces swizzled by
 // token so the fragment reads are conflict free; rows past N read as zero).
 // Phase 2: softmax in fp32 registers, then g^2 z^2 = p^T G p over the tile
-// pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice), each
-// pair's G pieces (the Gram kernel's three-piece split, in operand order)
-// read straight into registers, one pair ahead.
+// pairs kt >= mt of the symmetric G (off-diagonal pairs counted twice), the
+// pairs' G pieces (the Gram kernel's three-piece split, in operand order)
+// staged in the freed operand buffers once per workgroup and read from LDS.
+// Index of the stored Gram tile pair (mt, kt), kt >= mt (row-major upper
+// triangle of an mtc x mtc tile grid), and the end of a round of whole rows
+// kt0 .. of the phase-2 loop order that holds at most cap pairs.
+__host__ __device__ constexpr int gpair_of(int mtc, int mt, int kt) {
+  return mt * mtc - mt * (mt - 1) / 2 + (kt - mt);
+}
+__host__ __device__ constexpr int stage_end(int mtc, int kt0, int cap) {
+  int kt = kt0, n = 0;
+  while (kt < mtc && n + kt + 1 <= cap) n += ++kt;
+  return kt;
+}
 constexpr int kA2vWaves = 8;
 constexpr int kTok = 32 * kA2vWaves;  // tokens per workgroup
 constexpr int kCh = 64;               // channels per chunk
@@ -142,8 +153,13 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   constexpr int SLOTS = 8 * NA_PAD;  // 16-byte slots per A chunk: 4 MT wave-loads
   constexpr int ABUF = SLOTS * 8;    // bf16 elements per A buffer
   constexpr int kAL = (4 * MT + kA2vWaves - 1) / kA2vWaves;  // A wave-loads per wave, at most
-  __shared__ __align__(16) __bf16 abuf[2 * ABUF];                      // [2][piece][row][8]
-  __shared__ __align__(16) __bf16 xbuf[kXRing][kA2vWaves][32 * kCh];  // [ring][wave][token][piece][8]
+  // one LDS array: phase 1's A [2][piece][row][8] and X [ring][wave][token][piece][8];
+  // phase 2's staged G pieces
+  constexpr int kXW = 32 * kCh;  // bf16 elements of one wavefront's X chunk
+  constexpr int kSmem = (2 * ABUF + kXRing * kA2vWaves * kXW) * 2;
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  __bf16* const abuf = reinterpret_cast<__bf16*>(smem);
+  __bf16* const xbuf = abuf + 2 * ABUF;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -179,7 +195,8 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int n = 8 * m + (lane >> 3), q = (lane & 7) ^ (n & 7);
-      dma16_manual(xrs, lds_addr_of(&xbuf[rs][w][64 * m * 8]), (n * C + kCh * ch + 8 * q) * 2, 0);
+      dma16_manual(xrs, lds_addr_of(xbuf + (rs * kA2vWaves + w) * kXW + 64 * m * 8),
+                   (n * C + kCh * ch + 8 * q) * 2, 0);
     }
   };
 
@@ -205,7 +222,7 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
     if (ch + 1 < nchunks) dma_a(ch + 1, (ch + 1) & 1);
     if (ch + 2 < nchunks) dma_x(ch + 2, (R + 2) % kXRing);
     const __bf16* ab = abuf + (ch & 1) * ABUF;
-    const __bf16* xb = &xbuf[R][w][0];
+    const __bf16* xb = xbuf + (R * kA2vWaves + w) * kXW;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 bx =
@@ -223,6 +240,28 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
     if (ch + 1 < nchunks) step(ch + 1, std::integral_constant<int, 1>{});
     if (ch + 2 < nchunks) step(ch + 2, std::integral_constant<int, 2>{});
   }
+
+  constexpr int kPairBytes = 3 * 2 * 64 * 16;
+  constexpr int kCap = kSmem / kPairBytes;  // pairs per round
+  constexpr int kE1 = stage_end(MT, 0, kCap), kE2 = stage_end(MT, kE1, kCap);
+  static_assert(kE2 == MT, "the Gram pieces must fit in two rounds");
+  const i32x4 grs = make_buffer_rsrc(gsw, (uint32_t)gram_pairs(MT) * kPairBytes);
+  // stage the pairs of rows kt0 .. kt1-1: wave-load L = q * 6 + 2 piece + s
+  auto stage_dma = [&](int kt0, int kt1) {
+    const int np = (kt1 * (kt1 + 1) - kt0 * (kt0 + 1)) / 2;
+    for (int L = w; L < 6 * np; L += kA2vWaves) {  // (wave-uniform)
+      const int q = L / 6, k = (L % 6) >> 1, sb = L & 1;
+      int kt = kt0, first = 0;  // row of stage pair q and its first pair
+      while (first + kt + 1 <= q) first += ++kt;
+      const int pr = gpair_of(MT, q - first, kt);
+      dma16_manual(grs, lds_addr_of(smem + (size_t)L * 64 * 16),
+                   (384 * pr + 128 * k + 2 * lane + sb) * 16, 0);
+    }
+  };
+  // Phase 2's first round of G pieces replaces the operand buffers: requested
+  // once every wavefront is past its phase-1 reads, landing during the softmax.
+  __syncthreads();
+  stage_dma(0, kE1);
 
   // softmax over the audio axis; lane holds audio 32mt + 8(r/4) + 4hi + r%4
   float mx = -INFINITY;
@@ -245,6 +284,8 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
       z += p;
     }
   z += __shfl_xor(z, 32);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's G loads have landed
+  __syncthreads();                      // and every wave's
 
   // g^2 z^2 = sum over tile pairs of p_mt . (G[mt][kt] p_kt), kt >= mt, the
   // off-diagonal pairs twice (G is symmetric). Y = G[mt][kt] P_kt on bf16
@@ -253,53 +294,56 @@ __global__ __launch_bounds__(64 * kA2vWaves) void a2v_kernel(const __bf16* X, in
   // mid.mid, lo.hi, smallest first. Lane-local element r of acc[kt] is P at
   // audio 32 kt + 8 (r / 4) + 4 hi + r % 4, the k index the stored G pieces
   // use, so elements 8s .. 8s + 7 are the B operand of k-step s as they lie.
-  // Each pair's G pieces (six 16-byte loads per lane) are loaded one pair
-  // ahead.
-  const bf16x8* gl = reinterpret_cast<const bf16x8*>(gsw) + 2 * lane;
-  auto gpair = [&](int mt_, int kt_) { return mt_ * MT - mt_ * (mt_ - 1) / 2 + (kt_ - mt_); };
-  auto gload = [&](bf16x8 (&g)[3][2], int pr) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) g[k][s] = gl[384 * pr + 128 * k + s];
-  };
-  bf16x8 gn[3][2];
-  gload(gn, 0);
+  // The G pieces are staged in LDS once per workgroup (every wavefront needs
+  // every pair), in the loop order (kt, then mt <= kt), in at most two rounds
+  // of whole kt rows that fit the operand buffers: slot ((q 3 + piece) 2 + s)
+  // 64 + lane holds 16 bytes (lanes contiguous: conflict-free reads).
   float gsq = 0.f;
+  auto stage_run = [&](auto kt0c, auto kt1c) {
+    constexpr int KT0 = decltype(kt0c)::value, KT1 = decltype(kt1c)::value;
 #pragma unroll
-  for (int kt = 0; kt < MT; ++kt) {
-    bf16x8 pp[3][2];
+    for (int kt = KT0; kt < KT1; ++kt) {
+      bf16x8 pp[3][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) split3(acc[kt][r], pp, r);
+      for (int r = 0; r < 16; ++r) split3(acc[kt][r], pp, r);
 #pragma unroll
-    for (int mt = 0; mt <= kt; ++mt) {
-      bf16x8 gc[3][2];
+      for (int mt = 0; mt <= kt; ++mt) {
+        const int q = (kt * (kt + 1) - KT0 * (KT0 + 1)) / 2 + mt;
+        bf16x8 gc[3][2];
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
+        for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) gc[k][s] = gn[k][s];
-      // next pair in this loop order: (mt + 1, kt), else (0, kt + 1)
-      const int nmt = mt < kt ? mt + 1 : 0, nkt = mt < kt ? kt : kt + 1;
-      if (nkt < MT) gload(gn, gpair(nmt, nkt));
-      f32x16 y = {};
+          for (int sb = 0; sb < 2; ++sb)
+            gc[k][sb] = *reinterpret_cast<const bf16x8*>(
+                smem + ((size_t)((q * 3 + k) * 2 + sb) * 64 + lane) * 16);
+        f32x16 y = {};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        y = mfma32x32x16(gc[2][s], pp[0][s], y);  // lo . hi
-        y = mfma32x32x16(gc[1][s], pp[1][s], y);  // mid . mid
-        y = mfma32x32x16(gc[0][s], pp[2][s], y);  // hi . lo
+        for (int sb = 0; sb < 2; ++sb) {
+          y = mfma32x32x16(gc[2][sb], pp[0][sb], y);  // lo . hi
+          y = mfma32x32x16(gc[1][sb], pp[1][sb], y);  // mid . mid
+          y = mfma32x32x16(gc[0][sb], pp[2][sb], y);  // hi . lo
+        }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          y = mfma32x32x16(gc[1][sb], pp[0][sb], y);  // mid . hi
+          y = mfma32x32x16(gc[0][sb], pp[1][sb], y);  // hi . mid
+        }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) y = mfma32x32x16(gc[0][sb], pp[0][sb], y);  // hi . hi
+        float d = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) d = fmaf(y[r], acc[mt][r], d);
+        gsq += kt == mt ? d : 2.f * d;
       }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        y = mfma32x32x16(gc[1][s], pp[0][s], y);  // mid . hi
-        y = mfma32x32x16(gc[0][s], pp[1][s], y);  // hi . mid
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) y = mfma32x32x16(gc[0][s], pp[0][s], y);  // hi . hi
-      float d = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) d = fmaf(y[r], acc[mt][r], d);
-      gsq += kt == mt ? d : 2.f * d;
     }
+  };
+  stage_run(std::integral_constant<int, 0>{}, std::integral_constant<int, kE1>{});
+  if constexpr (kE1 < MT) {
+    __syncthreads();  // every wavefront is done with the first round
+    stage_dma(kE1, MT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    stage_run(std::integral_constant<int, kE1>{}, std::integral_constant<int, MT>{});
   }
   gsq += __shfl_xor(gsq, 32);
   if (hi == 0 && tok_ok) gout[tok] = sqrtf(fmaxf(gsq, 0.f)) / z;
